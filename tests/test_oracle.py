@@ -1,0 +1,357 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test names the mistake class it would catch. Sources: "Megatron-LM:
+GPU-Cluster Training Parallelism" (blog walkthrough), sections on the f/g
+operators, the head-interleaved QKV split, pre-LN placement and the fused
+kernels; plus closed forms from mathematics.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import brute, fd
+from oracle import layer as L
+from tensor_model_transformer_amd.synth import LayerDims, Workload, WORKLOADS, \
+    full_params, layer_inputs, rank_params
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel_max(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def tiny(mask="causal", t=2, affine="perturbed", batch=2, seq=5, hidden=8, heads=2, ffn=16,
+         seed=7, len_range=(3, 5)):
+    d = LayerDims(batch, seq, hidden, heads, ffn, t=t, dtype="f32", mask=mask)
+    return Workload("tiny", d, seed=seed, affine=affine, weight_std=0.3, out_proj_std=0.3,
+                    len_range=len_range if mask == "padding" else None)
+
+
+# --------------------------------------------------------------------------
+# check 4: brute-force triple-loop forward at the tiny fp32 GPT workload
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("which", ["rank0", "rank1", "full"])
+def test_brute_force_forward_matches(which):
+    w = WORKLOADS["tiny_gpt_fp32"].with_(affine="perturbed")
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    if which == "full":
+        p = full_params(w)
+        heads = d.heads
+    else:
+        p = rank_params(w, int(which[-1]))
+        heads = d.heads_local
+    ref = L.layer(p, x, dout, heads, d.mask, vl)["out"]
+    bf = np.array(brute.forward(p, x.astype(np.float64), heads, d.mask, vl))
+    assert rel_max(ref, bf) <= 1e-12
+
+
+def test_brute_force_padding_mask():
+    w = tiny(mask="padding", t=1, batch=3, seq=6, len_range=(2, 6))
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 0)
+    ref = L.layer(p, x, dout, d.heads, d.mask, vl)["out"]
+    bf = np.array(brute.forward(p, x.astype(np.float64), d.heads, d.mask, vl))
+    assert rel_max(ref, bf) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# check 1: the sum over shards equals the unsharded layer (f/g algebra)
+# --------------------------------------------------------------------------
+def _check_partials_equal_full(w):
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    per = [rank_params(w, r) for r in range(d.t)]
+    part = L.layer_partials(per, x, dout, d, vl)
+    full = L.layer_full(full_params(w), x, dout, d, vl)
+    for key in ("out", "dx"):
+        assert rel_max(part[key], full[key]) <= 1e-12, key
+    assert rel_max(part["h_mid"], full["h_mid"]) <= 1e-12
+    g = L.assemble_full_grads(part["grads"], d.t)
+    for name, ref in full["grads"].items():
+        assert rel_max(g[name], ref) <= 1e-11, name
+    # the partial sums really are sums of t distinct terms
+    assert len(part["pa"]) == d.t and len(part["dc_part"]) == d.t
+
+
+def test_shard_sum_equals_full_tiny_gpt():
+    _check_partials_equal_full(WORKLOADS["tiny_gpt_fp32"].with_(affine="perturbed"))
+
+
+def test_shard_sum_equals_full_t8_32heads():
+    # the page's worked split (32 heads over 8 ranks) at a small hidden size
+    d = LayerDims(2, 12, 256, 32, 512, t=8, dtype="bf16", mask="causal")
+    _check_partials_equal_full(Workload("t8", d, seed=11, affine="perturbed"))
+
+
+def test_shard_sum_equals_full_padding_t4():
+    d = LayerDims(3, 10, 64, 8, 128, t=4, dtype="bf16", mask="padding")
+    _check_partials_equal_full(Workload("t4pad", d, seed=12, affine="perturbed", len_range=(2, 10)))
+
+
+def test_t1_local_equals_full():
+    w = tiny(t=1)
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    loc = L.layer_local(rank_params(w, 0), x, dout, d, vl)
+    full = L.layer_full(full_params(w), x, dout, d, vl)
+    assert rel_max(loc["out"], full["out"]) == 0.0
+    assert rel_max(loc["dx"], full["dx"]) == 0.0
+
+
+def test_local_rank_differs_from_full_when_t_gt_1():
+    # LOCAL(r) is one rank's term, not the whole layer: guards against a
+    # harness that would silently compare the wrong mode
+    w = tiny(t=2)
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    loc = L.layer_local(rank_params(w, 0), x, dout, d, vl)
+    full = L.layer_full(full_params(w), x, dout, d, vl)
+    assert rel_max(loc["out"], full["out"]) > 1e-3
+
+
+def test_worked_example_head_ownership():
+    """Golden: H=32, t=8 -> rank 0 owns heads 0..3, rank 1 owns heads 4..7,
+    via the head-interleaved layout and contiguous column shards."""
+    rows = []
+    with open(os.path.join(GOLDEN, "shard_ownership.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            rows.append({k: int(v) for k, v in (kv.split("=") for kv in line.split())})
+    assert len(rows) == 2
+    for row in rows:
+        H, t, r = row["heads"], row["t"], row["rank"]
+        dh = 2
+        h = H * dh
+        d = LayerDims(1, 1, h, H, 4 * h, t=t)
+        # encode (global head, kind, e) into the unsharded interleaved columns
+        col = np.arange(3 * h)
+        head_of_col = col // (3 * dh)
+        kind_of_col = (col // dh) % 3
+        # the rank's contiguous column block, as the shard layout defines it
+        lo, hi = r * 3 * d.hidden_local, (r + 1) * 3 * d.hidden_local
+        assert hi - lo == 3 * h // t
+        shard_heads = head_of_col[lo:hi].astype(np.float64)
+        q, k, v = L.split_heads(shard_heads[None, :], 1, 1, d.heads_local, dh)
+        owned = sorted(set(q.ravel().astype(int)) | set(k.ravel().astype(int)) |
+                       set(v.ravel().astype(int)))
+        assert owned == list(range(row["first_head"], row["last_head"] + 1))
+        # each local head has its Q, K and V inside the shard
+        kinds = kind_of_col[lo:hi].astype(np.float64)
+        kq, kk, kv = L.split_heads(kinds[None, :], 1, 1, d.heads_local, dh)
+        assert np.all(kq == 0) and np.all(kk == 1) and np.all(kv == 2)
+
+
+def test_head_permutation_invariance():
+    """Permuting heads consistently (QKV column triples, b_qkv, W_o rows)
+    leaves the output unchanged and permutes the gradients the same way."""
+    w = tiny(t=1, hidden=12, heads=3)
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 0)
+    dh = d.head_dim
+    perm = [2, 0, 1]
+    cols = np.concatenate([np.arange(3 * dh * j, 3 * dh * (j + 1)) for j in perm])
+    rows = np.concatenate([np.arange(dh * j, dh * (j + 1)) for j in perm])
+    q = dict(p)
+    q["w_qkv"] = p["w_qkv"][:, cols]
+    q["b_qkv"] = p["b_qkv"][cols]
+    q["w_o"] = p["w_o"][rows]
+    r0 = L.layer(p, x, dout, d.heads, d.mask, vl)
+    r1 = L.layer(q, x, dout, d.heads, d.mask, vl)
+    assert rel_max(r1["out"], r0["out"]) <= 1e-13
+    assert rel_max(r1["dx"], r0["dx"]) <= 1e-12
+    assert rel_max(r1["grads"]["w_qkv"], r0["grads"]["w_qkv"][:, cols]) <= 1e-12
+    assert rel_max(r1["grads"]["w_o"], r0["grads"]["w_o"][rows]) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# check 2 and softmax/mask closed forms
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mask", ["causal", "padding"])
+def test_attention_rows_sum_to_one(mask):
+    w = tiny(mask=mask, t=1, batch=3, seq=9, len_range=(1, 9))
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    r = L.layer(rank_params(w, 0), x, dout, d.heads, d.mask, vl, want_p=True)
+    p = r["p"]
+    assert np.max(np.abs(p.sum(axis=-1) - 1.0)) <= 1e-12
+    assert np.all(p >= 0)
+    s = d.seq
+    i = np.arange(s)[:, None]
+    k = np.arange(s)[None, :]
+    if mask == "causal":
+        assert np.all(p[:, :, k > i] == 0.0)
+    else:
+        for bi, Lb in enumerate(vl):
+            assert np.all(p[bi, :, :, Lb:] == 0.0)
+
+
+def test_causal_first_row_copies_v():
+    w = tiny(t=1, seq=7)
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 0)
+    r = L.layer(p, x, dout, d.heads, d.mask, vl)
+    q, k, v = L.split_heads(r["qkv"], d.batch, d.seq, d.heads, d.head_dim)
+    o = L.rows_to_heads(r["o"], d.batch, d.seq, d.heads, d.head_dim)
+    assert np.array_equal(o[:, :, 0, :], v[:, :, 0, :])
+
+
+@pytest.mark.parametrize("mask", ["causal", "padding"])
+def test_zero_qkv_weight_gives_mean_of_valid_values(mask):
+    """Zero Q and K projections make every score equal, so P is uniform over
+    the allowed keys and O is the mean of the allowed V rows."""
+    w = tiny(mask=mask, t=1, batch=2, seq=6, len_range=(2, 6))
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 0)
+    dh = d.head_dim
+    wq = np.array(p["w_qkv"], dtype=np.float64)
+    for j in range(d.heads):       # zero the Q and K columns: scores all equal
+        wq[:, 3 * dh * j: 3 * dh * j + 2 * dh] = 0.0
+    bq = np.array(p["b_qkv"], dtype=np.float64)
+    for j in range(d.heads):
+        bq[3 * dh * j: 3 * dh * j + 2 * dh] = 0.0
+    p2 = dict(p, w_qkv=wq, b_qkv=bq)
+    r = L.layer(p2, x, dout, d.heads, d.mask, vl)
+    _, _, v = L.split_heads(r["qkv"], d.batch, d.seq, d.heads, dh)
+    o = L.rows_to_heads(r["o"], d.batch, d.seq, d.heads, dh)
+    for bi in range(d.batch):
+        for i in range(d.seq):
+            nk = i + 1 if mask == "causal" else vl[bi]
+            ref = v[bi, :, :nk, :].mean(axis=1)
+            assert np.max(np.abs(o[bi, :, i, :] - ref)) <= 1e-13
+
+
+def test_causality_metamorphic():
+    """Perturbing x at positions > i leaves out rows <= i bit-identical."""
+    w = tiny(t=1, seq=8)
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 0)
+    r0 = L.layer(p, x, dout, d.heads, d.mask, vl)["out"]
+    x2 = np.array(x, dtype=np.float64)
+    x2[:, 5:, :] += 0.75
+    r1 = L.layer(p, x2, dout, d.heads, d.mask, vl)["out"]
+    assert np.array_equal(r0[:, :5], r1[:, :5])
+    assert not np.allclose(r0[:, 5:], r1[:, 5:])
+
+
+def test_padding_metamorphic():
+    """Perturbing x at padded positions (>= valid length) changes only those rows."""
+    w = tiny(mask="padding", t=1, batch=2, seq=8, len_range=(3, 6))
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 0)
+    r0 = L.layer(p, x, dout, d.heads, d.mask, vl)["out"]
+    x2 = np.array(x, dtype=np.float64)
+    for bi, Lb in enumerate(vl):
+        x2[bi, Lb:, :] -= 1.5
+    r1 = L.layer(p, x2, dout, d.heads, d.mask, vl)["out"]
+    for bi, Lb in enumerate(vl):
+        assert np.array_equal(r0[bi, :Lb], r1[bi, :Lb])
+        assert not np.allclose(r0[bi, Lb:], r1[bi, Lb:])
+
+
+# --------------------------------------------------------------------------
+# LayerNorm and GeLU closed forms
+# --------------------------------------------------------------------------
+def test_layernorm_invariants():
+    rng = np.random.default_rng(3)
+    x = rng.normal(size=(6, 40)) * 3 + 1
+    eps = 1e-5
+    y, xhat, rstd = L.layernorm_fwd(x, np.ones(40), np.zeros(40), eps)
+    var = x.var(axis=1)
+    assert np.max(np.abs(xhat.sum(axis=1))) <= 1e-12
+    assert np.max(np.abs((xhat ** 2).mean(axis=1) - var / (var + eps))) <= 1e-12
+    dy = rng.normal(size=x.shape)
+    gamma = rng.normal(size=40)
+    dx, dg, db = L.layernorm_bwd(dy, xhat, rstd, gamma)
+    assert np.max(np.abs(dx.sum(axis=1))) <= 1e-11
+    # sum_j dx*xhat = rstd * sum_j(g*xhat) * eps/(var+eps): zero only when eps = 0
+    g = dy * gamma
+    want = rstd[:, 0] * (g * xhat).sum(axis=1) * eps / (var + eps)
+    assert np.max(np.abs((dx * xhat).sum(axis=1) - want)) <= 1e-11
+    _, xhat0, rstd0 = L.layernorm_fwd(x, np.ones(40), np.zeros(40), 0.0)
+    dx0, _, _ = L.layernorm_bwd(dy, xhat0, rstd0, gamma)
+    assert np.max(np.abs((dx0 * xhat0).sum(axis=1))) <= 1e-11
+    # a constant shift of x does not change y; a scale only changes eps's weight
+    y2, _, _ = L.layernorm_fwd(x + 5.0, np.ones(40), np.zeros(40), eps)
+    assert np.max(np.abs(y2 - y)) <= 1e-12
+
+
+def test_gelu_closed_forms():
+    u = np.array([-3.0, -1.0, -0.5, 0.0, 0.5, 1.0, 3.0])
+    g = L.gelu(u)
+    assert g[3] == 0.0
+    # odd-part identity GeLU(u) - GeLU(-u) = u
+    assert np.max(np.abs(g - L.gelu(-u) - u)) <= 1e-15
+    for ui, gi in zip(u, g):
+        assert abs(gi - 0.5 * ui * (1.0 + math.erf(ui / math.sqrt(2.0)))) <= 1e-15
+    # Phi(1) = 0.8413447460685429 (standard normal CDF)
+    assert abs(L.gelu(np.array([1.0]))[0] - 0.8413447460685429) <= 1e-15
+    # derivative against a central difference
+    h = 1e-6
+    num = (L.gelu(u + h) - L.gelu(u - h)) / (2 * h)
+    assert np.max(np.abs(num - L.gelu_grad(u))) <= 1e-8
+    num_t = (L.gelu(u + h, "tanh") - L.gelu(u - h, "tanh")) / (2 * h)
+    assert np.max(np.abs(num_t - L.gelu_grad(u, "tanh"))) <= 1e-8
+    # the tanh form approximates the erf form to about 1e-3
+    assert np.max(np.abs(L.gelu(u, "tanh") - g)) <= 1e-3
+
+
+# --------------------------------------------------------------------------
+# check 3: gradients agree with finite differences on tiny shapes
+# --------------------------------------------------------------------------
+FD_CASES = [("causal", 1), ("causal", 2), ("padding", 1), ("padding", 2)]
+
+
+@pytest.mark.parametrize("mask,t", FD_CASES)
+def test_finite_differences_directional(mask, t):
+    w = tiny(mask=mask, t=t)
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 0)
+    heads = d.heads_local
+    r = L.layer(p, x, dout, heads, d.mask, vl)
+    rng = np.random.default_rng(99)
+    names = ["x"] + list(p.keys())
+    for name in names:
+        base = x if name == "x" else p[name]
+        v = rng.normal(size=np.shape(base))
+        ana = float(np.sum((r["dx"] if name == "x" else r["grads"][name]) * v))
+        num = fd.directional(p, x, dout, heads, d.mask, vl, name, v)
+        assert abs(ana - num) <= 1e-6 * max(1.0, abs(num)), (name, ana, num)
+
+
+@pytest.mark.parametrize("mask", ["causal", "padding"])
+def test_finite_differences_elementwise_small_tensors(mask):
+    w = tiny(mask=mask, t=2)
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 1)
+    heads = d.heads_local
+    r = L.layer(p, x, dout, heads, d.mask, vl)
+    for name in ("b_qkv", "b_o", "b_fc1", "b_fc2", "ln1_gamma", "ln1_beta",
+                 "ln2_gamma", "ln2_beta", "w_o"):
+        num = fd.elementwise(p, x, dout, heads, d.mask, vl, name)
+        ana = r["grads"][name]
+        assert np.max(np.abs(num - ana)) <= 1e-6 * max(1.0, np.max(np.abs(num))), name
+
+
+def test_flops_match_survey_counts():
+    # algorithmic FLOP counts of the five workloads (fwd+bwd = 3x forward)
+    want = {"tiny_gpt_fp32": 78.7e6, "gpt_1p2b_t1": 1.4690e12, "gpt_8p3b_t8": 0.7151e12,
+            "gpt_1t_t8": 12.160e12}
+    for name, f in want.items():
+        w = WORKLOADS[name]
+        got = L.flops_fwd_bwd(w.dims)
+        assert abs(got - f) / f < 1e-3, (name, got)
