@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Throughput of one tensor-parallel rank's pre-LN layer shard, forward +
+backward, on one MI355X, through the C ABI of libtplayer.so.
+
+A step is one tp_layer_fwd(TP_ALL) + tp_layer_bwd(TP_ALL) over one
+micro-batch of seeded synthetic input already resident in HBM. The metric is
+algorithmic TFLOP/s (GEMMs 2MNK, attention 4*dh*H_l per allowed query-key
+pair, backward = 2x forward; no recomputation, masked work, LayerNorm or
+elementwise work counted) and its fraction of the bf16 dense MFMA peak.
+
+Prints ONE JSON line. `--gpus N` with N > 1 exits: this build runs one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": (2500.0, "TFLOP/s"), "f32": (157.3, "TFLOP/s")}  # MI355X dense MFMA / fp32 vector
+HBM_PEAK_GBS = 8000.0
+METRIC = "TFLOP/s per GPU, fwd+bwd of one TP-rank layer shard; % of bf16 MFMA peak"
+
+
+def algorithmic_flops(d, valid_len):
+    n = d.tokens
+    gemm = 2 * n * (d.hidden * 3 * d.hidden_local + d.hidden_local * d.hidden
+                    + d.hidden * d.ffn_local + d.ffn_local * d.hidden)
+    if d.mask == "causal":
+        pairs = d.batch * d.seq * (d.seq + 1) // 2
+    else:
+        pairs = d.seq * int(sum(int(v) for v in valid_len))
+    return 3 * (gemm + 4 * d.head_dim * d.heads_local * pairs)
+
+
+def cpu_baseline(w, seqs):
+    """The fp64 oracle timed on the host on a bounded sample: the same layer
+    shard with `seqs` sequences instead of the full micro-batch."""
+    import numpy as np
+    from oracle import layer as OL
+    from tensor_model_transformer_amd.synth import layer_inputs, rank_params
+
+    d = w.dims
+    ws = w.with_(dims=d.__class__(seqs, d.seq, d.hidden, d.heads, d.ffn, d.t, d.dtype, d.mask))
+    params = rank_params(ws)
+    x, dout, vl = layer_inputs(ws)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    OL.layer_local(params, x, dout, ws.dims, vl)
+    dt = time.perf_counter() - t0
+    f = algorithmic_flops(ws.dims, vl)
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{seqs} of {d.batch} sequences of the same shard (fp64 NumPy, LOCAL mode, "
+                      f"fwd+bwd, {f / 1e9:.1f} GFLOP)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt_1p2b_t1")
+    ap.add_argument("--cpu-seqs", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU tensor parallelism is described in DESIGN.md, not launched.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tensor_model_transformer_amd import binding as B
+    from tensor_model_transformer_amd.shard import Shard, _check
+    from tensor_model_transformer_amd.synth import WORKLOADS, layer_inputs, rank_params
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    d = w.dims
+    params = rank_params(w)
+    x, dout, vl = layer_inputs(w)
+    sh = Shard(d, w.rank)
+    p = sh.upload_params(params, vl if d.mask == "padding" else None)
+    xd, doutd = sh.act(x), sh.act(dout)
+    out, dx = sh.empty_act(), sh.empty_act()
+    grads = sh.zero_grads()
+    del params
+
+    def step():
+        _check("tp_layer_fwd", sh.fwd(p, out, x=xd))
+        _check("tp_layer_bwd", sh.bwd(p, grads, x=xd, dout=doutd, dx=dx))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / args.steps
+    flops = algorithmic_flops(d, vl)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    print(f"[bench] {w.name}: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s "
+          f"(wall {wall:.2f} s for {args.steps} steps)", file=sys.stderr, flush=True)
+
+    # Per-kernel-class event timing over the same number of steps.
+    _check("tp_layer_profile", B.tp_layer_profile(sh.handle, 1))
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for k in B.KCLASSES:
+        rc, n, kms, kfl, kby = B.tp_layer_profile_read(sh.handle, k)
+        _check("tp_layer_profile_read", rc)
+        if n:
+            breakdown[k] = {"launches_per_step": n / args.steps, "ms_per_step": kms / args.steps,
+                            "gflop_per_step": kfl / args.steps / 1e9,
+                            "gbyte_per_step": kby / args.steps / 1e9}
+    B.tp_layer_profile(sh.handle, 0)
+    dom = max(breakdown, key=lambda k: breakdown[k]["ms_per_step"])
+    bd = breakdown[dom]
+    if bd["gflop_per_step"] > 0:
+        peak, unit = PEAK[d.dtype]
+        achieved = bd["gflop_per_step"] / bd["ms_per_step"]  # GFLOP/ms = TFLOP/s
+        roof = {"kernel": dom, "bound": "mfma" if d.dtype == "bf16" else "alu",
+                "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                "traffic": None}
+    else:
+        achieved = bd["gbyte_per_step"] / bd["ms_per_step"] * 1e3  # GB/s
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    roof["launches_per_step"] = bd["launches_per_step"]
+    roof["avg_launch_ms"] = bd["ms_per_step"] / bd["launches_per_step"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seqs)
+        print(f"[bench] cpu oracle: {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['cores']} threads "
+              f"({cpu['seconds']:.1f} s)", file=sys.stderr, flush=True)
+
+    peak = PEAK[d.dtype][0]
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": d.dtype, "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights)",
+        "pct_of_peak": 100.0 * value / peak,
+        "config": {"workload": w.name, "micro_batch": d.batch, "seq_len": d.seq,
+                   "hidden": d.hidden, "heads": d.heads, "ffn": d.ffn, "t": d.t,
+                   "rank": w.rank, "mask": d.mask, "gflop_per_step": flops / 1e9},
+        "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown,
+    }
+    print(json.dumps(line))
+    sh.close()
+
+
+if __name__ == "__main__":
+    main()

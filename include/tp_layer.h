@@ -1,0 +1,248 @@
+/*
+ * tp_layer.h -- one tensor-parallel rank's share of a pre-LayerNorm
+ * transformer layer, forward and backward, on an AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes is defined in "Megatron-LM: GPU-Cluster Training
+ * Parallelism" (blog walkthrough of arXiv 1909.08053 / 2104.04473):
+ *   - section "Paper 1: The f/g Conjugate Operators": FC1 is split by columns
+ *     (GeLU applied to the local slice), FC2 by rows; the attention block is
+ *     split by heads and its output projection by rows. g sums the two
+ *     row-parallel outputs in forward (identity in backward); f is the identity
+ *     in forward and sums the input gradients of the two column-parallel GEMMs
+ *     in backward. Two exchanges per direction per layer.
+ *   - section "Paper 1: QKV Column-Parallel Splitting in Detail": the fused QKV
+ *     weight has head-interleaved columns [Q_0 K_0 V_0 | Q_1 K_1 V_1 | ...], so
+ *     rank r of t owns the contiguous column block [r*3h/t, (r+1)*3h/t), i.e.
+ *     whole heads r*H/t .. (r+1)*H/t - 1, and attention needs no exchange.
+ *   - section "Paper 1: BERT LayerNorm Rearrangement": pre-LN placement,
+ *     y = x + Sublayer(LN(x)).
+ *   - section "Fused Transformer Kernels": bias+GeLU after FC1,
+ *     bias(+dropout)+residual after the row-parallel GEMMs, scale-mask-softmax
+ *     with general or causal masks, attention read in place (no transposes).
+ *
+ * One rank's forward (TP_ALL), with n = batch*seq tokens, h hidden,
+ * H_l = heads/t local heads of dimension dh = hidden/heads, h_l = H_l*dh,
+ * f_l = ffn/t:
+ *   a     = LN1(x)                               (gamma1, beta1; eps; biased var)
+ *   qkv   = a @ W_qkv,r + b_qkv,r                [n, 3*h_l] head-interleaved
+ *   o     = softmax_mask(Q K^T / sqrt(dh)) V     per local head, [n, h_l]
+ *   h_mid = x + b_o + o @ W_o,r                  (g: sum over ranks)
+ *   c     = LN2(h_mid)
+ *   z     = GeLU(c @ W_fc1,r + b_fc1,r)          [n, f_l]
+ *   out   = h_mid + b_fc2 + z @ W_fc2,r          (g: sum over ranks)
+ * Backward is the exact gradient of sum(out * dout).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensors are device pointers, row-major and contiguous, 16-byte
+ *    aligned (TP_ERR_ALIGN otherwise). Tokens are [batch, seq, .].
+ *  - Weights use the X @ W orientation [in, out]. Shapes of rank r's slices:
+ *      ln1_gamma, ln1_beta, ln2_gamma, ln2_beta, b_o, b_fc2 : [h]   (replicated)
+ *      w_qkv [h, 3*h_l], b_qkv [3*h_l]  (columns r*3*h_l ... of the full tensor)
+ *      w_o   [h_l, h]                   (rows r*h_l ... of the full tensor)
+ *      w_fc1 [h, f_l],   b_fc1 [f_l]
+ *      w_fc2 [f_l, h]
+ *  - Storage dtype (TP_DTYPE_F32 or TP_DTYPE_BF16) applies to x, dout, dx,
+ *    out (TP_ALL) and every parameter. Accumulation and statistics are fp32.
+ *    Every gradient of a parameter is written in fp32. With TP_DTYPE_BF16
+ *    the activations and gradients kept inside the layer (LayerNorm outputs,
+ *    qkv, attention output, FC1 pre/post activation and their gradients) are
+ *    IEEE fp16, fed to fp16 MFMA (same rate as bf16 on gfx950); bf16 weights
+ *    and dout are converted to fp16 as they are loaded, which is exact in
+ *    fp16's normal range. The residual stream h_mid and its gradient are fp32.
+ *  - Exchange partials (the tensors the f/g all-reduce would sum) are fp32
+ *    [n, h] buffers owned by the caller.
+ *  - The caller owns all memory, including the workspace. The library never
+ *    allocates device memory, never synchronises the stream and keeps no
+ *    pointer beyond a call. Work is enqueued on `hip_stream` (a hipStream_t;
+ *    NULL = the null stream) and the call returns after enqueue. A handle must
+ *    not be used on two streams at once. Asynchronous device faults surface at
+ *    the caller's synchronisation.
+ *  - Return value: TP_OK (0) or a negative TP_ERR_* code. No exceptions cross
+ *    the ABI, nothing is printed, nothing aborts. After an error the handle
+ *    stays valid and nothing has been enqueued (except TP_ERR_HIP, which
+ *    reports a failed launch: some kernels of that call may have run).
+ */
+#ifndef TP_LAYER_H
+#define TP_LAYER_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TP_OK = 0,
+  TP_ERR_ARG = -1,          /* NULL handle/struct/pointer or a value <= 0 */
+  TP_ERR_SHAPE = -2,        /* divisibility or rank range */
+  TP_ERR_UNSUPPORTED = -3,  /* dtype, mask, gelu form or head dim not built */
+  TP_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
+  TP_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than required */
+  TP_ERR_HIP = -6,          /* a HIP launch or runtime call failed */
+  TP_ERR_PHASE = -7         /* phase out of range */
+};
+
+enum { TP_DTYPE_F32 = 0, TP_DTYPE_BF16 = 1 };
+enum { TP_MASK_CAUSAL = 0, TP_MASK_PADDING = 1 };
+enum { TP_GELU_ERF = 0, TP_GELU_TANH = 1 };
+
+/* Forward phases. TP_ALL runs the whole shard with both g exchanges taken as
+ * the identity: the rank's own partial stands in for the sum (exactly the
+ * unsharded layer when t = 1). The split phases expose the two g exchanges
+ * so a caller can sum the t partials between them. */
+enum { TP_ALL = 0, TP_FWD_ATTN = 1, TP_FWD_MLP = 2 };
+/* Backward phases (TP_ALL = 0 as above), split at the two f exchanges. */
+enum { TP_BWD_MLP = 1, TP_BWD_ATTN = 2, TP_BWD_LN1 = 3 };
+
+typedef struct tp_layer tp_layer;
+
+typedef struct {
+  float ln_eps;     /* LayerNorm epsilon (default 1e-5) */
+  int gelu;         /* TP_GELU_ERF (default) or TP_GELU_TANH */
+} tp_layer_opts;
+
+/* Parameters of rank r (shapes above) and, for TP_MASK_PADDING, the number
+ * of valid key positions of each sequence (int32 [batch], values in
+ * [1, seq]; keys at positions >= valid_len[b] are excluded, every query row
+ * is still computed; values outside [1, seq] give undefined results but no
+ * out-of-bounds access). valid_len is ignored for TP_MASK_CAUSAL. */
+typedef struct {
+  const void *ln1_gamma, *ln1_beta;
+  const void *w_qkv, *b_qkv;
+  const void *w_o, *b_o;
+  const void *ln2_gamma, *ln2_beta;
+  const void *w_fc1, *b_fc1;
+  const void *w_fc2, *b_fc2;
+  const int *valid_len;
+} tp_params;
+
+typedef struct {
+  const tp_params *params;
+  const void *x;         /* [n, h] storage dtype: TP_ALL, TP_FWD_ATTN */
+  const float *h_mid;    /* TP_FWD_MLP: the summed fp32 [n, h] from the first g */
+  void *out;             /* TP_ALL: [n, h] storage dtype.
+                            TP_FWD_ATTN: fp32 [n, h] partial o @ W_o,r
+                              (+ x + b_o on rank 0).
+                            TP_FWD_MLP: fp32 [n, h] partial z @ W_fc2,r
+                              (+ h_mid + b_fc2 on rank 0). */
+  void *workspace;       /* tp_layer_create's workspace_bytes, same buffer for
+                            the matching backward and untouched in between */
+  size_t workspace_bytes;
+} tp_fwd_io;
+
+typedef struct {
+  const tp_params *params;
+  const void *x;         /* [n, h] storage dtype, the forward input: TP_ALL, TP_BWD_LN1 */
+  const void *dout;      /* [n, h] storage dtype: TP_ALL, TP_BWD_MLP, TP_BWD_ATTN */
+  const float *dc;       /* TP_BWD_ATTN: summed fp32 [n, h] (first f exchange) */
+  const float *da;       /* TP_BWD_LN1: summed fp32 [n, h] (second f exchange) */
+  float *partial;        /* TP_BWD_MLP: fp32 [n, h] <- this rank's term of the gradient
+                              of LN2's output, du @ W_fc1,r^T (first f exchange input);
+                            TP_BWD_ATTN: fp32 [n, h] <- this rank's term of the gradient
+                              of LN1's output, dqkv @ W_qkv,r^T (second f exchange input) */
+  void *dx;              /* TP_ALL, TP_BWD_LN1: [n, h] storage dtype */
+  /* fp32 gradients, shapes of the matching parameters. Written by:
+   *   TP_BWD_MLP : d_w_fc2, d_b_fc2, d_w_fc1, d_b_fc1
+   *   TP_BWD_ATTN: d_ln2_gamma, d_ln2_beta, d_w_o, d_b_o, d_w_qkv, d_b_qkv
+   *   TP_BWD_LN1 : d_ln1_gamma, d_ln1_beta
+   *   TP_ALL     : all of them */
+  float *d_ln1_gamma, *d_ln1_beta;
+  float *d_w_qkv, *d_b_qkv;
+  float *d_w_o, *d_b_o;
+  float *d_ln2_gamma, *d_ln2_beta;
+  float *d_w_fc1, *d_b_fc1;
+  float *d_w_fc2, *d_b_fc2;
+  int accumulate;        /* 0: overwrite the parameter gradients; 1: add to them */
+  void *workspace;
+  size_t workspace_bytes;
+} tp_bwd_io;
+
+/* Create a handle for rank `rank` of a t-way split of a layer with hidden
+ * size `hidden`, `heads` attention heads, FFN size `ffn`, sequence length
+ * `seq` and micro-batch `micro_batch`.
+ *   dtype: TP_DTYPE_F32 or TP_DTYPE_BF16. mask: TP_MASK_CAUSAL/TP_MASK_PADDING.
+ *   opts: NULL for the defaults (eps 1e-5, exact-erf GeLU).
+ * Checks: every size > 0; hidden % heads == 0; heads % t == 0; ffn % t == 0;
+ * (ffn/t) % 8 == 0; 0 <= rank < t; head dim in {32, 64, 96, 128, 160}
+ * (TP_ERR_UNSUPPORTED otherwise). Allocates no device memory. On success
+ * writes the handle to *out and the workspace size the fwd/bwd calls need to
+ * *workspace_bytes; on failure sets *out = NULL. */
+int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch,
+                    int t, int rank, int dtype, int mask,
+                    const tp_layer_opts *opts, tp_layer **out,
+                    size_t *workspace_bytes);
+
+/* Enqueue a forward phase (TP_ALL, TP_FWD_ATTN or TP_FWD_MLP). */
+int tp_layer_fwd(tp_layer *L, int phase, const tp_fwd_io *io, void *hip_stream);
+
+/* Enqueue a backward phase (TP_ALL, TP_BWD_MLP, TP_BWD_ATTN or TP_BWD_LN1).
+ * Needs the workspace of the matching forward (TP_ALL after TP_ALL; the split
+ * phases after both split forward phases), untouched since. */
+int tp_layer_bwd(tp_layer *L, int phase, const tp_bwd_io *io, void *hip_stream);
+
+/* Free the handle (host memory only). NULL is allowed. */
+int tp_layer_destroy(tp_layer *L);
+
+/* Single-GPU stand-in for the f/g all-reduce: dst[i] = sum_p parts[p][i] for
+ * i < count, summed in fp32 in the order p = 0, 1, ... and written as
+ * `dst_dtype` (TP_DTYPE_F32 or TP_DTYPE_BF16, round to nearest even).
+ * `parts` is a host array of `nparts` (1..16) fp32 device pointers. It is
+ * what the sum of the t ranks' partials would produce on t GPUs, used to
+ * check the f/g identity with every shard run in sequence on one device. */
+int tp_exchange_sum(void *dst, int dst_dtype, const float *const *parts,
+                    int nparts, size_t count, void *hip_stream);
+
+/* Test tap: byte offset and size inside the workspace of an intermediate
+ * kept between forward and backward (TP_TAP_*). Layout is row-major;
+ * "act" is fp16 for TP_DTYPE_BF16 and fp32 for TP_DTYPE_F32:
+ *   TP_TAP_LN1_OUT  a      [n, h]      act
+ *   TP_TAP_QKV      qkv    [n, 3*h_l]  act
+ *   TP_TAP_ATTN_OUT o      [n, h_l]    act
+ *   TP_TAP_LSE      log2-domain softmax normaliser [batch, H_l, seq] fp32:
+ *                   log2(sum_k exp(S_ik)) with S the scaled scores
+ *   TP_TAP_H_MID    h_mid  [n, h]      fp32
+ *   TP_TAP_LN2_OUT  c      [n, h]      act
+ *   TP_TAP_FC1_PRE  u      [n, f_l]    act (FC1 output before GeLU)
+ *   TP_TAP_FC1_OUT  z      [n, f_l]    act
+ *   TP_TAP_DQKV     dqkv   [n, 3*h_l]  act (after a backward)
+ *   TP_TAP_DH       dh     [n, h]      fp32 (residual-stream grad, after TP_BWD_ATTN)
+ * Returns TP_ERR_ARG for an unknown id. */
+enum {
+  TP_TAP_LN1_OUT = 0, TP_TAP_QKV = 1, TP_TAP_ATTN_OUT = 2, TP_TAP_LSE = 3,
+  TP_TAP_H_MID = 4, TP_TAP_LN2_OUT = 5, TP_TAP_FC1_PRE = 6, TP_TAP_FC1_OUT = 7,
+  TP_TAP_DQKV = 8, TP_TAP_DH = 9
+};
+int tp_layer_tap(const tp_layer *L, int tap, size_t *offset, size_t *bytes);
+
+/* Measurement support (not needed to run the layer). When enabled, every
+ * kernel launch group the handle enqueues is bracketed by two hipEvents
+ * recorded on the call's stream, tagged with one of the classes below and
+ * with its algorithmic work: FLOPs (2*M*N*K per GEMM; 4*dh*H_l per allowed
+ * query-key pair for the attention forward, twice that backward) and bytes
+ * (each input read once, each output written once). Enabling, disabling or
+ * re-enabling clears what was recorded. The events are created on first use
+ * and reused; no device memory is allocated. */
+enum {
+  TP_K_GEMM = 0,      /* MFMA / FMA GEMMs incl. their split-K reduction */
+  TP_K_ATTN_FWD = 1,  /* attention forward */
+  TP_K_ATTN_BWD = 2,  /* attention backward (delta, dK/dV, dQ) */
+  TP_K_LN_FWD = 3,    /* LayerNorm forward */
+  TP_K_LN_BWD = 4,    /* LayerNorm backward + residual-gradient add */
+  TP_K_REDUCE = 5,    /* column sums and partial reductions (bias / gamma / beta grads) */
+  TP_K_COUNT = 6
+};
+int tp_layer_profile(tp_layer *L, int enable);
+
+/* Totals for one class since profiling was enabled: number of launch groups,
+ * summed event time in milliseconds, summed algorithmic FLOPs and bytes.
+ * Waits on the host for the recorded events (call after the work is
+ * enqueued; it synchronises with the last recorded event). */
+int tp_layer_profile_read(tp_layer *L, int kclass, long *launches, double *ms,
+                          double *flops, double *bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_LAYER_H */

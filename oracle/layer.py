@@ -105,15 +105,17 @@ def key_mask(seq, mask, valid_len):
 
 def attention_fwd(q, k, v, allowed):
     """q, k, v: [b, H, s, dh]; allowed: [b, s, s]. Scaled masked softmax
-    attention. Returns (o [b, H, s, dh], p [b, H, s, s])."""
+    attention. Returns (o [b, H, s, dh], p [b, H, s, s], lse [b, H, s]) where
+    lse is the natural log of the softmax normaliser of the scaled scores."""
     dh = q.shape[-1]
     s = np.matmul(q, np.swapaxes(k, -1, -2)) / np.sqrt(dh)
     allowed = allowed[:, None, :, :]
     s = np.where(allowed, s, -np.inf)
     m = s.max(axis=-1, keepdims=True)
     e = np.where(allowed, np.exp(s - m), 0.0)
-    p = e / e.sum(axis=-1, keepdims=True)
-    return np.matmul(p, v), p
+    tot = e.sum(axis=-1, keepdims=True)
+    p = e / tot
+    return np.matmul(p, v), p, (m + np.log(tot))[..., 0]
 
 
 def attention_bwd(q, k, v, p, do):
@@ -162,14 +164,16 @@ def _f64(p):
 # The layer on one set of weights (LOCAL on a rank's slices, FULL on all)
 # ----------------------------------------------------------------------------
 def layer(params, x, dout, heads, mask="causal", valid_len=None, eps=1e-5,
-          gelu_form="erf", want_p=False):
+          gelu_form="erf", want_p=False, progress=None):
     """Forward and backward of the pre-LN layer on the given weights.
 
     params: dict of ln1_gamma, ln1_beta, w_qkv [h, 3*hl], b_qkv, w_o [hl, h],
     b_o, ln2_gamma, ln2_beta, w_fc1 [h, fl], b_fc1, w_fc2 [fl, h], b_fc2.
     heads: number of heads those weights hold (hl = heads * dh).
     x, dout: [b, s, h]. Returns a dict of outputs, gradients and the
-    intermediates (rows are tokens, n = b*s)."""
+    intermediates (rows are tokens, n = b*s). ``progress(step)`` is called
+    after each step when given (long runs report as they go)."""
+    say = progress or (lambda step: None)
     P = _f64(params)
     x = np.asarray(x, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
@@ -187,13 +191,16 @@ def layer(params, x, dout, heads, mask="causal", valid_len=None, eps=1e-5,
     a, xhat1, rstd1 = layernorm_fwd(X, P["ln1_gamma"], P["ln1_beta"], eps)
     qkv = a @ P["w_qkv"] + P["b_qkv"]
     q, k, v = split_heads(qkv, b, s, heads, dh)
-    oh, p = attention_fwd(q, k, v, allowed)
+    say("qkv")
+    oh, p, lse = attention_fwd(q, k, v, allowed)
     o = heads_to_rows(oh)
+    say("attention")
     h_mid = X + P["b_o"] + o @ P["w_o"]
     c, xhat2, rstd2 = layernorm_fwd(h_mid, P["ln2_gamma"], P["ln2_beta"], eps)
     u = c @ P["w_fc1"] + P["b_fc1"]
     z = gelu(u, gelu_form)
     out = h_mid + P["b_fc2"] + z @ P["w_fc2"]
+    say("forward")
 
     # backward of loss = sum(out * dout)
     g = {}
@@ -204,6 +211,7 @@ def layer(params, x, dout, heads, mask="causal", valid_len=None, eps=1e-5,
     g["b_fc1"] = du.sum(axis=0)
     g["w_fc1"] = c.T @ du
     dc = du @ P["w_fc1"].T
+    say("mlp backward")
     dh2, g["ln2_gamma"], g["ln2_beta"] = layernorm_bwd(dc, xhat2, rstd2, P["ln2_gamma"])
     dhm = dh2 + D
     g["b_o"] = dhm.sum(axis=0)
@@ -211,32 +219,24 @@ def layer(params, x, dout, heads, mask="causal", valid_len=None, eps=1e-5,
     do = dhm @ P["w_o"].T
     dq, dk, dv = attention_bwd(q, k, v, p, rows_to_heads(do, b, s, heads, dh))
     dqkv = merge_heads(dq, dk, dv)
+    say("attention backward")
     g["b_qkv"] = dqkv.sum(axis=0)
     g["w_qkv"] = a.T @ dqkv
     da = dqkv @ P["w_qkv"].T
     dx1, g["ln1_gamma"], g["ln1_beta"] = layernorm_bwd(da, xhat1, rstd1, P["ln1_gamma"])
     dx = dx1 + dhm
+    say("backward")
 
     res = {
         "out": out.reshape(b, s, h), "dx": dx.reshape(b, s, h), "grads": g,
         "a": a, "mean1": X.mean(axis=1), "rstd1": rstd1[:, 0], "qkv": qkv, "o": o,
         "h_mid": h_mid, "rstd2": rstd2[:, 0], "c": c, "u": u, "z": z,
         "du": du, "dc": dc, "dh": dhm, "do": do, "dqkv": dqkv, "da": da,
-        "lse": _lse(q, k, allowed),
+        "lse": lse,
     }
     if want_p:
         res["p"] = p
     return res
-
-
-def _lse(q, k, allowed):
-    """Natural-log softmax normaliser per (batch, head, query) of the scaled
-    scores over allowed keys."""
-    dh = q.shape[-1]
-    s = np.matmul(q, np.swapaxes(k, -1, -2)) / np.sqrt(dh)
-    s = np.where(allowed[:, None], s, -np.inf)
-    m = s.max(axis=-1)
-    return m + np.log(np.exp(s - m[..., None]).sum(axis=-1))
 
 
 def layer_local(rank_params, x, dout, dims, valid_len=None, **kw):
@@ -281,7 +281,7 @@ def layer_partials(per_rank, x, dout, dims, valid_len=None, eps=1e-5, gelu_form=
     for r in range(t):
         qkv = a @ P[r]["w_qkv"] + P[r]["b_qkv"]
         q, k, v = split_heads(qkv, b, s, Hl, dh)
-        oh, p = attention_fwd(q, k, v, allowed)
+        oh, p, _ = attention_fwd(q, k, v, allowed)
         o = heads_to_rows(oh)
         part = o @ P[r]["w_o"]
         if r == 0:

@@ -1,0 +1,712 @@
+// Causal / padding-masked softmax attention over one rank's local heads,
+// forward and backward.
+//
+// What is computed: "Megatron-LM: GPU-Cluster Training Parallelism", section
+// "Paper 1: QKV Column-Parallel Splitting in Detail" (each rank runs complete
+// heads on its own Q, K, V; no exchange inside attention) and section
+// "Fused Transformer Kernels" (scale-mask-softmax with general or causal
+// masks; Q, K, V read in place from the fused projection output, no transpose
+// kernels). S = Q K^T / sqrt(dh), masked keys excluded, P = row softmax,
+// O = P V. The tiled, online-softmax evaluation that never materialises the
+// s x s matrix is the memory-efficient attention the megatron-core package
+// description names (FlashAttention); it changes rounding only.
+//
+// 16-bit path (fp16 operands on the gfx950 MFMA 32x32x16 f16, fp32
+// accumulate; the layer's internal activations are fp16). The forward runs
+// transposed (S^T = K Q^T and O^T = V^T P^T) so that each lane owns one query:
+// the running max / sum of the online softmax stay in registers and the
+// 32x32 accumulator of S^T feeds the P^T operand of the next MFMA directly.
+// Within each 16-key slice the accumulator holds keys in the order
+// {4h..4h+3, 8+4h..8+4h+3} for lane half h; V^T is written to LDS in that
+// same order so both MFMA operands agree. Scores are kept in the log2 domain
+// (scale * log2(e) folded into S) and the per-row normaliser is saved as
+// lse2 = max + log2(sum).
+//
+// Backward (deterministic, no atomics): delta = rowsum(dO * O); one kernel
+// owns a block of keys and sweeps the queries (dK, dV); another owns a block
+// of queries and sweeps the keys (dQ). P is recomputed from lse2.
+//
+// fp32 path: one thread per query (forward, dQ) or key (dK, dV) with exact
+// fp32 arithmetic.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace tpl {
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 ld8(const f16* p) {
+  return *reinterpret_cast<const f16x8*>(p);
+}
+
+__device__ __forceinline__ f16x8 pack8(const float* v) {
+  uint4 u;
+  u.x = pack2h(v[0], v[1]);
+  u.y = pack2h(v[2], v[3]);
+  u.z = pack2h(v[4], v[5]);
+  u.w = pack2h(v[6], v[7]);
+  return __builtin_bit_cast(f16x8, u);
+}
+
+__device__ __forceinline__ void transpose8x8_b16(const uint4 r[8], uint4 w[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t* lo = reinterpret_cast<const uint32_t*>(&r[2 * p]);
+      const uint32_t* hi = reinterpret_cast<const uint32_t*>(&r[2 * p + 1]);
+      o[p] = __builtin_amdgcn_perm(hi[j >> 1], lo[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+    }
+    w[j] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Row (within a block of rows) stored at LDS position 8*g + s of a transposed
+// tile: position p = 16c + 8h + s holds row 16c + 4h + s (s < 4) or
+// 16c + 8 + 4h + (s - 4) (s >= 4) -- the order a 32x32 accumulator column
+// holds its rows in, two 16-row MFMA steps per 32 rows.
+__device__ __forceinline__ int perm_row(int g, int s) {
+  const int c = g >> 1, h = g & 1;
+  return 16 * c + (s < 4 ? 4 * h + s : 8 + 4 * h + (s - 4));
+}
+
+// Stores rows [r0, r0+R) x D of a row-major 16-bit matrix (row stride ld) into
+// LDS transposed: dst[d * ldt + position]. Rows >= nrows are zero. One 8x8
+// block per thread-iteration.
+template <int R, int D>
+__device__ __forceinline__ void load_transposed(const f16* __restrict__ src, long ld, int r0,
+                                                int nrows, f16* dst, int ldt, int tid, int nt) {
+  constexpr int nblk = (R / 8) * (D / 8);
+  for (int bidx = tid; bidx < nblk; bidx += nt) {
+    const int g = bidx % (R / 8), dg = bidx / (R / 8);
+    uint4 r[8], w[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int row = r0 + perm_row(g, s);
+      r[s] = row < nrows ? *reinterpret_cast<const uint4*>(src + (size_t)row * ld + 8 * dg)
+                         : make_uint4(0, 0, 0, 0);
+    }
+    transpose8x8_b16(r, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dst + (8 * dg + e) * ldt + 8 * g) = w[e];
+  }
+}
+
+// Row-major copy of rows [r0, r0+R) x D into LDS (row stride ldr).
+template <int R, int D>
+__device__ __forceinline__ void load_rows(const f16* __restrict__ src, long ld, int r0, int nrows,
+                                          f16* dst, int ldr, int tid, int nt) {
+  constexpr int nch = R * (D / 8);
+  for (int c = tid; c < nch; c += nt) {
+    const int row = c / (D / 8), dc = c % (D / 8);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + row < nrows) v = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + row) * ld + 8 * dc);
+    *reinterpret_cast<uint4*>(dst + row * ldr + 8 * dc) = v;
+  }
+}
+
+// ============================================================================
+// fp16 forward
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
+    const f16* __restrict__ qkv, f16* __restrict__ o, float* __restrict__ lse2,
+    const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2) {
+  constexpr int KB = 64, LDK = D + 8, LDV = KB + 8;
+  extern __shared__ __align__(16) unsigned char smem[];
+  f16* Ks = reinterpret_cast<f16*>(smem);  // [KB][LDK]
+  f16* Vt = Ks + KB * LDK;                   // [D][LDV]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int qb = causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int qw0 = qb * 128 + w * 32;
+  const int q = qw0 + l32;
+  const long ldq = 3L * Hl * D, ldo = (long)Hl * D;
+  const size_t tok0 = (size_t)b * seq;
+  const f16* Qp = qkv + tok0 * ldq + (size_t)head * 3 * D;
+  const f16* Kp = Qp + D;
+  const f16* Vp = Qp + 2 * D;
+  const int L = causal ? seq : min(max(valid_len[b], 0), seq);
+  const int kv_end = causal ? min(seq, qb * 128 + 128) : L;
+  const int lim = causal ? min(q + 1, seq) : L;  // this lane's keys are [0, lim)
+
+  f16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (q < seq) v = *reinterpret_cast<const uint4*>(Qp + (size_t)q * ldq + 16 * ks + 8 * hh);
+    qf[ks] = __builtin_bit_cast(f16x8, v);
+  }
+  f32x16 O[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) O[t][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int kb0 = 0; kb0 < kv_end; kb0 += KB) {
+    __syncthreads();
+    load_rows<KB, D>(Kp, ldq, kb0, seq, Ks, LDK, tid, 256);
+    load_transposed<KB, D>(Vp, ldq, kb0, seq, Vt, LDV, tid, 256);
+    __syncthreads();
+    if (causal && kb0 > qw0 + 31) continue;  // every key after every query of this wave
+
+    f32x16 S[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[st][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        S[st] = mfma32(ld8(Ks + (32 * st + l32) * LDK + 16 * ks + 8 * hh), qf[ks], S[st]);
+    }
+    // S[st][4*jj+ii]: key kb0 + 32*st + 8*jj + 4*hh + ii, query q
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const float s = key < lim ? S[st][e] * sl2 : -INFINITY;
+        S[st][e] = s;
+        mx = fmaxf(mx, s);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float ls = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2f(S[st][e] - m_new);
+        S[st][e] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) O[t][e] *= alpha;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float pv[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) pv[s] = S[c >> 1][8 * (c & 1) + s];
+      const f16x8 pf = pack8(pv);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+        O[t] = mfma32(ld8(Vt + (32 * t + l32) * LDV + 16 * c + 8 * hh), pf, O[t]);
+    }
+  }
+
+  if (q < seq) {
+    const float inv = 1.f / l_run;
+    f16* op = o + (tok0 + q) * ldo + (size_t)head * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float v[4] = {O[t][4 * jj] * inv, O[t][4 * jj + 1] * inv, O[t][4 * jj + 2] * inv,
+                      O[t][4 * jj + 3] * inv};
+        Vec4<f16>::store(op + 32 * t + 8 * jj + 4 * hh, v);
+      }
+    if (hh == 0) lse2[((size_t)b * Hl + head) * seq + q] = m_run + log2f(l_run);
+  }
+}
+
+// ============================================================================
+// delta = rowsum(dO * O) per (token, head), fp32
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o,
+                                                         const T* __restrict__ dO,
+                                                         float* __restrict__ delta, int seq,
+                                                         int Hl, int D, long ntasks) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= ntasks) return;
+  const long tok = idx / Hl;
+  const int head = (int)(idx % Hl);
+  const T* a = o + tok * Hl * D + (long)head * D;
+  const T* g = dO + tok * Hl * D + (long)head * D;
+  float acc = 0.f;
+  for (int d = 0; d < D; d += 8) {
+    float x[8], y[8];
+    Vec8<T>::load(a + d, x);
+    Vec8<T>::load(g + d, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
+  }
+  const long b = tok / seq, q = tok % seq;
+  delta[(b * Hl + head) * seq + q] = acc;
+}
+
+// ============================================================================
+// fp16 backward: dK, dV (a workgroup owns 128 keys, 32 per wave)
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
+    const f16* __restrict__ qkv, const f16* __restrict__ dO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, f16* __restrict__ dqkv, const int* __restrict__ valid_len,
+    int seq, int Hl, int causal, float sl2, float scale) {
+  constexpr int QB = 32, LDR = D + 8, LDT = QB + 8;
+  extern __shared__ __align__(16) unsigned char smem[];
+  f16* Qs = reinterpret_cast<f16*>(smem);  // [QB][LDR]
+  f16* dOs = Qs + QB * LDR;                  // [QB][LDR]
+  f16* Qt = dOs + QB * LDR;                  // [D][LDT]
+  f16* dOt = Qt + D * LDT;                   // [D][LDT]
+  float* ls = reinterpret_cast<float*>(dOt + D * LDT);  // [QB]
+  float* dl = ls + QB;                                   // [QB]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int kblk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int kw0 = kblk * 128 + w * 32;
+  const int key = kw0 + l32;
+  const long ldq = 3L * Hl * D, ldo = (long)Hl * D;
+  const size_t tok0 = (size_t)b * seq;
+  const f16* Qp = qkv + tok0 * ldq + (size_t)head * 3 * D;
+  const f16* Kp = Qp + D;
+  const f16* Vp = Qp + 2 * D;
+  const f16* dOp = dO + tok0 * ldo + (size_t)head * D;
+  const float* lsp = lse2 + ((size_t)b * Hl + head) * seq;
+  const float* dlp = delta + ((size_t)b * Hl + head) * seq;
+  const int L = causal ? seq : min(max(valid_len[b], 0), seq);
+
+  f16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (key < seq) {
+      kv = *reinterpret_cast<const uint4*>(Kp + (size_t)key * ldq + 16 * ks + 8 * hh);
+      vv = *reinterpret_cast<const uint4*>(Vp + (size_t)key * ldq + 16 * ks + 8 * hh);
+    }
+    kf[ks] = __builtin_bit_cast(f16x8, kv);
+    vf[ks] = __builtin_bit_cast(f16x8, vv);
+  }
+  f32x16 dK[D / 32], dV[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dK[t][e] = dV[t][e] = 0.f;
+
+  const bool wave_keys_valid = kw0 < (causal ? seq : L);
+  const int q_begin = causal ? kblk * 128 : 0;
+  for (int q0 = q_begin; q0 < seq; q0 += QB) {
+    __syncthreads();
+    load_rows<QB, D>(Qp, ldq, q0, seq, Qs, LDR, tid, 256);
+    load_rows<QB, D>(dOp, ldo, q0, seq, dOs, LDR, tid, 256);
+    load_transposed<QB, D>(Qp, ldq, q0, seq, Qt, LDT, tid, 256);
+    load_transposed<QB, D>(dOp, ldo, q0, seq, dOt, LDT, tid, 256);
+    if (tid < QB) {
+      const int qq = q0 + tid;
+      ls[tid] = qq < seq ? lsp[qq] : 0.f;
+      dl[tid] = qq < seq ? dlp[qq] : 0.f;
+    }
+    __syncthreads();
+    if (!wave_keys_valid || (causal && q0 + QB - 1 < kw0)) continue;
+
+    f32x16 S, dP;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      S = mfma32(ld8(Qs + l32 * LDR + 16 * ks + 8 * hh), kf[ks], S);
+      dP = mfma32(ld8(dOs + l32 * LDR + 16 * ks + 8 * hh), vf[ks], dP);
+    }
+    // element e: query q0 + 8*(e>>2) + 4*hh + (e&3), key = this lane's key
+    float P[16], dS[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int qr = 8 * (e >> 2) + 4 * hh + (e & 3);
+      const int qq = q0 + qr;
+      const bool ok = qq < seq && key < L && (!causal || key <= qq);
+      const float p = ok ? exp2f(S[e] * sl2 - ls[qr]) : 0.f;
+      P[e] = p;
+      dS[e] = p * (dP[e] - dl[qr]);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f16x8 pf = pack8(P + 8 * c);
+      const f16x8 sf = pack8(dS + 8 * c);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        dV[t] = mfma32(ld8(dOt + (32 * t + l32) * LDT + 16 * c + 8 * hh), pf, dV[t]);
+        dK[t] = mfma32(ld8(Qt + (32 * t + l32) * LDT + 16 * c + 8 * hh), sf, dK[t]);
+      }
+    }
+  }
+
+  if (key < seq) {
+    f16* dk = dqkv + (tok0 + key) * ldq + (size_t)head * 3 * D + D;
+    f16* dv = dk + D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float a[4], c[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dK[t][4 * jj + e] * scale;
+          c[e] = dV[t][4 * jj + e];
+        }
+        Vec4<f16>::store(dk + 32 * t + 8 * jj + 4 * hh, a);
+        Vec4<f16>::store(dv + 32 * t + 8 * jj + 4 * hh, c);
+      }
+  }
+}
+
+// ============================================================================
+// fp16 backward: dQ (a workgroup owns 128 queries, 32 per wave)
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
+    const f16* __restrict__ qkv, const f16* __restrict__ dO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, f16* __restrict__ dqkv, const int* __restrict__ valid_len,
+    int seq, int Hl, int causal, float sl2, float scale) {
+  constexpr int KB = 64, LDR = D + 8, LDT = KB + 8;
+  extern __shared__ __align__(16) unsigned char smem[];
+  f16* Ks = reinterpret_cast<f16*>(smem);  // [KB][LDR]
+  f16* Vs = Ks + KB * LDR;                   // [KB][LDR]
+  f16* Kt = Vs + KB * LDR;                   // [D][LDT]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int qb = causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int qw0 = qb * 128 + w * 32;
+  const int q = qw0 + l32;
+  const long ldq = 3L * Hl * D, ldo = (long)Hl * D;
+  const size_t tok0 = (size_t)b * seq;
+  const f16* Qp = qkv + tok0 * ldq + (size_t)head * 3 * D;
+  const f16* Kp = Qp + D;
+  const f16* Vp = Qp + 2 * D;
+  const f16* dOp = dO + tok0 * ldo + (size_t)head * D;
+  const int L = causal ? seq : min(max(valid_len[b], 0), seq);
+  const int kv_end = causal ? min(seq, qb * 128 + 128) : L;
+  const int lim = causal ? min(q + 1, seq) : L;
+  const bool qok = q < seq;
+  const float lq = qok ? lse2[((size_t)b * Hl + head) * seq + q] : 0.f;
+  const float dq_ = qok ? delta[((size_t)b * Hl + head) * seq + q] : 0.f;
+
+  f16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
+    if (qok) {
+      a = *reinterpret_cast<const uint4*>(Qp + (size_t)q * ldq + 16 * ks + 8 * hh);
+      c = *reinterpret_cast<const uint4*>(dOp + (size_t)q * ldo + 16 * ks + 8 * hh);
+    }
+    qf[ks] = __builtin_bit_cast(f16x8, a);
+    gf[ks] = __builtin_bit_cast(f16x8, c);
+  }
+  f32x16 dQ[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dQ[t][e] = 0.f;
+
+  for (int kb0 = 0; kb0 < kv_end; kb0 += KB) {
+    __syncthreads();
+    load_rows<KB, D>(Kp, ldq, kb0, seq, Ks, LDR, tid, 256);
+    load_rows<KB, D>(Vp, ldq, kb0, seq, Vs, LDR, tid, 256);
+    load_transposed<KB, D>(Kp, ldq, kb0, seq, Kt, LDT, tid, 256);
+    __syncthreads();
+    if (causal && kb0 > qw0 + 31) continue;
+
+    float dS[2][16];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      f32x16 S, dP;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        S = mfma32(ld8(Ks + (32 * st + l32) * LDR + 16 * ks + 8 * hh), qf[ks], S);
+        dP = mfma32(ld8(Vs + (32 * st + l32) * LDR + 16 * ks + 8 * hh), gf[ks], dP);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const float p = (qok && key < lim) ? exp2f(S[e] * sl2 - lq) : 0.f;
+        dS[st][e] = p * (dP[e] - dq_);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x8 sf = pack8(&dS[c >> 1][8 * (c & 1)]);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+        dQ[t] = mfma32(ld8(Kt + (32 * t + l32) * LDT + 16 * c + 8 * hh), sf, dQ[t]);
+    }
+  }
+
+  if (qok) {
+    f16* dq = dqkv + (tok0 + q) * ldq + (size_t)head * 3 * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = dQ[t][4 * jj + e] * scale;
+        Vec4<f16>::store(dq + 32 * t + 8 * jj + 4 * hh, a);
+      }
+  }
+}
+
+// ============================================================================
+// fp32 kernels: one thread per query (forward, dQ) or per key (dK, dV)
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restrict__ qkv,
+                                                         float* __restrict__ o,
+                                                         float* __restrict__ lse2,
+                                                         const int* __restrict__ valid_len,
+                                                         int batch, int seq, int Hl, int causal,
+                                                         float sl2) {
+  const long idx = (long)blockIdx.x * 64 + threadIdx.x;
+  if (idx >= (long)batch * Hl * seq) return;
+  const int q = (int)(idx % seq);
+  const int head = (int)((idx / seq) % Hl);
+  const int b = (int)(idx / ((long)seq * Hl));
+  const long ldq = 3L * Hl * D;
+  const float* base = qkv + (size_t)b * seq * ldq + (size_t)head * 3 * D;
+  const int lim = causal ? q + 1 : min(max(valid_len[b], 0), seq);
+  float qv[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qv[d] = base[(size_t)q * ldq + d];
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int k = 0; k < lim; ++k) {
+    const float* kr = base + (size_t)k * ldq + D;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = fmaf(qv[d], kr[d], s);
+    s *= sl2;
+    const float mn = fmaxf(m, s);
+    const float a = exp2f(m - mn), p = exp2f(s - mn);
+    l = l * a + p;
+    const float* vr = kr + D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = acc[d] * a + p * vr[d];
+    m = mn;
+  }
+  float* op = o + ((size_t)b * seq + q) * Hl * D + (size_t)head * D;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
+  lse2[((size_t)b * Hl + head) * seq + q] = m + log2f(l);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(
+    const float* __restrict__ qkv, const float* __restrict__ dO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, float* __restrict__ dqkv, const int* __restrict__ valid_len,
+    int batch, int seq, int Hl, int causal, float sl2, float scale) {
+  const long idx = (long)blockIdx.x * 64 + threadIdx.x;
+  if (idx >= (long)batch * Hl * seq) return;
+  const int q = (int)(idx % seq);
+  const int head = (int)((idx / seq) % Hl);
+  const int b = (int)(idx / ((long)seq * Hl));
+  const long ldq = 3L * Hl * D, ldo = (long)Hl * D;
+  const float* base = qkv + (size_t)b * seq * ldq + (size_t)head * 3 * D;
+  const float* g = dO + ((size_t)b * seq + q) * ldo + (size_t)head * D;
+  const size_t si = ((size_t)b * Hl + head) * seq + q;
+  const float lq = lse2[si], dl = delta[si];
+  const int lim = causal ? q + 1 : min(max(valid_len[b], 0), seq);
+  float qv[D], gv[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qv[d] = base[(size_t)q * ldq + d];
+    gv[d] = g[d];
+    acc[d] = 0.f;
+  }
+  for (int k = 0; k < lim; ++k) {
+    const float* kr = base + (size_t)k * ldq + D;
+    const float* vr = kr + D;
+    float s = 0.f, dp = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      s = fmaf(qv[d], kr[d], s);
+      dp = fmaf(gv[d], vr[d], dp);
+    }
+    const float p = exp2f(s * sl2 - lq);
+    const float ds = p * (dp - dl);
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
+  }
+  float* out = dqkv + ((size_t)b * seq + q) * ldq + (size_t)head * 3 * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) out[d] = acc[d] * scale;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(
+    const float* __restrict__ qkv, const float* __restrict__ dO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, float* __restrict__ dqkv, const int* __restrict__ valid_len,
+    int batch, int seq, int Hl, int causal, float sl2, float scale) {
+  const long idx = (long)blockIdx.x * 64 + threadIdx.x;
+  if (idx >= (long)batch * Hl * seq) return;
+  const int k = (int)(idx % seq);
+  const int head = (int)((idx / seq) % Hl);
+  const int b = (int)(idx / ((long)seq * Hl));
+  const long ldq = 3L * Hl * D, ldo = (long)Hl * D;
+  const float* base = qkv + (size_t)b * seq * ldq + (size_t)head * 3 * D;
+  const float* lsp = lse2 + ((size_t)b * Hl + head) * seq;
+  const float* dlp = delta + ((size_t)b * Hl + head) * seq;
+  const bool valid = causal ? true : k < min(valid_len[b], seq);
+  float kv[D], vv[D], dk[D], dv[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    kv[d] = base[(size_t)k * ldq + D + d];
+    vv[d] = base[(size_t)k * ldq + 2 * D + d];
+    dk[d] = dv[d] = 0.f;
+  }
+  if (valid) {
+    for (int q = causal ? k : 0; q < seq; ++q) {
+      const float* qr = base + (size_t)q * ldq;
+      const float* g = dO + ((size_t)b * seq + q) * ldo + (size_t)head * D;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(qr[d], kv[d], s);
+        dp = fmaf(g[d], vv[d], dp);
+      }
+      const float p = exp2f(s * sl2 - lsp[q]);
+      const float ds = p * (dp - dlp[q]);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        dv[d] = fmaf(p, g[d], dv[d]);
+        dk[d] = fmaf(ds, qr[d], dk[d]);
+      }
+    }
+  }
+  float* out = dqkv + ((size_t)b * seq + k) * ldq + (size_t)head * 3 * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    out[D + d] = dk[d] * scale;
+    out[2 * D + d] = dv[d];
+  }
+}
+
+// ============================================================================
+// Host launchers
+// ============================================================================
+template <int D>
+static size_t fwd_lds() { return (size_t)(64 * (D + 8) + D * 72) * 2; }
+template <int D>
+static size_t dkdv_lds() { return (size_t)(2 * 32 * (D + 8) + 2 * D * 40) * 2 + 2 * 32 * 4; }
+template <int D>
+static size_t dq_lds() { return (size_t)(2 * 64 * (D + 8) + D * 72) * 2; }
+
+template <typename K>
+static hipError_t set_lds(K kern, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+template <int D>
+static hipError_t fwd_d(int dtype, const void* qkv, void* o, float* lse2, const int* vl,
+                        int batch, int seq, int Hl, int causal, float sl2, hipStream_t s) {
+  if (dtype == DT_F16) {
+    auto k = attn_fwd_f16_kernel<D>;
+    hipError_t e = set_lds(k, fwd_lds<D>());
+    if (e != hipSuccess) return e;
+    dim3 grid((seq + 127) / 128, Hl, batch);
+    hipLaunchKernelGGL(k, grid, dim3(256), fwd_lds<D>(), s, (const f16*)qkv, (f16*)o, lse2, vl,
+                       seq, Hl, causal, sl2);
+  } else {
+    const long n = (long)batch * Hl * seq;
+    attn_fwd_f32_kernel<D><<<(unsigned)((n + 63) / 64), 64, 0, s>>>(
+        (const float*)qkv, (float*)o, lse2, vl, batch, seq, Hl, causal, sl2);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t bwd_d(int dtype, const void* qkv, const void* dO, const float* lse2,
+                        const float* delta, void* dqkv, const int* vl, int batch, int seq, int Hl,
+                        int causal, float sl2, float scale, hipStream_t s) {
+  if (dtype == DT_F16) {
+    auto k1 = attn_bwd_dkdv_f16_kernel<D>;
+    auto k2 = attn_bwd_dq_f16_kernel<D>;
+    hipError_t e = set_lds(k1, dkdv_lds<D>());
+    if (e == hipSuccess) e = set_lds(k2, dq_lds<D>());
+    if (e != hipSuccess) return e;
+    dim3 grid((seq + 127) / 128, Hl, batch);
+    hipLaunchKernelGGL(k1, grid, dim3(256), dkdv_lds<D>(), s, (const f16*)qkv, (const f16*)dO,
+                       lse2, delta, (f16*)dqkv, vl, seq, Hl, causal, sl2, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k2, grid, dim3(256), dq_lds<D>(), s, (const f16*)qkv, (const f16*)dO,
+                       lse2, delta, (f16*)dqkv, vl, seq, Hl, causal, sl2, scale);
+  } else {
+    const long n = (long)batch * Hl * seq;
+    const unsigned g = (unsigned)((n + 63) / 64);
+    attn_bwd_dkdv_f32_kernel<D><<<g, 64, 0, s>>>((const float*)qkv, (const float*)dO, lse2, delta,
+                                                 (float*)dqkv, vl, batch, seq, Hl, causal, sl2,
+                                                 scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    attn_bwd_dq_f32_kernel<D><<<g, 64, 0, s>>>((const float*)qkv, (const float*)dO, lse2, delta,
+                                               (float*)dqkv, vl, batch, seq, Hl, causal, sl2,
+                                               scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t attn_fwd(int dtype, const void* qkv, void* o, float* lse2, const int* valid_len,
+                    int batch, int seq, int Hl, int D, int mask, hipStream_t s) {
+  if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
+  const int causal = mask == 0;
+  const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
+  switch (D) {
+    case 32: return fwd_d<32>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 64: return fwd_d<64>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 96: return fwd_d<96>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 128: return fwd_d<128>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 160: return fwd_d<160>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse2,
+                    float* delta, void* dqkv, const int* valid_len, int batch, int seq, int Hl,
+                    int D, int mask, hipStream_t s) {
+  if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
+  const long ntasks = (long)batch * seq * Hl;
+  if (dtype == DT_F16)
+    attn_delta_kernel<f16><<<(unsigned)((ntasks + 255) / 256), 256, 0, s>>>(
+        (const f16*)o, (const f16*)dO, delta, seq, Hl, D, ntasks);
+  else
+    attn_delta_kernel<float><<<(unsigned)((ntasks + 255) / 256), 256, 0, s>>>(
+        (const float*)o, (const float*)dO, delta, seq, Hl, D, ntasks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int causal = mask == 0;
+  const double sc = 1.0 / sqrt((double)D);
+  const float sl2 = (float)(1.4426950408889634 * sc), scale = (float)sc;
+  switch (D) {
+    case 32: return bwd_d<32>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 64: return bwd_d<64>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 96: return bwd_d<96>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 128: return bwd_d<128>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 160: return bwd_d<160>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tpl

@@ -1,0 +1,201 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels of the TP layer shard.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpl {
+
+typedef uint16_t bf16;  // storage of bfloat16 values (upper half of an fp32)
+typedef _Float16 f16;   // IEEE binary16 (internal activations of the bf16 path)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(bf16 v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+// Round to nearest even (gfx950 has a hardware conversion for this).
+__device__ __forceinline__ bf16 f2bf(float v) {
+  return __builtin_bit_cast(bf16, (__bf16)v);
+}
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Two floats to packed fp16, round to nearest even.
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+  f16x2 h = {(f16)lo, (f16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+// 8 bf16 values to 8 fp16 values. Every normal bf16 value inside the fp16
+// range is exactly representable, so the rounding mode only matters for
+// values below fp16's normal range (absolute error < 2^-24).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16),
+                                        __uint_as_float(w[i] & 0xffff0000u));
+    w[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---- 8-element vector I/O for float, bf16 and fp16 storage -------------------
+template <typename T> struct Vec8;
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float v[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float v[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+template <> struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float v[8]) {
+    uint4 a = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16* p, const float v[8]) {
+    uint4 a;
+    a.x = pack2(v[0], v[1]);
+    a.y = pack2(v[2], v[3]);
+    a.z = pack2(v[4], v[5]);
+    a.w = pack2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = a;
+  }
+};
+
+template <> struct Vec8<f16> {
+  static __device__ __forceinline__ void load(const f16* p, float v[8]) {
+    f16x8 a = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+  }
+  static __device__ __forceinline__ void store(f16* p, const float v[8]) {
+    uint4 a;
+    a.x = pack2h(v[0], v[1]);
+    a.y = pack2h(v[2], v[3]);
+    a.z = pack2h(v[4], v[5]);
+    a.w = pack2h(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = a;
+  }
+};
+
+// 4-element vector I/O (epilogues write 4 consecutive columns per lane).
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float* p, float v[4]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float v[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct Vec4<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float v[4]) {
+    uint2 a = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(a.x << 16);
+    v[1] = __uint_as_float(a.x & 0xffff0000u);
+    v[2] = __uint_as_float(a.y << 16);
+    v[3] = __uint_as_float(a.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void store(bf16* p, const float v[4]) {
+    uint2 a;
+    a.x = pack2(v[0], v[1]);
+    a.y = pack2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(p) = a;
+  }
+};
+
+template <> struct Vec4<f16> {
+  static __device__ __forceinline__ void load(const f16* p, float v[4]) {
+    uint2 a = *reinterpret_cast<const uint2*>(p);
+    f16x2 x = __builtin_bit_cast(f16x2, a.x), y = __builtin_bit_cast(f16x2, a.y);
+    v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)y[0]; v[3] = (float)y[1];
+  }
+  static __device__ __forceinline__ void store(f16* p, const float v[4]) {
+    uint2 a;
+    a.x = pack2h(v[0], v[1]);
+    a.y = pack2h(v[2], v[3]);
+    *reinterpret_cast<uint2*>(p) = a;
+  }
+};
+
+// Runtime-typed 4-element access (dtype codes of kernels.hpp: 0 f32, 1 bf16, 2 f16).
+__device__ __forceinline__ void load4_dt(const void* base, int dt, size_t off, float v[4]) {
+  if (dt == 0) Vec4<float>::load((const float*)base + off, v);
+  else if (dt == 1) Vec4<bf16>::load((const bf16*)base + off, v);
+  else Vec4<f16>::load((const f16*)base + off, v);
+}
+__device__ __forceinline__ void store4_dt(void* base, int dt, size_t off, const float v[4]) {
+  if (dt == 0) Vec4<float>::store((float*)base + off, v);
+  else if (dt == 1) Vec4<bf16>::store((bf16*)base + off, v);
+  else Vec4<f16>::store((f16*)base + off, v);
+}
+
+// ---- reductions ---------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Sum of NV values over the whole block (blockDim.x a multiple of 64, at
+// most 1024). `red` must hold 16*NV floats. All threads get the result.
+template <int NV>
+__device__ __forceinline__ void block_sum(float (&v)[NV], float* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
+  __syncthreads();  // `red` may still be read by a previous call
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) red[wid * NV + i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += red[w * NV + i];
+    v[i] = s;
+  }
+}
+
+// ---- GeLU (exact erf form, or the tanh approximation) ---------------------------
+__device__ __forceinline__ float gelu_f(float u, int tanh_form) {
+  if (tanh_form) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * u * (1.f + tanhf(c * (u + 0.044715f * u * u * u)));
+  }
+  return 0.5f * u * (1.f + erff(u * 0.7071067811865476f));
+}
+__device__ __forceinline__ float gelu_grad_f(float u, int tanh_form) {
+  if (tanh_form) {
+    const float c = 0.7978845608028654f;
+    float th = tanhf(c * (u + 0.044715f * u * u * u));
+    return 0.5f * (1.f + th) + 0.5f * u * (1.f - th * th) * c * (1.f + 0.134145f * u * u);
+  }
+  // Phi(u) + u * phi(u)
+  return 0.5f * (1.f + erff(u * 0.7071067811865476f)) +
+         u * 0.3989422804014327f * expf(-0.5f * u * u);
+}
+
+}  // namespace tpl

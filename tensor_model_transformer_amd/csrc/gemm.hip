@@ -1,0 +1,466 @@
+// GEMMs of the layer shard: C[M,N] = A[M,K] @ B[K,N] with fused epilogues.
+//
+// The four projections of "Megatron-LM: GPU-Cluster Training Parallelism",
+// section "Paper 1: The f/g Conjugate Operators" (column-parallel QKV and FC1,
+// row-parallel output projection and FC2) and their data/weight gradients.
+// Epilogue fusions follow section "Fused Transformer Kernels": bias + GeLU
+// after FC1, bias + residual after the row-parallel GEMMs; backward adds the
+// GeLU derivative to the FC2 data-gradient epilogue.
+//
+// 16-bit path: MFMA 32x32x16 on fp16 operands (v_mfma_f32_32x32x16_f16,
+// fp32 accumulate; the same rate as bf16 on gfx950) on LDS double-buffered
+// tiles. Internal activations are fp16; bf16 tensors at the layer boundary
+// (weights, the upstream gradient) are converted to fp16 as they are staged,
+// which is exact for every bf16 value in fp16's normal range. LDS always
+// holds both operands K-contiguous ([rows][BK+8], 16-byte padding against
+// bank conflicts) so every MFMA operand
+// is one 16-byte LDS read. Operands that are contiguous along M or N in HBM
+// (weights [in,out] in forward; both operands of a weight gradient) are
+// transposed in registers, 8x8 blocks of 16-bit values at a time, between the global load
+// and the LDS store. The MFMA is issued with B as the first operand, so the
+// accumulator holds C transposed: each lane owns one output row and 4
+// consecutive columns per 32x32 tile, which the epilogue writes as one vector.
+//
+// fp32 path: a plain tiled FMA kernel (exact fp32 arithmetic).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace tpl {
+
+// ----------------------------------------------------------------------------
+// Epilogue on 4 consecutive columns n..n+3 of row m (N % 4 == 0).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float v[4]) {
+  if (m >= g.M || n >= g.N) return;
+  if (g.bias) {
+    float b[4];
+    load4_dt(g.bias, g.bias_dtype, n, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += b[e];
+  }
+  if (g.resid) {
+    float r[4];
+    load4_dt(g.resid, g.resid_dtype, (size_t)m * g.ldr + n, r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += r[e];
+  }
+  if (g.epi == EPI_BIAS_GELU) {
+    float z[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = gelu_f(v[e], g.gelu_tanh);
+    store4_dt(g.C2, g.c2_dtype, (size_t)m * g.ldc2 + n, z);
+  } else if (g.epi == EPI_DGELU) {
+    float u[4];
+    load4_dt(g.aux, g.aux_dtype, (size_t)m * g.ldaux + n, u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e], g.gelu_tanh);
+  }
+  const size_t off = (size_t)m * g.ldc + n;
+  if (g.accumulate && g.c_dtype == DT_F32) {
+    float o[4];
+    Vec4<float>::load((const float*)g.C + off, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += o[e];
+  }
+  store4_dt(g.C, g.c_dtype, off, v);
+}
+
+// Split-K partial (raw accumulator) store.
+__device__ __forceinline__ void partial4(const GemmArgs& g, int split_idx, int m, int n,
+                                         const float v[4]) {
+  if (m >= g.M || n >= g.N) return;
+  Vec4<float>::store(g.ws + ((size_t)split_idx * g.M + m) * g.N + n, v);
+}
+
+// ----------------------------------------------------------------------------
+// fp16 MFMA GEMM
+// ----------------------------------------------------------------------------
+// In-register transpose of an 8x8 block of 16-bit values: r[i] holds 8 elements of
+// source row i; w[j] receives element j of every source row.
+__device__ __forceinline__ void transpose8x8(const uint4 r[8], uint4 w[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t* lo = reinterpret_cast<const uint32_t*>(&r[2 * p]);
+      const uint32_t* hi = reinterpret_cast<const uint32_t*>(&r[2 * p + 1]);
+      // low half <- element j of row 2p, high half <- element j of row 2p+1
+      o[p] = __builtin_amdgcn_perm(hi[j >> 1], lo[j >> 1],
+                                   (j & 1) ? 0x07060302u : 0x05040100u);
+    }
+    w[j] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+template <int ROWS, int BK, int NT, bool KMAJ>
+struct TileLoader {
+  // K-contiguous source: 16-byte chunks of 8 k-values; ROWS*BK/8 chunks.
+  // Row-contiguous source: 8(k) x 8(row) blocks; ROWS*BK/64 blocks.
+  static constexpr int kChunks = ROWS * BK / 8;
+  static constexpr int kPer = KMAJ ? (kChunks + NT - 1) / NT : 8 * ((ROWS * BK / 64 + NT - 1) / NT);
+  uint4 st[kPer];
+  bool cvt;  // the source is bf16: convert to fp16 when staging into LDS
+
+  // src(row, k) = KMAJ ? p[row*ld + k] : p[k*ld + row]; 16-bit elements.
+  // The loaded registers are consumed only by store(), after the MFMAs of
+  // the current tile, so the global-load latency overlaps the compute.
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ p, long ld, int row0, int nrows,
+                                       int k0, int K, int tid) {
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int c = tid + i * NT;
+        const int row = c / (BK / 8), kc = c % (BK / 8);
+        const int gr = row0 + row, gk = k0 + 8 * kc;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (c < kChunks && gr < nrows && gk < K)
+          v = *reinterpret_cast<const uint4*>(p + (size_t)gr * ld + gk);
+        st[i] = v;
+      }
+    } else {
+      constexpr int nblk = ROWS * BK / 64;
+#pragma unroll
+      for (int i = 0; i < kPer / 8; ++i) {
+        const int b = tid + i * NT;
+        const int kb = b % (BK / 8), rb = b / (BK / 8);
+        const int gr = row0 + 8 * rb;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int gk = k0 + 8 * kb + r;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (b < nblk && gr < nrows && gk < K)
+            v = *reinterpret_cast<const uint4*>(p + (size_t)gk * ld + gr);
+          st[8 * i + r] = v;
+        }
+      }
+    }
+  }
+
+  // LDS tile: [ROWS][BK + 8] fp16, K-contiguous.
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) {
+    constexpr int LDK = BK + 8;
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int c = tid + i * NT;
+        const int row = c / (BK / 8), kc = c % (BK / 8);
+        if (c < kChunks)
+          *reinterpret_cast<uint4*>(lds + row * LDK + 8 * kc) = cvt ? bf16x8_to_f16x8(st[i]) : st[i];
+      }
+    } else {
+      constexpr int nblk = ROWS * BK / 64;
+#pragma unroll
+      for (int i = 0; i < kPer / 8; ++i) {
+        const int b = tid + i * NT;
+        const int kb = b % (BK / 8), rb = b / (BK / 8);
+        if (b < nblk) {
+          uint4 w[8];
+          if (cvt) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) st[8 * i + r] = bf16x8_to_f16x8(st[8 * i + r]);
+          }
+          transpose8x8(&st[8 * i], w);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<uint4*>(lds + (8 * rb + j) * LDK + 8 * kb) = w[j];
+        }
+      }
+    }
+  }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int ktiles_per_split) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int LDK = BK + 8;
+  static_assert(TM >= 1 && TN >= 1 && BK % 16 == 0, "tile shape");
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);       // [2][BM*LDK] fp16
+  uint16_t* Bs = As + 2 * BM * LDK;                       // [2][BN*LDK] fp16
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const int tile = blockIdx.x;
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  const int split_idx = blockIdx.y;
+  const int ktiles = (g.K + BK - 1) / BK;
+  const int kt0 = split_idx * ktiles_per_split;
+  const int kt1 = min(ktiles, kt0 + ktiles_per_split);
+
+  const uint16_t* A = (const uint16_t*)g.A;
+  const uint16_t* B = (const uint16_t*)g.B;
+  TileLoader<BM, BK, NT, AK> la;
+  TileLoader<BN, BK, NT, BKM> lb;
+  la.cvt = g.a_dtype == DT_BF16;
+  lb.cvt = g.b_dtype == DT_BF16;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  if (kt0 < kt1) {
+    la.load(A, g.lda, m0, g.M, kt0 * BK, g.K, tid);
+    lb.load(B, g.ldb, n0, g.N, kt0 * BK, g.K, tid);
+    la.store(As, tid);
+    lb.store(Bs, tid);
+    __syncthreads();
+  }
+  const int lrow = lane & 31, lk = 8 * (lane >> 5);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) {
+      la.load(A, g.lda, m0, g.M, (kt + 1) * BK, g.K, tid);
+      lb.load(B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, tid);
+    }
+    const uint16_t* as = As + cur * BM * LDK + (wm * WTM + lrow) * LDK + lk;
+    const uint16_t* bs = Bs + cur * BN * LDK + (wn * WTN + lrow) * LDK + lk;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      f16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const f16x8*>(as + i * 32 * LDK + ks * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const f16x8*>(bs + j * 32 * LDK + ks * 16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      la.store(As + (cur ^ 1) * BM * LDK, tid);
+      lb.store(Bs + (cur ^ 1) * BN * LDK, tid);
+    }
+    __syncthreads();
+  }
+
+  // acc[i][j][4*jj + e] = C[m][n] with m = row of this lane, n = 8*jj + 4*(lane/32) + e
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + lrow;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * jj + 4 * half;
+        float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
+                      acc[i][j][4 * jj + 3]};
+        if (gridDim.y > 1) partial4(g, split_idx, m, n, v);
+        else epilogue4(g, m, n, v);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// fp32 FMA GEMM (64x64 tiles, 16-deep K steps, 4x4 outputs per thread)
+// ----------------------------------------------------------------------------
+template <bool AK, bool BKM>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, int ktiles_per_split) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
+  const int ktiles = (g.K + BK - 1) / BK;
+  const int kt0 = blockIdx.y * ktiles_per_split;
+  const int kt1 = min(ktiles, kt0 + ktiles_per_split);
+  const float* A = (const float*)g.A;
+  const float* B = (const float*)g.B;
+  float acc[4][4] = {};
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * 256;
+      int r, k;
+      if (AK) { r = e / BK; k = e % BK; } else { k = e / BM; r = e % BM; }
+      const int gm = m0 + r, gk = k0 + k;
+      float v = 0.f;
+      if (gm < g.M && gk < g.K) v = AK ? A[(size_t)gm * g.lda + gk] : A[(size_t)gk * g.lda + gm];
+      As[k][r] = v;
+      int c;
+      if (BKM) { c = e / BK; k = e % BK; } else { k = e / BN; c = e % BN; }
+      const int gn = n0 + c;
+      const int gk2 = k0 + k;
+      float w = 0.f;
+      if (gn < g.N && gk2 < g.K) w = BKM ? B[(size_t)gn * g.ldb + gk2] : B[(size_t)gk2 * g.ldb + gn];
+      Bs[k][c] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+    if (gridDim.y > 1) partial4(g, blockIdx.y, m0 + ty * 4 + i, n0 + tx * 4, v);
+    else epilogue4(g, m0 + ty * 4 + i, n0 + tx * 4, v);
+  }
+}
+
+// Split-K reduction: C (+)= sum_s ws[s]  (fp32 output, plain store epilogue).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
+  const size_t nvec = (size_t)g.M * g.N / 4;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nvec) return;
+  const size_t idx = 4 * i;
+  const int m = (int)(idx / g.N), n = (int)(idx % g.N);
+  float acc[4], v[4];
+  Vec4<float>::load(g.ws + idx, acc);
+  for (int s = 1; s < g.split; ++s) {
+    Vec4<float>::load(g.ws + (size_t)s * g.M * g.N + idx, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += v[e];
+  }
+  float* c = (float*)g.C + (size_t)m * g.ldc + n;
+  if (g.accumulate) {
+    Vec4<float>::load(c, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += v[e];
+  }
+  Vec4<float>::store(c, acc);
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+struct TileCfg {
+  int bm, bn;
+};
+static constexpr TileCfg kBig = {256, 256};
+static constexpr TileCfg kSmall = {128, 128};
+static constexpr int kCUs = 256;
+
+static long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+static TileCfg choose_tile(int M, int N, int split) {
+  const long tb = ceil_div(M, kBig.bm) * ceil_div(N, kBig.bn) * split;
+  const long ts = ceil_div(M, kSmall.bm) * ceil_div(N, kSmall.bn) * split;
+  // one 256x256 workgroup per CU (LDS); two 128x128 ones, ~20% less efficient
+  const double cost_big = (double)ceil_div(tb, kCUs) * 65536.0;
+  const double cost_small = (double)ceil_div(ts, 2 * kCUs) * 2.0 * 16384.0 / 0.8;
+  return cost_big <= cost_small ? kBig : kSmall;
+}
+
+int gemm_choose_split(const GemmArgs& g) {
+  if (g.math != DT_F16) return 1;
+  if (g.epi != EPI_STORE || g.bias || g.resid || g.c_dtype != DT_F32) return 1;
+  const long tiles = ceil_div(g.M, kBig.bm) * ceil_div(g.N, kBig.bn);
+  const long ktiles = ceil_div(g.K, 64);
+  int best = 1;
+  double best_util = 0.0;
+  for (int s = 1; s <= 16; ++s) {
+    if (ktiles / s < 8) break;  // keep >= 8 K-tiles per split
+    const long w = tiles * s;
+    const double util = (double)w / (double)(kCUs * ceil_div(w, kCUs));
+    if (util > best_util + 0.05) {
+      best_util = util;
+      best = s;
+    }
+    if (util >= 0.85) break;
+  }
+  return best;
+}
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
+static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
+  constexpr int BK = 64;
+  constexpr int NT = WM * WN * 64;
+  const size_t lds = (size_t)2 * (BM + BN) * (BK + 8) * sizeof(uint16_t);
+  auto kern = gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM>;
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int ktiles = (int)ceil_div(g.K, BK);
+  const int per = (int)ceil_div(ktiles, split);
+  const int real_split = (int)ceil_div(ktiles, per);
+  dim3 grid((unsigned)(ceil_div(g.M, BM) * ceil_div(g.N, BN)), (unsigned)real_split);
+  GemmArgs a = g;
+  a.split = real_split;
+  hipLaunchKernelGGL(kern, grid, dim3(NT), lds, s, a, per);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || real_split == 1) return e;
+  const size_t nvec = (size_t)g.M * g.N / 4;
+  splitk_reduce_kernel<<<(unsigned)ceil_div((long)nvec, 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <bool AK, bool BKM>
+static hipError_t dispatch_f16(const GemmArgs& g, int split, hipStream_t s) {
+  const TileCfg t = choose_tile(g.M, g.N, split);
+  if (t.bm == 256) return launch_f16<256, 256, 2, 4, AK, BKM>(g, split, s);
+  return launch_f16<128, 128, 2, 2, AK, BKM>(g, split, s);
+}
+
+template <bool AK, bool BKM>
+static hipError_t launch_f32(const GemmArgs& g, int split, hipStream_t s) {
+  const int ktiles = (int)ceil_div(g.K, 16);
+  const int per = (int)ceil_div(ktiles, split);
+  const int real_split = (int)ceil_div(ktiles, per);
+  dim3 grid((unsigned)(ceil_div(g.M, 64) * ceil_div(g.N, 64)), (unsigned)real_split);
+  GemmArgs a = g;
+  a.split = real_split;
+  gemm_f32_kernel<AK, BKM><<<grid, 256, 0, s>>>(a, per);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || real_split == 1) return e;
+  const size_t nvec = (size_t)g.M * g.N / 4;
+  splitk_reduce_kernel<<<(unsigned)ceil_div((long)nvec, 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t gemm(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.K < 0) return g.M == 0 || g.N == 0 ? hipSuccess : hipErrorInvalidValue;
+  if (g.N % 4) return hipErrorInvalidValue;
+  int split = g.split < 1 ? 1 : g.split;
+  if (split > 1 && (!g.ws || g.epi != EPI_STORE || g.bias || g.resid || g.c_dtype != DT_F32))
+    return hipErrorInvalidValue;
+  if (g.math == DT_F16) {
+    if (g.a_dtype == DT_F32 || g.b_dtype == DT_F32) return hipErrorInvalidValue;
+    // 16-byte operand chunks: the contiguous dimension must be a multiple of 8
+    if (g.a_kmajor ? (g.K % 8) : (g.M % 8)) return hipErrorInvalidValue;
+    if (g.b_kmajor ? (g.K % 8) : (g.N % 8)) return hipErrorInvalidValue;
+    if (g.a_kmajor && g.b_kmajor) return dispatch_f16<true, true>(g, split, s);
+    if (g.a_kmajor && !g.b_kmajor) return dispatch_f16<true, false>(g, split, s);
+    if (!g.a_kmajor && !g.b_kmajor) return dispatch_f16<false, false>(g, split, s);
+    return dispatch_f16<false, true>(g, split, s);
+  }
+  if (g.a_dtype != DT_F32 || g.b_dtype != DT_F32) return hipErrorInvalidValue;
+  if (g.a_kmajor && g.b_kmajor) return launch_f32<true, true>(g, split, s);
+  if (g.a_kmajor && !g.b_kmajor) return launch_f32<true, false>(g, split, s);
+  if (!g.a_kmajor && !g.b_kmajor) return launch_f32<false, false>(g, split, s);
+  return launch_f32<false, true>(g, split, s);
+}
+
+}  // namespace tpl

@@ -1,0 +1,102 @@
+// Internal launch interface of the HIP kernels (host side). Not part of the
+// C ABI: tp_layer.cpp is the only caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace tpl {
+
+// Element types. The bf16 layer keeps bf16 at its boundary (inputs, weights,
+// output, input gradient) and fp16 for internal activations and gradients;
+// the fp32 layer is fp32 throughout.
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// ---------------------------------------------------------------------------
+// LayerNorm and reductions (norm.hip)
+// ---------------------------------------------------------------------------
+// y = gamma * (x - mean) * rstd + beta per row of h; saves mean and rstd.
+// x is `x_dtype`, gamma/beta are `p_dtype`, y is `y_dtype`. If x_copy != NULL
+// the fp32 value of x is also written there (keeps a caller's summed h_mid).
+hipError_t ln_fwd(int x_dtype, int p_dtype, int y_dtype, const void* x, const void* gamma,
+                  const void* beta, void* y, float* mean, float* rstd,
+                  float* x_copy, int rows, int h, float eps, hipStream_t s);
+
+// LayerNorm backward plus the residual-gradient add:
+//   dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) + dres,  g = dy * gamma
+// dy fp32; x is `x_dtype`; dres is `dres_dtype`; gamma is `p_dtype`.
+// Writes dx as fp32 (dx_f32, optional) and/or `st_dtype` (dx_st, optional).
+// Column partial sums over row blocks go to part [nblk][3][h]:
+//   0: sum dy*xhat (dgamma), 1: sum dy (dbeta), 2: sum dx (if want_dsum).
+hipError_t ln_bwd(int p_dtype, const float* dy, int x_dtype, const void* x,
+                  const float* mean, const float* rstd, const void* gamma,
+                  int dres_dtype, const void* dres, float* dx_f32, int st_dtype, void* dx_st,
+                  float* part, int rows_per_blk, int rows, int h, int want_dsum,
+                  hipStream_t s);
+int ln_bwd_blocks(int rows, int h, int* rows_per_blk);
+
+// Column partial sums of a [rows, cols] matrix (leading dim ld) over row
+// blocks: part[blk][cols].
+hipError_t colsum_partial(int y_dtype, const void* y, int rows, int cols, int ld,
+                          float* part, int rows_per_blk, hipStream_t s);
+int colsum_blocks(int rows, int cols, int* rows_per_blk);
+
+// out_k[j] (+)= sum_b part[b][k][j] for k < nout (part is [nblk][nout][width]).
+// The buffer must hold reduce_scratch_floats(nblk, nout, width) floats: the
+// block partials followed by room for the group partials of stage 1.
+hipError_t reduce_partials(const float* part, int nblk, int nout, int width,
+                           float* out0, float* out1, float* out2, int accumulate,
+                           hipStream_t s);
+size_t reduce_scratch_floats(int nblk, int nout, int width);
+
+// dst[i] = sum_p parts[p][i]  (fp32 sum in order), written as dst_dtype.
+hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts,
+                        int nparts, size_t count, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// GEMM (gemm.hip): C[M,N] = A[M,K] @ B[K,N] with a fused epilogue.
+// ---------------------------------------------------------------------------
+enum { EPI_STORE = 0, EPI_BIAS_GELU = 1, EPI_DGELU = 2 };
+
+struct GemmArgs {
+  // Arithmetic: DT_F32 (fp32 FMA) or DT_F16 (fp16 MFMA, fp32 accumulate;
+  // bf16 operands are converted to fp16 while staged into LDS).
+  int math;
+  int M, N, K;
+  // A(m,k) = A[m*lda + k] if a_kmajor else A[k*lda + m]
+  const void* A; long lda; int a_kmajor; int a_dtype;
+  // B(k,n) = B[n*ldb + k] if b_kmajor else B[k*ldb + n]
+  const void* B; long ldb; int b_kmajor; int b_dtype;
+  // epilogue, per element: v = acc (+ bias[n]) (+ resid[m,n]);
+  //   EPI_BIAS_GELU: C = v, C2 = GeLU(v);  EPI_DGELU: C = v * GeLU'(aux[m,n]);
+  //   accumulate: C (fp32) += v.
+  int epi;
+  const void* bias; int bias_dtype;    // [N]
+  const void* resid; long ldr; int resid_dtype;
+  void* C; long ldc; int c_dtype;
+  void* C2; long ldc2; int c2_dtype;
+  const void* aux; long ldaux; int aux_dtype;
+  int gelu_tanh;
+  int accumulate;
+  int split;                           // split-K factor (>= 1)
+  float* ws;                           // split*M*N fp32 when split > 1
+};
+hipError_t gemm(const GemmArgs& g, hipStream_t s);
+// Split-K factor and workspace floats the launcher will use for g.
+int gemm_choose_split(const GemmArgs& g);
+
+// ---------------------------------------------------------------------------
+// Attention (attn.hip). qkv: [batch*seq, 3*Hl*D] head-interleaved;
+// o, dO: [batch*seq, Hl*D]; lse2, delta: [batch, Hl, seq] fp32.
+// dtype: DT_F32 (fp32 kernels) or DT_F16 (fp16 operands, MFMA, fp32 accumulate).
+// mask: 0 causal, 1 padding (valid_len[batch] keys).
+// ---------------------------------------------------------------------------
+hipError_t attn_fwd(int dtype, const void* qkv, void* o, float* lse2,
+                    const int* valid_len, int batch, int seq, int Hl, int D,
+                    int mask, hipStream_t s);
+hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO,
+                    const float* lse2, float* delta, void* dqkv,
+                    const int* valid_len, int batch, int seq, int Hl, int D,
+                    int mask, hipStream_t s);
+
+}  // namespace tpl

@@ -1,0 +1,396 @@
+// LayerNorm forward/backward, column reductions and the single-GPU exchange
+// sum. All HBM-bound: one pass over each tensor, 16-byte vector accesses,
+// fp32 statistics, deterministic (no atomics) two-stage column sums.
+//
+// LayerNorm placement follows "Megatron-LM: GPU-Cluster Training Parallelism",
+// section "Paper 1: BERT LayerNorm Rearrangement" (pre-LN: each sublayer reads
+// LN of the residual stream, whose un-normalised value is carried forward).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace tpl {
+
+template <typename T> struct DtOf;
+template <> struct DtOf<float> { static constexpr int v = DT_F32; };
+template <> struct DtOf<bf16> { static constexpr int v = DT_BF16; };
+template <> struct DtOf<f16> { static constexpr int v = DT_F16; };
+
+// ----------------------------------------------------------------------------
+// LayerNorm forward: one workgroup per row, the row held in registers.
+// ----------------------------------------------------------------------------
+template <typename Tin, typename T, typename To, int NT, int NV>
+__global__ __launch_bounds__(NT) void ln_fwd_kernel(
+    const Tin* __restrict__ x, const T* __restrict__ gamma, const T* __restrict__ beta,
+    To* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out,
+    float* __restrict__ x_copy, int h, float eps) {
+  __shared__ float red[16];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvec = h >> 3;
+  const Tin* xr = x + (size_t)row * h;
+  float v[NV][8];
+  float acc[1] = {0.f};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = tid + i * NT;
+    if (j < nvec) {
+      Vec8<Tin>::load(xr + 8 * j, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[0] += v[i][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    }
+  }
+  block_sum<1>(acc, red);
+  const float mu = acc[0] / (float)h;
+  float sq[1] = {0.f};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = tid + i * NT;
+    if (j < nvec) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[i][e] - mu;
+        sq[0] += d * d;
+      }
+    }
+  }
+  block_sum<1>(sq, red);
+  const float rstd = 1.f / sqrtf(sq[0] / (float)h + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = tid + i * NT;
+    if (j < nvec) {
+      float g[8], b[8], o[8];
+      Vec8<T>::load(gamma + 8 * j, g);
+      Vec8<T>::load(beta + 8 * j, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = g[e] * ((v[i][e] - mu) * rstd) + b[e];
+      Vec8<To>::store(y + (size_t)row * h + 8 * j, o);
+      if (x_copy) Vec8<float>::store(x_copy + (size_t)row * h + 8 * j, v[i]);
+    }
+  }
+  if (tid == 0) {
+    mean_out[row] = mu;
+    rstd_out[row] = rstd;
+  }
+}
+
+// Threads per row and 8-wide vectors per thread for a row of h elements.
+static bool row_config(int h, int* nt, int* nv) {
+  const int nvec = h / 8;
+  if (nvec <= 256) { *nt = 256; *nv = 1; }
+  else if (nvec <= 512) { *nt = 256; *nv = 2; }
+  else if (nvec <= 1024) { *nt = 512; *nv = 2; }
+  else if (nvec <= 2048) { *nt = 1024; *nv = 2; }
+  else if (nvec <= 4096) { *nt = 1024; *nv = 4; }
+  else return false;
+  return true;
+}
+
+template <typename Tin, typename T, typename To>
+static hipError_t ln_fwd_t(const void* x, const void* gamma, const void* beta, void* y,
+                           float* mean, float* rstd, float* x_copy, int rows, int h,
+                           float eps, hipStream_t s) {
+  int nt, nv;
+  if (!row_config(h, &nt, &nv)) return hipErrorInvalidValue;
+  if (rows == 0) return hipSuccess;
+#define TPL_LNF(NT_, NV_)                                                                   \
+  if (nt == NT_ && nv == NV_) {                                                             \
+    ln_fwd_kernel<Tin, T, To, NT_, NV_><<<rows, NT_, 0, s>>>(                               \
+        (const Tin*)x, (const T*)gamma, (const T*)beta, (To*)y, mean, rstd, x_copy, h, eps); \
+    return hipGetLastError();                                                               \
+  }
+  TPL_LNF(256, 1) TPL_LNF(256, 2) TPL_LNF(512, 2) TPL_LNF(1024, 2) TPL_LNF(1024, 4)
+#undef TPL_LNF
+  return hipErrorInvalidValue;
+}
+
+hipError_t ln_fwd(int x_dtype, int p_dtype, int y_dtype, const void* x, const void* gamma,
+                  const void* beta, void* y, float* mean, float* rstd, float* x_copy,
+                  int rows, int h, float eps, hipStream_t s) {
+  if (p_dtype == DT_BF16 && y_dtype == DT_F16) {
+    if (x_dtype == DT_BF16)
+      return ln_fwd_t<bf16, bf16, f16>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s);
+    if (x_dtype == DT_F32)
+      return ln_fwd_t<float, bf16, f16>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s);
+  }
+  if (p_dtype == DT_F32 && y_dtype == DT_F32 && x_dtype == DT_F32)
+    return ln_fwd_t<float, float, float>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s);
+  return hipErrorInvalidValue;
+}
+
+// ----------------------------------------------------------------------------
+// LayerNorm backward + residual-gradient add. A workgroup walks a block of
+// rows; each thread owns the same columns in every row and accumulates the
+// column sums (dgamma, dbeta, dx) for them, written once per block.
+// ----------------------------------------------------------------------------
+template <typename T, typename Tx, typename Tr, typename Ts, int NT, int NV>
+__global__ __launch_bounds__(NT) void ln_bwd_kernel(
+    const float* __restrict__ dy, const Tx* __restrict__ x, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const T* __restrict__ gamma, const Tr* __restrict__ dres,
+    float* __restrict__ dx_f32, Ts* __restrict__ dx_st, float* __restrict__ part,
+    int rows_per_blk, int rows, int h, int want_dsum) {
+  __shared__ float red[32];
+  const int tid = threadIdx.x;
+  const int nvec = h >> 3;
+  const int r0 = blockIdx.x * rows_per_blk;
+  const int r1 = min(rows, r0 + rows_per_blk);
+  float dg[NV][8], db[NV][8], ds[NV][8];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dg[i][e] = db[i][e] = ds[i][e] = 0.f;
+
+  for (int row = r0; row < r1; ++row) {
+    const float mu = mean[row], rs = rstd[row];
+    float gy[NV][8], xh[NV][8];
+    float sums[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = tid + i * NT;
+      if (j < nvec) {
+        float d[8], xv[8], g[8];
+        Vec8<float>::load(dy + (size_t)row * h + 8 * j, d);
+        Vec8<Tx>::load(x + (size_t)row * h + 8 * j, xv);
+        Vec8<T>::load(gamma + 8 * j, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xh[i][e] = (xv[e] - mu) * rs;
+          gy[i][e] = d[e] * g[e];
+          sums[0] += gy[i][e];
+          sums[1] += gy[i][e] * xh[i][e];
+          dg[i][e] += d[e] * xh[i][e];
+          db[i][e] += d[e];
+        }
+      }
+    }
+    block_sum<2>(sums, red);
+    const float mg = sums[0] / (float)h, mgx = sums[1] / (float)h;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = tid + i * NT;
+      if (j < nvec) {
+        float r[8], o[8];
+        Vec8<Tr>::load(dres + (size_t)row * h + 8 * j, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[e] = rs * (gy[i][e] - mg - xh[i][e] * mgx) + r[e];
+          ds[i][e] += o[e];
+        }
+        if (dx_f32) Vec8<float>::store(dx_f32 + (size_t)row * h + 8 * j, o);
+        if (dx_st) Vec8<Ts>::store(dx_st + (size_t)row * h + 8 * j, o);
+      }
+    }
+  }
+  float* pb = part + (size_t)blockIdx.x * 3 * h;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = tid + i * NT;
+    if (j < nvec) {
+      Vec8<float>::store(pb + 8 * j, dg[i]);
+      Vec8<float>::store(pb + h + 8 * j, db[i]);
+      if (want_dsum) Vec8<float>::store(pb + 2 * h + 8 * j, ds[i]);
+    }
+  }
+}
+
+int ln_bwd_blocks(int rows, int h, int* rows_per_blk) {
+  (void)h;
+  const int rpb = rows <= 4096 ? 8 : 16;
+  *rows_per_blk = rpb;
+  return (rows + rpb - 1) / rpb;
+}
+
+template <typename T, typename Tx, typename Tr, typename Ts>
+static hipError_t ln_bwd_t(const float* dy, const void* x, const float* mean,
+                           const float* rstd, const void* gamma, const void* dres,
+                           float* dx_f32, void* dx_st, float* part, int rows_per_blk,
+                           int rows, int h, int want_dsum, hipStream_t s) {
+  int nt, nv;
+  if (!row_config(h, &nt, &nv)) return hipErrorInvalidValue;
+  const int nblk = (rows + rows_per_blk - 1) / rows_per_blk;
+  if (nblk == 0) return hipSuccess;
+#define TPL_LNB(NT_, NV_)                                                                  \
+  if (nt == NT_ && nv == NV_) {                                                            \
+    ln_bwd_kernel<T, Tx, Tr, Ts, NT_, NV_><<<nblk, NT_, 0, s>>>(                           \
+        dy, (const Tx*)x, mean, rstd, (const T*)gamma, (const Tr*)dres, dx_f32, (Ts*)dx_st, \
+        part, rows_per_blk, rows, h, want_dsum);                                           \
+    return hipGetLastError();                                                              \
+  }
+  TPL_LNB(256, 1) TPL_LNB(256, 2) TPL_LNB(512, 2) TPL_LNB(1024, 2) TPL_LNB(1024, 4)
+#undef TPL_LNB
+  return hipErrorInvalidValue;
+}
+
+hipError_t ln_bwd(int p_dtype, const float* dy, int x_dtype, const void* x,
+                  const float* mean, const float* rstd, const void* gamma, int dres_dtype,
+                  const void* dres, float* dx_f32, int st_dtype, void* dx_st, float* part,
+                  int rows_per_blk, int rows, int h, int want_dsum, hipStream_t s) {
+  if (p_dtype == DT_F32 && x_dtype == DT_F32 && dres_dtype == DT_F32 && st_dtype == DT_F32)
+    return ln_bwd_t<float, float, float, float>(dy, x, mean, rstd, gamma, dres, dx_f32, dx_st,
+                                                part, rows_per_blk, rows, h, want_dsum, s);
+  if (p_dtype != DT_BF16) return hipErrorInvalidValue;
+  // LN2 backward: x = h_mid (fp32), dres = upstream gradient (bf16), dx -> fp32 + fp16
+  if (x_dtype == DT_F32 && dres_dtype == DT_BF16 && st_dtype == DT_F16)
+    return ln_bwd_t<bf16, float, bf16, f16>(dy, x, mean, rstd, gamma, dres, dx_f32, dx_st, part,
+                                            rows_per_blk, rows, h, want_dsum, s);
+  // LN1 backward: x = layer input (bf16), dres = dh (fp32), dx -> bf16
+  if (x_dtype == DT_BF16 && dres_dtype == DT_F32 && st_dtype == DT_BF16)
+    return ln_bwd_t<bf16, bf16, float, bf16>(dy, x, mean, rstd, gamma, dres, dx_f32, dx_st, part,
+                                             rows_per_blk, rows, h, want_dsum, s);
+  return hipErrorInvalidValue;
+}
+
+// ----------------------------------------------------------------------------
+// Column partial sums (bias gradients): part[blk][c] = sum over the block's rows.
+// ----------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ y, int rows,
+                                                     int cols, int ld, float* __restrict__ part,
+                                                     int rows_per_blk) {
+  const int j = blockIdx.x * 256 + threadIdx.x;  // vector index (8 columns)
+  if (8 * j >= cols) return;
+  const int r0 = blockIdx.y * rows_per_blk;
+  const int r1 = min(rows, r0 + rows_per_blk);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < r1; ++r) {
+    float v[8];
+    Vec8<T>::load(y + (size_t)r * ld + 8 * j, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  }
+  Vec8<float>::store(part + (size_t)blockIdx.y * cols + 8 * j, acc);
+}
+
+int colsum_blocks(int rows, int cols, int* rows_per_blk) {
+  const int gx = (cols / 8 + 255) / 256;
+  int nblk = (512 + gx - 1) / gx;  // aim for ~512 workgroups
+  int rpb = (rows + nblk - 1) / nblk;
+  if (rpb < 16) rpb = 16;
+  *rows_per_blk = rpb;
+  return (rows + rpb - 1) / rpb;
+}
+
+hipError_t colsum_partial(int y_dtype, const void* y, int rows, int cols, int ld, float* part,
+                          int rows_per_blk, hipStream_t s) {
+  const int nblk = (rows + rows_per_blk - 1) / rows_per_blk;
+  if (nblk == 0 || cols == 0) return hipSuccess;
+  dim3 grid((cols / 8 + 255) / 256, nblk);
+  if (y_dtype == DT_BF16)
+    colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)y, rows, cols, ld, part, rows_per_blk);
+  else if (y_dtype == DT_F16)
+    colsum_kernel<f16><<<grid, 256, 0, s>>>((const f16*)y, rows, cols, ld, part, rows_per_blk);
+  else
+    colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)y, rows, cols, ld, part, rows_per_blk);
+  return hipGetLastError();
+}
+
+// out_k[j] (+)= sum_b part[b][k][j], in two deterministic stages: stage 1
+// sums groups of kGroup consecutive blocks per column (many workgroups, short
+// loops); stage 2 sums the group results in order. The group partials live
+// after the nblk block partials in the same buffer (see reduce_scratch_floats).
+constexpr int kGroup = 16;
+
+__global__ __launch_bounds__(256) void reduce_stage1_kernel(const float* __restrict__ part,
+                                                            int nblk, int total,
+                                                            float* __restrict__ grp) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int b0 = blockIdx.y * kGroup, b1 = min(nblk, b0 + kGroup);
+  float acc = 0.f;
+  for (int b = b0; b < b1; ++b) acc += part[(size_t)b * total + idx];
+  grp[(size_t)blockIdx.y * total + idx] = acc;
+}
+
+__global__ __launch_bounds__(256) void reduce_stage2_kernel(const float* __restrict__ grp,
+                                                            int ngrp, int nout, int width,
+                                                            float* out0, float* out1, float* out2,
+                                                            int accumulate) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int total = nout * width;
+  if (idx >= total) return;
+  float acc = 0.f;
+  for (int g = 0; g < ngrp; ++g) acc += grp[(size_t)g * total + idx];
+  const int k = idx / width, j = idx - k * width;
+  float* o = k == 0 ? out0 : (k == 1 ? out1 : out2);
+  if (!o) return;
+  o[j] = accumulate ? o[j] + acc : acc;
+}
+
+size_t reduce_scratch_floats(int nblk, int nout, int width) {
+  const size_t total = (size_t)nout * width;
+  return (size_t)nblk * total + (size_t)((nblk + kGroup - 1) / kGroup) * total;
+}
+
+hipError_t reduce_partials(const float* part, int nblk, int nout, int width, float* out0,
+                           float* out1, float* out2, int accumulate, hipStream_t s) {
+  const int total = nout * width;
+  if (total == 0) return hipSuccess;
+  const int ngrp = (nblk + kGroup - 1) / kGroup;
+  float* grp = const_cast<float*>(part) + (size_t)nblk * total;
+  reduce_stage1_kernel<<<dim3((total + 255) / 256, ngrp), 256, 0, s>>>(part, nblk, total, grp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  reduce_stage2_kernel<<<(total + 255) / 256, 256, 0, s>>>(grp, ngrp, nout, width, out0, out1,
+                                                            out2, accumulate);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Exchange sum (single-GPU stand-in for the all-reduce of fp32 partials).
+// ----------------------------------------------------------------------------
+struct PartPtrs {
+  const float* p[16];
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void exchange_sum_kernel(T* __restrict__ dst, PartPtrs parts,
+                                                           int nparts, size_t nvec) {
+  const size_t j = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= nvec) return;
+  float acc[8], v[8];
+  Vec8<float>::load(parts.p[0] + 8 * j, acc);
+  for (int p = 1; p < nparts; ++p) {
+    Vec8<float>::load(parts.p[p] + 8 * j, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  }
+  Vec8<T>::store(dst + 8 * j, acc);
+}
+
+template <typename T>
+__global__ void exchange_sum_tail_kernel(T* dst, PartPtrs parts, int nparts, size_t begin,
+                                         size_t count) {
+  const size_t i = begin + threadIdx.x;
+  if (i >= count) return;
+  float acc = parts.p[0][i];
+  for (int p = 1; p < nparts; ++p) acc += parts.p[p][i];
+  if constexpr (DtOf<T>::v == DT_BF16) dst[i] = f2bf(acc);
+  else dst[i] = acc;
+}
+
+hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts, int nparts,
+                        size_t count, hipStream_t s) {
+  if (nparts < 1 || nparts > 16) return hipErrorInvalidValue;
+  PartPtrs pp = {};
+  for (int p = 0; p < nparts; ++p) pp.p[p] = parts[p];
+  const size_t nvec = count / 8, tail = count - nvec * 8;
+  if (nvec) {
+    const unsigned grid = (unsigned)((nvec + 255) / 256);
+    if (dst_dtype == DT_BF16)
+      exchange_sum_kernel<bf16><<<grid, 256, 0, s>>>((bf16*)dst, pp, nparts, nvec);
+    else
+      exchange_sum_kernel<float><<<grid, 256, 0, s>>>((float*)dst, pp, nparts, nvec);
+  }
+  if (tail) {
+    if (dst_dtype == DT_BF16)
+      exchange_sum_tail_kernel<bf16><<<1, 64, 0, s>>>((bf16*)dst, pp, nparts, nvec * 8, count);
+    else
+      exchange_sum_tail_kernel<float><<<1, 64, 0, s>>>((float*)dst, pp, nparts, nvec * 8, count);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpl

@@ -1,0 +1,620 @@
+// C ABI of the tensor-parallel layer shard: argument checks, workspace plan
+// and the phase driver that enqueues the HIP kernels in order.
+//
+// Phase structure: "Megatron-LM: GPU-Cluster Training Parallelism", section
+// "Paper 1: The f/g Conjugate Operators" -- two exchanges forward (g after the
+// row-parallel output projection and after FC2) and two backward (f before
+// the input gradients of the column-parallel QKV and FC1 leave the rank).
+// TP_ALL takes every exchange as the identity; the split phases stop at each
+// exchange so a caller can sum the ranks' fp32 partials in between.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <initializer_list>
+#include <new>
+#include <vector>
+
+#include "../../include/tp_layer.h"
+#include "kernels.hpp"
+
+using namespace tpl;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Region {
+  size_t off = 0, bytes = 0;
+};
+
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+
+struct Prof {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  long launches[TP_K_COUNT] = {};
+  double ms[TP_K_COUNT] = {}, flops[TP_K_COUNT] = {}, bytes[TP_K_COUNT] = {};
+};
+
+}  // namespace
+
+struct tp_layer {
+  int hidden, heads, ffn, seq, batch, t, rank, dtype, mask;
+  float eps;
+  int gelu_tanh;
+  // derived
+  int n, dh, Hl, hl, fl, esz;
+  int sdt;   // storage type at the boundary (x, params, out, dx): DT_BF16 or DT_F32
+  int adt;   // internal activations and their gradients: DT_F16 or DT_F32
+  // workspace regions
+  Region mean1, rstd1, a, qkv, o, lse2, h_mid, mean2, rstd2, c, u, z;
+  Region du, dc, dh_f, dh_s, dO, delta, dqkv, da, part, splitk;
+  size_t ws_bytes;
+  int split_w2, split_w1, split_wo, split_wqkv;
+  double attn_pairs;  // allowed query-key pairs (causal); 0 for padding (lengths on device)
+  Prof prof;
+};
+
+namespace {
+
+GemmArgs gemm_base(const tp_layer* L) {
+  GemmArgs g = {};
+  g.math = L->adt;  // fp16 MFMA for the bf16 layer, fp32 FMA for the fp32 layer
+  g.a_dtype = g.b_dtype = g.c_dtype = g.c2_dtype = g.aux_dtype = L->adt;
+  g.bias_dtype = g.resid_dtype = L->sdt;
+  g.split = 1;
+  g.gelu_tanh = L->gelu_tanh;
+  return g;
+}
+
+// Weight-gradient GEMM: C[M,N] (+)= X^T @ Y with X [n, M], Y [n, N] (both
+// token-major, i.e. contiguous along M and N).
+GemmArgs wgrad_args(const tp_layer* L, int M, int N, const void* X, const void* Y, float* C,
+                    int accumulate) {
+  GemmArgs g = gemm_base(L);
+  g.M = M;
+  g.N = N;
+  g.K = L->n;
+  g.A = X;
+  g.lda = M;
+  g.a_kmajor = 0;
+  g.B = Y;
+  g.ldb = N;
+  g.b_kmajor = 0;
+  g.C = C;
+  g.ldc = N;
+  g.c_dtype = DT_F32;
+  g.accumulate = accumulate;
+  return g;
+}
+
+void plan(tp_layer* L) {
+  size_t off = 0;
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.bytes = bytes;
+    off += align_up(bytes);
+  };
+  const size_t n = (size_t)L->n, h = (size_t)L->hidden, e = (size_t)L->esz;
+  const size_t stats = (size_t)L->batch * L->Hl * L->seq * 4;
+  take(L->mean1, n * 4);
+  take(L->rstd1, n * 4);
+  take(L->a, n * h * e);
+  take(L->qkv, n * 3 * L->hl * e);
+  take(L->o, n * L->hl * e);
+  take(L->lse2, stats);
+  take(L->h_mid, n * h * 4);
+  take(L->mean2, n * 4);
+  take(L->rstd2, n * 4);
+  take(L->c, n * h * e);
+  take(L->u, n * L->fl * e);
+  take(L->z, n * L->fl * e);
+  take(L->du, n * L->fl * e);
+  take(L->dc, n * h * 4);
+  take(L->dh_f, n * h * 4);
+  take(L->dh_s, n * h * e);
+  take(L->dO, n * L->hl * e);
+  take(L->delta, stats);
+  take(L->dqkv, n * 3 * L->hl * e);
+  take(L->da, n * h * 4);
+  // reduction partials: LayerNorm [nblk][3][h]; column sums [nblk][cols]
+  int rpb;
+  size_t part = reduce_scratch_floats(ln_bwd_blocks(L->n, L->hidden, &rpb), 3, L->hidden);
+  const int cols[3] = {L->hidden, L->fl, 3 * L->hl};
+  for (int i = 0; i < 3; ++i) {
+    const size_t p = reduce_scratch_floats(colsum_blocks(L->n, cols[i], &rpb), 1, cols[i]);
+    if (p > part) part = p;
+  }
+  take(L->part, part * 4);
+  // split-K partials of the weight gradients
+  size_t sk = 0;
+  struct W {
+    int M, N;
+    int* split;
+  } ws[4] = {{L->fl, L->hidden, &L->split_w2},
+             {L->hidden, L->fl, &L->split_w1},
+             {L->hl, L->hidden, &L->split_wo},
+             {L->hidden, 3 * L->hl, &L->split_wqkv}};
+  for (auto& w : ws) {
+    GemmArgs g = wgrad_args(L, w.M, w.N, nullptr, nullptr, nullptr, 0);
+    *w.split = gemm_choose_split(g);
+    if (*w.split > 1) {
+      const size_t b = (size_t)(*w.split) * w.M * w.N * 4;
+      if (b > sk) sk = b;
+    }
+  }
+  take(L->splitk, sk);
+  L->ws_bytes = off;
+}
+
+template <typename T>
+T* at(void* ws, const Region& r) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + r.off);
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (!p) return TP_ERR_ARG;
+    if (!aligned(p)) return TP_ERR_ALIGN;
+  }
+  return TP_OK;
+}
+
+int check_params(const tp_layer* L, const tp_params* p) {
+  if (!p) return TP_ERR_ARG;
+  int e = check_ptrs({p->ln1_gamma, p->ln1_beta, p->w_qkv, p->b_qkv, p->w_o, p->b_o,
+                      p->ln2_gamma, p->ln2_beta, p->w_fc1, p->b_fc1, p->w_fc2, p->b_fc2});
+  if (e) return e;
+  if (L->mask == TP_MASK_PADDING) return check_ptrs({p->valid_len});
+  return TP_OK;
+}
+
+int check_ws(const tp_layer* L, void* ws, size_t bytes) {
+  if (!ws || bytes < L->ws_bytes) return TP_ERR_WORKSPACE;
+  if (!aligned(ws)) return TP_ERR_ALIGN;
+  return TP_OK;
+}
+
+#define HIP_TRY(x)                        \
+  do {                                    \
+    if ((x) != hipSuccess) return TP_ERR_HIP; \
+  } while (0)
+
+// Brackets one launch group with a pair of events when profiling is on.
+struct Scope {
+  tp_layer* L;
+  hipStream_t s;
+  int cls;
+  double fl, by;
+  hipEvent_t a = nullptr, b = nullptr;
+  static hipEvent_t get(Prof& p) {
+    if (!p.pool.empty()) {
+      hipEvent_t e = p.pool.back();
+      p.pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  Scope(tp_layer* L_, hipStream_t s_, int cls_, double fl_, double by_)
+      : L(L_), s(s_), cls(cls_), fl(fl_), by(by_) {
+    if (!L->prof.on) return;
+    a = get(L->prof);
+    b = get(L->prof);
+    if (!a || !b || hipEventRecord(a, s) != hipSuccess) {
+      if (a) L->prof.pool.push_back(a);
+      if (b) L->prof.pool.push_back(b);
+      a = b = nullptr;
+    }
+  }
+  ~Scope() {
+    if (!a) return;
+    (void)hipEventRecord(b, s);
+    L->prof.recs.push_back({cls, a, b, fl, by});
+  }
+};
+
+double gemm_bytes(const tp_layer* L, const GemmArgs& g) {
+  const double e = L->esz;
+  double b = ((double)g.M * g.K + (double)g.K * g.N) * e;
+  b += (double)g.M * g.N * (g.c_dtype == DT_F32 ? 4.0 : e) * (g.accumulate ? 2.0 : 1.0);
+  if (g.resid) b += (double)g.M * g.N * (g.resid_dtype == DT_F32 ? 4.0 : e);
+  if (g.C2) b += (double)g.M * g.N * e;
+  if (g.aux) b += (double)g.M * g.N * e;
+  return b;
+}
+
+int run_gemm(tp_layer* L, const GemmArgs& g, hipStream_t s) {
+  Scope ps(L, s, TP_K_GEMM, 2.0 * g.M * g.N * (double)g.K, gemm_bytes(L, g));
+  HIP_TRY(gemm(g, s));
+  return TP_OK;
+}
+
+// ---- forward pieces --------------------------------------------------------
+// x -> a -> qkv -> o -> (o @ W_o) [+ b_o + x] into `dst` (fp32 [n, h]).
+int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool designated,
+             void* ws, hipStream_t s) {
+  const int n = L->n, h = L->hidden, hl = L->hl;
+  int e;
+  const double nh = (double)n * h;
+  {
+  Scope ps(L, s, TP_K_LN_FWD, 0, nh * 2 * L->esz + 8.0 * n);
+  HIP_TRY(ln_fwd(L->sdt, L->sdt, L->adt, x, p->ln1_gamma, p->ln1_beta, at<void>(ws, L->a),
+                 at<float>(ws, L->mean1), at<float>(ws, L->rstd1), nullptr, n, h, L->eps, s));
+  }
+  GemmArgs g = gemm_base(L);
+  g.M = n; g.N = 3 * hl; g.K = h;
+  g.A = at<void>(ws, L->a); g.lda = h; g.a_kmajor = 1;
+  g.B = p->w_qkv; g.ldb = 3 * hl; g.b_kmajor = 0; g.b_dtype = L->sdt;
+  g.bias = p->b_qkv;
+  g.C = at<void>(ws, L->qkv); g.ldc = 3 * hl;
+  if ((e = run_gemm(L, g, s))) return e;
+  {
+  Scope ps(L, s, TP_K_ATTN_FWD, 4.0 * L->dh * L->Hl * L->attn_pairs,
+           (double)n * 4 * hl * L->esz + 4.0 * n * L->Hl);
+  HIP_TRY(attn_fwd(L->adt, at<void>(ws, L->qkv), at<void>(ws, L->o), at<float>(ws, L->lse2),
+                   p->valid_len, L->batch, L->seq, L->Hl, L->dh, L->mask, s));
+  }
+  g = gemm_base(L);
+  g.M = n; g.N = h; g.K = hl;
+  g.A = at<void>(ws, L->o); g.lda = hl; g.a_kmajor = 1;
+  g.B = p->w_o; g.ldb = h; g.b_kmajor = 0; g.b_dtype = L->sdt;
+  if (designated) {
+    g.bias = p->b_o;
+    g.resid = x; g.ldr = h; g.resid_dtype = L->sdt;
+  }
+  g.C = dst; g.ldc = h; g.c_dtype = DT_F32;
+  if ((e = run_gemm(L, g, s))) return e;
+  return TP_OK;
+}
+
+// h_mid (fp32) -> c -> u, z -> (z @ W_fc2) [+ b_fc2 + h_mid] into `out`.
+int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, int out_f32,
+            bool designated, void* ws, hipStream_t s) {
+  const int n = L->n, h = L->hidden, fl = L->fl;
+  int e;
+  float* h_mid = at<float>(ws, L->h_mid);
+  {
+  Scope ps(L, s, TP_K_LN_FWD, 0,
+           (double)n * h * (4 + L->esz + (h_mid_in == h_mid ? 0 : 4)) + 8.0 * n);
+  HIP_TRY(ln_fwd(DT_F32, L->sdt, L->adt, h_mid_in, p->ln2_gamma, p->ln2_beta, at<void>(ws, L->c),
+                 at<float>(ws, L->mean2), at<float>(ws, L->rstd2),
+                 h_mid_in == h_mid ? nullptr : h_mid, n, h, L->eps, s));
+  }
+  GemmArgs g = gemm_base(L);
+  g.M = n; g.N = fl; g.K = h;
+  g.A = at<void>(ws, L->c); g.lda = h; g.a_kmajor = 1;
+  g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 0; g.b_dtype = L->sdt;
+  g.bias = p->b_fc1;
+  g.epi = EPI_BIAS_GELU;
+  g.C = at<void>(ws, L->u); g.ldc = fl;
+  g.C2 = at<void>(ws, L->z); g.ldc2 = fl;
+  if ((e = run_gemm(L, g, s))) return e;
+  g = gemm_base(L);
+  g.M = n; g.N = h; g.K = fl;
+  g.A = at<void>(ws, L->z); g.lda = fl; g.a_kmajor = 1;
+  g.B = p->w_fc2; g.ldb = h; g.b_kmajor = 0; g.b_dtype = L->sdt;
+  if (designated) {
+    g.bias = p->b_fc2;
+    g.resid = h_mid; g.ldr = h; g.resid_dtype = DT_F32;
+  }
+  g.C = out; g.ldc = h; g.c_dtype = out_f32 ? DT_F32 : L->sdt;
+  if ((e = run_gemm(L, g, s))) return e;
+  return TP_OK;
+}
+
+// ---- backward pieces -------------------------------------------------------
+// Bias gradient: out (+)= column sums of y [n, cols] (two-stage, deterministic).
+int bias_grad(tp_layer* L, const void* y, int y_dtype, int cols, float* out, int accumulate,
+              void* ws, hipStream_t s) {
+  Scope ps(L, s, TP_K_REDUCE, 0, (double)L->n * cols * L->esz + 4.0 * cols);
+  float* part = at<float>(ws, L->part);
+  int rpb;
+  const int nb = colsum_blocks(L->n, cols, &rpb);
+  HIP_TRY(colsum_partial(y_dtype, y, L->n, cols, cols, part, rpb, s));
+  HIP_TRY(reduce_partials(part, nb, 1, cols, out, nullptr, nullptr, accumulate, s));
+  return TP_OK;
+}
+
+// LayerNorm backward + residual-gradient add, then the reduction of its
+// column partials into dgamma, dbeta (and the column sums of dx if dsum).
+int ln_backward(tp_layer* L, const float* dy, int x_dtype, const void* x, const float* mean,
+                const float* rstd, const void* gamma, int dres_dtype, const void* dres,
+                float* dx_f32, int st_dtype, void* dx_st, float* dgamma, float* dbeta,
+                float* dsum, int accumulate, void* ws, hipStream_t s) {
+  const int n = L->n, h = L->hidden;
+  float* part = at<float>(ws, L->part);
+  int rpb;
+  const int nb = ln_bwd_blocks(n, h, &rpb);
+  {
+    const double x_sz = x_dtype == DT_F32 ? 4 : L->esz, r_sz = dres_dtype == DT_F32 ? 4 : L->esz;
+    const double out_sz = (dx_f32 ? 4 : 0) + (dx_st ? L->esz : 0);
+    Scope ps(L, s, TP_K_LN_BWD, 0, (double)n * h * (4 + x_sz + r_sz + out_sz) + 8.0 * n);
+    HIP_TRY(ln_bwd(L->sdt, dy, x_dtype, x, mean, rstd, gamma, dres_dtype, dres, dx_f32, st_dtype,
+                   dx_st, part, rpb, n, h, dsum != nullptr, s));
+  }
+  Scope ps(L, s, TP_K_REDUCE, 0, (double)nb * 3 * h * 4);
+  HIP_TRY(reduce_partials(part, nb, 3, h, dgamma, dbeta, dsum, accumulate, s));
+  return TP_OK;
+}
+
+// dout -> du, dW2, db2, dA, db1, dc (fp32 into `dc_out`).
+int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out, void* ws,
+            hipStream_t s) {
+  const int n = L->n, h = L->hidden, fl = L->fl;
+  int e;
+  float* skw = at<float>(ws, L->splitk);
+  GemmArgs g = gemm_base(L);
+  g.M = n; g.N = fl; g.K = h;
+  g.A = io->dout; g.lda = h; g.a_kmajor = 1; g.a_dtype = L->sdt;
+  g.B = p->w_fc2; g.ldb = h; g.b_kmajor = 1; g.b_dtype = L->sdt;
+  g.epi = EPI_DGELU;
+  g.aux = at<void>(ws, L->u); g.ldaux = fl;
+  g.C = at<void>(ws, L->du); g.ldc = fl;
+  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s))) return e;
+  g = wgrad_args(L, fl, h, at<void>(ws, L->z), io->dout, io->d_w_fc2, io->accumulate);
+  g.b_dtype = L->sdt;
+  g.split = L->split_w2; g.ws = skw;
+  if ((e = run_gemm(L, g, s))) return e;
+  g = wgrad_args(L, h, fl, at<void>(ws, L->c), at<void>(ws, L->du), io->d_w_fc1, io->accumulate);
+  g.split = L->split_w1; g.ws = skw;
+  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = bias_grad(L, at<void>(ws, L->du), L->adt, fl, io->d_b_fc1, io->accumulate, ws, s)))
+    return e;
+  g = gemm_base(L);
+  g.M = n; g.N = h; g.K = fl;
+  g.A = at<void>(ws, L->du); g.lda = fl; g.a_kmajor = 1;
+  g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 1; g.b_dtype = L->sdt;
+  g.C = dc_out; g.ldc = h; g.c_dtype = DT_F32;
+  return run_gemm(L, g, s);
+}
+
+// dc (summed) -> dh, LN2 grads, db_o -> dW_o, do -> attention -> dqkv ->
+// dW_qkv, db_qkv -> da (fp32 into `da_out`).
+int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* dc,
+             float* da_out, void* ws, hipStream_t s) {
+  const int n = L->n, h = L->hidden, hl = L->hl;
+  int e;
+  float* skw = at<float>(ws, L->splitk);
+  if ((e = ln_backward(L, dc, DT_F32, at<void>(ws, L->h_mid), at<float>(ws, L->mean2),
+                       at<float>(ws, L->rstd2), p->ln2_gamma, L->sdt, io->dout,
+                       at<float>(ws, L->dh_f), L->adt, at<void>(ws, L->dh_s), io->d_ln2_gamma,
+                       io->d_ln2_beta, io->d_b_o, io->accumulate, ws, s)))
+    return e;
+  GemmArgs g = gemm_base(L);
+  g.M = n; g.N = hl; g.K = h;
+  g.A = at<void>(ws, L->dh_s); g.lda = h; g.a_kmajor = 1;
+  g.B = p->w_o; g.ldb = h; g.b_kmajor = 1; g.b_dtype = L->sdt;
+  g.C = at<void>(ws, L->dO); g.ldc = hl;
+  if ((e = run_gemm(L, g, s))) return e;
+  g = wgrad_args(L, hl, h, at<void>(ws, L->o), at<void>(ws, L->dh_s), io->d_w_o, io->accumulate);
+  g.split = L->split_wo; g.ws = skw;
+  if ((e = run_gemm(L, g, s))) return e;
+  {
+    Scope ps(L, s, TP_K_ATTN_BWD, 8.0 * L->dh * L->Hl * L->attn_pairs,
+             (double)n * 8 * hl * L->esz + 8.0 * n * L->Hl);
+    HIP_TRY(attn_bwd(L->adt, at<void>(ws, L->qkv), at<void>(ws, L->o), at<void>(ws, L->dO),
+                     at<float>(ws, L->lse2), at<float>(ws, L->delta), at<void>(ws, L->dqkv),
+                     p->valid_len, L->batch, L->seq, L->Hl, L->dh, L->mask, s));
+  }
+  g = wgrad_args(L, h, 3 * hl, at<void>(ws, L->a), at<void>(ws, L->dqkv), io->d_w_qkv,
+                 io->accumulate);
+  g.split = L->split_wqkv; g.ws = skw;
+  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = bias_grad(L, at<void>(ws, L->dqkv), L->adt, 3 * hl, io->d_b_qkv, io->accumulate, ws,
+                     s)))
+    return e;
+  g = gemm_base(L);
+  g.M = n; g.N = h; g.K = 3 * hl;
+  g.A = at<void>(ws, L->dqkv); g.lda = 3 * hl; g.a_kmajor = 1;
+  g.B = p->w_qkv; g.ldb = 3 * hl; g.b_kmajor = 1; g.b_dtype = L->sdt;
+  g.C = da_out; g.ldc = h; g.c_dtype = DT_F32;
+  return run_gemm(L, g, s);
+}
+
+// da (summed) -> dx (+ dh), LN1 grads.
+int bwd_ln1(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* da, void* ws,
+            hipStream_t s) {
+  return ln_backward(L, da, L->sdt, io->x, at<float>(ws, L->mean1), at<float>(ws, L->rstd1),
+                     p->ln1_gamma, DT_F32, at<void>(ws, L->dh_f), nullptr, L->sdt, io->dx,
+                     io->d_ln1_gamma, io->d_ln1_beta, nullptr, io->accumulate, ws, s);
+}
+
+void prof_fold(Prof& p) {
+  for (auto& r : p.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      p.launches[r.cls] += 1;
+      p.ms[r.cls] += ms;
+      p.flops[r.cls] += r.flops;
+      p.bytes[r.cls] += r.bytes;
+    }
+    p.pool.push_back(r.a);
+    p.pool.push_back(r.b);
+  }
+  p.recs.clear();
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, int t, int rank,
+                    int dtype, int mask, const tp_layer_opts* opts, tp_layer** out,
+                    size_t* workspace_bytes) {
+  if (!out) return TP_ERR_ARG;
+  *out = nullptr;
+  if (!workspace_bytes) return TP_ERR_ARG;
+  if (hidden <= 0 || heads <= 0 || ffn <= 0 || seq <= 0 || micro_batch <= 0 || t <= 0)
+    return TP_ERR_ARG;
+  if (dtype != TP_DTYPE_F32 && dtype != TP_DTYPE_BF16) return TP_ERR_UNSUPPORTED;
+  if (mask != TP_MASK_CAUSAL && mask != TP_MASK_PADDING) return TP_ERR_UNSUPPORTED;
+  if (hidden % heads || heads % t || ffn % t || (ffn / t) % 8) return TP_ERR_SHAPE;
+  if (rank < 0 || rank >= t) return TP_ERR_SHAPE;
+  const int dh = hidden / heads;
+  if (dh != 32 && dh != 64 && dh != 96 && dh != 128 && dh != 160) return TP_ERR_UNSUPPORTED;
+  if (hidden > 32768) return TP_ERR_UNSUPPORTED;  // LayerNorm keeps a row in registers
+  const long n = (long)seq * micro_batch;
+  if (n > (1L << 30) / 4) return TP_ERR_UNSUPPORTED;
+  float eps = 1e-5f;
+  int gelu = TP_GELU_ERF;
+  if (opts) {
+    eps = opts->ln_eps;
+    gelu = opts->gelu;
+    if (!(eps > 0.f)) return TP_ERR_ARG;
+    if (gelu != TP_GELU_ERF && gelu != TP_GELU_TANH) return TP_ERR_UNSUPPORTED;
+  }
+  tp_layer* L = new (std::nothrow) tp_layer();
+  if (!L) return TP_ERR_ARG;
+  L->hidden = hidden; L->heads = heads; L->ffn = ffn; L->seq = seq; L->batch = micro_batch;
+  L->t = t; L->rank = rank; L->dtype = dtype; L->mask = mask;
+  L->eps = eps; L->gelu_tanh = gelu == TP_GELU_TANH;
+  L->n = (int)n; L->dh = dh; L->Hl = heads / t; L->hl = L->Hl * dh; L->fl = ffn / t;
+  L->esz = dtype == TP_DTYPE_BF16 ? 2 : 4;
+  L->sdt = dtype == TP_DTYPE_BF16 ? DT_BF16 : DT_F32;
+  L->adt = dtype == TP_DTYPE_BF16 ? DT_F16 : DT_F32;
+  L->attn_pairs = mask == TP_MASK_CAUSAL ? (double)micro_batch * seq * (seq + 1) / 2.0 : 0.0;
+  plan(L);
+  *out = L;
+  *workspace_bytes = L->ws_bytes;
+  return TP_OK;
+}
+
+int tp_layer_fwd(tp_layer* L, int phase, const tp_fwd_io* io, void* hip_stream) {
+  if (!L || !io) return TP_ERR_ARG;
+  if (phase < TP_ALL || phase > TP_FWD_MLP) return TP_ERR_PHASE;
+  int e = check_params(L, io->params);
+  if (e) return e;
+  if ((e = check_ws(L, io->workspace, io->workspace_bytes))) return e;
+  hipStream_t s = (hipStream_t)hip_stream;
+  void* ws = io->workspace;
+  const tp_params* p = io->params;
+  const bool designated = L->rank == 0;
+  switch (phase) {
+    case TP_ALL:
+      if ((e = check_ptrs({io->x, io->out}))) return e;
+      if ((e = fwd_attn(L, p, io->x, at<float>(ws, L->h_mid), true, ws, s))) return e;
+      return fwd_mlp(L, p, at<float>(ws, L->h_mid), io->out, 0, true, ws, s);
+    case TP_FWD_ATTN:
+      if ((e = check_ptrs({io->x, io->out}))) return e;
+      return fwd_attn(L, p, io->x, (float*)io->out, designated, ws, s);
+    default:
+      if ((e = check_ptrs({io->h_mid, io->out}))) return e;
+      return fwd_mlp(L, p, io->h_mid, io->out, 1, designated, ws, s);
+  }
+}
+
+int tp_layer_bwd(tp_layer* L, int phase, const tp_bwd_io* io, void* hip_stream) {
+  if (!L || !io) return TP_ERR_ARG;
+  if (phase < TP_ALL || phase > TP_BWD_LN1) return TP_ERR_PHASE;
+  int e = check_params(L, io->params);
+  if (e) return e;
+  if ((e = check_ws(L, io->workspace, io->workspace_bytes))) return e;
+  hipStream_t s = (hipStream_t)hip_stream;
+  void* ws = io->workspace;
+  const tp_params* p = io->params;
+  switch (phase) {
+    case TP_ALL:
+      if ((e = check_ptrs({io->x, io->dout, io->dx, io->d_ln1_gamma, io->d_ln1_beta, io->d_w_qkv,
+                           io->d_b_qkv, io->d_w_o, io->d_b_o, io->d_ln2_gamma, io->d_ln2_beta,
+                           io->d_w_fc1, io->d_b_fc1, io->d_w_fc2, io->d_b_fc2})))
+        return e;
+      if ((e = bwd_mlp(L, p, io, at<float>(ws, L->dc), ws, s))) return e;
+      if ((e = bwd_attn(L, p, io, at<float>(ws, L->dc), at<float>(ws, L->da), ws, s))) return e;
+      return bwd_ln1(L, p, io, at<float>(ws, L->da), ws, s);
+    case TP_BWD_MLP:
+      if ((e = check_ptrs({io->dout, io->partial, io->d_w_fc1, io->d_b_fc1, io->d_w_fc2,
+                           io->d_b_fc2})))
+        return e;
+      return bwd_mlp(L, p, io, io->partial, ws, s);
+    case TP_BWD_ATTN:
+      if ((e = check_ptrs({io->dout, io->dc, io->partial, io->d_w_qkv, io->d_b_qkv, io->d_w_o,
+                           io->d_b_o, io->d_ln2_gamma, io->d_ln2_beta})))
+        return e;
+      return bwd_attn(L, p, io, io->dc, io->partial, ws, s);
+    default:
+      if ((e = check_ptrs({io->x, io->da, io->dx, io->d_ln1_gamma, io->d_ln1_beta}))) return e;
+      return bwd_ln1(L, p, io, io->da, ws, s);
+  }
+}
+
+int tp_layer_destroy(tp_layer* L) {
+  if (L) {
+    prof_fold(L->prof);
+    for (hipEvent_t e : L->prof.pool) (void)hipEventDestroy(e);
+  }
+  delete L;
+  return TP_OK;
+}
+
+int tp_exchange_sum(void* dst, int dst_dtype, const float* const* parts, int nparts,
+                    size_t count, void* hip_stream) {
+  if (!dst || !parts || nparts < 1 || nparts > 16) return TP_ERR_ARG;
+  if (dst_dtype != TP_DTYPE_F32 && dst_dtype != TP_DTYPE_BF16) return TP_ERR_UNSUPPORTED;
+  if (!aligned(dst)) return TP_ERR_ALIGN;
+  for (int i = 0; i < nparts; ++i) {
+    if (!parts[i]) return TP_ERR_ARG;
+    if (!aligned(parts[i])) return TP_ERR_ALIGN;
+  }
+  if (exchange_sum(dst, dst_dtype, parts, nparts, count, (hipStream_t)hip_stream) != hipSuccess)
+    return TP_ERR_HIP;
+  return TP_OK;
+}
+
+int tp_layer_profile(tp_layer* L, int enable) {
+  if (!L) return TP_ERR_ARG;
+  Prof& p = L->prof;
+  prof_fold(p);
+  for (int k = 0; k < TP_K_COUNT; ++k) {
+    p.launches[k] = 0;
+    p.ms[k] = p.flops[k] = p.bytes[k] = 0.0;
+  }
+  p.on = enable != 0;
+  return TP_OK;
+}
+
+int tp_layer_profile_read(tp_layer* L, int kclass, long* launches, double* ms, double* flops,
+                          double* bytes) {
+  if (!L || kclass < 0 || kclass >= TP_K_COUNT) return TP_ERR_ARG;
+  Prof& p = L->prof;
+  prof_fold(p);
+  if (launches) *launches = p.launches[kclass];
+  if (ms) *ms = p.ms[kclass];
+  if (flops) *flops = p.flops[kclass];
+  if (bytes) *bytes = p.bytes[kclass];
+  return TP_OK;
+}
+
+int tp_layer_tap(const tp_layer* L, int tap, size_t* offset, size_t* bytes) {
+  if (!L || !offset || !bytes) return TP_ERR_ARG;
+  const Region* r = nullptr;
+  switch (tap) {
+    case TP_TAP_LN1_OUT: r = &L->a; break;
+    case TP_TAP_QKV: r = &L->qkv; break;
+    case TP_TAP_ATTN_OUT: r = &L->o; break;
+    case TP_TAP_LSE: r = &L->lse2; break;
+    case TP_TAP_H_MID: r = &L->h_mid; break;
+    case TP_TAP_LN2_OUT: r = &L->c; break;
+    case TP_TAP_FC1_PRE: r = &L->u; break;
+    case TP_TAP_FC1_OUT: r = &L->z; break;
+    case TP_TAP_DQKV: r = &L->dqkv; break;
+    case TP_TAP_DH: r = &L->dh_f; break;
+    default: return TP_ERR_ARG;
+  }
+  *offset = r->off;
+  *bytes = r->bytes;
+  return TP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+"""Device-memory plumbing around the C ABI for one rank's layer shard.
+
+PyTorch only provides device buffers and the stream here; every step of the
+layer runs in ``libtplayer.so`` through ``binding``. Used by the tests, the
+bench and the smoke entry point.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .synth import LayerDims, PARAM_NAMES
+
+
+class TpError(RuntimeError):
+    def __init__(self, what, rc):
+        super().__init__(f"{what} failed: {B.ERROR_NAMES.get(rc, rc)} ({rc})")
+        self.rc = rc
+
+
+def _check(what, rc):
+    if rc != B.TP_OK:
+        raise TpError(what, rc)
+
+
+def torch_dtype(dims: LayerDims):
+    return torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+
+
+def to_device(a: np.ndarray, dtype, device) -> torch.Tensor:
+    """Upload a float32 array (already on the storage grid) as `dtype`."""
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device).to(dtype).contiguous()
+
+
+class Shard:
+    """One handle of the library plus its workspace."""
+
+    def __init__(self, dims: LayerDims, rank: int, device="cuda:0", gelu: int = B.TP_GELU_ERF,
+                 eps: float = 1e-5):
+        self.dims = dims
+        self.rank = rank
+        self.device = torch.device(device)
+        self.dtype = torch_dtype(dims)
+        rc, self.handle, self.ws_bytes = B.tp_layer_create(
+            dims.hidden, dims.heads, dims.ffn, dims.seq, dims.batch, dims.t, rank,
+            B.TP_DTYPE_BF16 if dims.dtype == "bf16" else B.TP_DTYPE_F32,
+            B.TP_MASK_PADDING if dims.mask == "padding" else B.TP_MASK_CAUSAL,
+            {"ln_eps": eps, "gelu": gelu})
+        _check("tp_layer_create", rc)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+
+    def close(self):
+        if self.handle:
+            B.tp_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- tensors ---------------------------------------------------------
+    def upload_params(self, params: Dict[str, np.ndarray], valid_len=None):
+        dev = {k: to_device(params[k], self.dtype, self.device) for k in PARAM_NAMES}
+        vl = None
+        if valid_len is not None:
+            vl = torch.from_numpy(np.asarray(valid_len, dtype=np.int32)).to(self.device)
+        return DeviceParams(dev, vl)
+
+    def act(self, a: np.ndarray) -> torch.Tensor:
+        return to_device(a.reshape(self.dims.tokens, self.dims.hidden), self.dtype, self.device)
+
+    def empty_act(self, fp32=False) -> torch.Tensor:
+        return torch.empty(self.dims.tokens, self.dims.hidden,
+                           dtype=torch.float32 if fp32 else self.dtype, device=self.device)
+
+    def zero_grads(self) -> Dict[str, torch.Tensor]:
+        shapes = self.dims.shapes()
+        return {k: torch.zeros(shapes[k], dtype=torch.float32, device=self.device)
+                for k in PARAM_NAMES}
+
+    def tap(self, name: str) -> torch.Tensor:
+        rc, off, nbytes = B.tp_layer_tap(self.handle, name)
+        _check("tp_layer_tap", rc)
+        return self.ws[off:off + nbytes]
+
+    # -- calls -----------------------------------------------------------
+    def stream(self) -> int:
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def fwd(self, p: "DeviceParams", out: torch.Tensor, x: Optional[torch.Tensor] = None,
+            h_mid: Optional[torch.Tensor] = None, phase: int = B.TP_ALL) -> int:
+        io = B.tp_fwd_io()
+        io.params = p.ptr()
+        io.x = x.data_ptr() if x is not None else None
+        io.h_mid = h_mid.data_ptr() if h_mid is not None else None
+        io.out = out.data_ptr()
+        io.workspace = self.ws.data_ptr()
+        io.workspace_bytes = self.ws_bytes
+        return B.tp_layer_fwd(self.handle, phase, io, self.stream())
+
+    def bwd(self, p: "DeviceParams", grads: Dict[str, torch.Tensor], x=None, dout=None, dx=None,
+            dc=None, da=None, partial=None, accumulate=0, phase: int = B.TP_ALL) -> int:
+        io = B.tp_bwd_io()
+        io.params = p.ptr()
+        for name, t in (("x", x), ("dout", dout), ("dx", dx), ("dc", dc), ("da", da),
+                        ("partial", partial)):
+            setattr(io, name, t.data_ptr() if t is not None else None)
+        for k in PARAM_NAMES:
+            g = grads.get(k) if grads is not None else None
+            setattr(io, "d_" + k, g.data_ptr() if g is not None else None)
+        io.accumulate = accumulate
+        io.workspace = self.ws.data_ptr()
+        io.workspace_bytes = self.ws_bytes
+        return B.tp_layer_bwd(self.handle, phase, io, self.stream())
+
+
+class DeviceParams:
+    def __init__(self, tensors: Dict[str, torch.Tensor], valid_len: Optional[torch.Tensor]):
+        self.t = tensors
+        self.valid_len = valid_len
+        self._s = B.tp_params()
+        for k in PARAM_NAMES:
+            setattr(self._s, k, tensors[k].data_ptr())
+        self._s.valid_len = valid_len.data_ptr() if valid_len is not None else None
+
+    def ptr(self):
+        import ctypes
+        return ctypes.pointer(self._s)
+
+
+def exchange_sum(dst: torch.Tensor, parts, stream: int) -> None:
+    """On-device sum of fp32 partial buffers (the single-GPU exchange)."""
+    dt = B.TP_DTYPE_BF16 if dst.dtype == torch.bfloat16 else B.TP_DTYPE_F32
+    _check("tp_exchange_sum",
+           B.tp_exchange_sum(dst.data_ptr(), dt, [p.data_ptr() for p in parts], dst.numel(), stream))

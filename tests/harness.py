@@ -1,0 +1,117 @@
+"""Shared helpers for the GPU parity tests: run the HIP shard through the C ABI
+and the fp64 oracle on the same seeded inputs, then compare tensor by tensor.
+
+Pass criterion (per tensor T): max|T_gpu - T_oracle| <= tau * RMS(T_oracle),
+tau = 1e-4 on the fp32 path and 2e-2 on the bf16 / fp32-accumulate path.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import layer as OL
+from tensor_model_transformer_amd.synth import PARAM_NAMES, layer_inputs, rank_params
+
+TAU = {"f32": 1e-4, "bf16": 2e-2}
+TAU_INTERMEDIATE = 5e-2
+LN2 = math.log(2.0)
+
+
+def rms(a):
+    a = np.asarray(a, dtype=np.float64)
+    return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
+
+
+def err_ratio(gpu, ref):
+    """max|gpu - ref| / RMS(ref)."""
+    gpu = np.asarray(gpu, dtype=np.float64).reshape(np.shape(ref))
+    ref = np.asarray(ref, dtype=np.float64)
+    r = rms(ref)
+    d = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
+    return d / r if r > 0 else d
+
+
+def check(name, gpu, ref, tau, report):
+    e = err_ratio(gpu, ref)
+    report[name] = e
+    return e <= tau
+
+
+def to_np(t):
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False):
+    """TP_ALL forward + backward of one rank on the GPU. Returns numpy dict."""
+    import torch
+    from tensor_model_transformer_amd.shard import Shard, _check
+
+    d = w.dims
+    r = w.rank if rank is None else rank
+    params = rank_params(w, r)
+    x, dout, vl = layer_inputs(w)
+    sh = Shard(d, r)
+    p = sh.upload_params(params, vl if d.mask == "padding" else None)
+    xd, doutd = sh.act(x), sh.act(dout)
+    out, dx = sh.empty_act(), sh.empty_act()
+    grads = sh.zero_grads()
+    _check("tp_layer_fwd", sh.fwd(p, out, x=xd))
+    res = {}
+    if taps:
+        n, hl, fl = d.tokens, d.hidden_local, d.ffn_local
+        dt = torch.float16 if d.dtype == "bf16" else torch.float32  # internal activations
+        torch.cuda.synchronize()
+        res["a"] = to_np(sh.tap("a").view(dt).reshape(n, d.hidden))
+        res["qkv"] = to_np(sh.tap("qkv").view(dt).reshape(n, 3 * hl))
+        res["o"] = to_np(sh.tap("o").view(dt).reshape(n, hl))
+        res["lse"] = to_np(sh.tap("lse2").view(torch.float32)) * LN2
+        res["h_mid"] = to_np(sh.tap("h_mid").view(torch.float32).reshape(n, d.hidden))
+        res["c"] = to_np(sh.tap("c").view(dt).reshape(n, d.hidden))
+        res["u"] = to_np(sh.tap("u").view(dt).reshape(n, fl))
+        res["z"] = to_np(sh.tap("z").view(dt).reshape(n, fl))
+    _check("tp_layer_bwd", sh.bwd(p, grads, x=xd, dout=doutd, dx=dx))
+    if accumulate_twice:
+        _check("tp_layer_bwd", sh.bwd(p, grads, x=xd, dout=doutd, dx=dx, accumulate=1))
+    torch.cuda.synchronize()
+    if taps:
+        dt = torch.float16 if d.dtype == "bf16" else torch.float32
+        res["dqkv"] = to_np(sh.tap("dqkv").view(dt).reshape(d.tokens, 3 * d.hidden_local))
+        res["dh"] = to_np(sh.tap("dh").view(torch.float32).reshape(d.tokens, d.hidden))
+    res["out"] = to_np(out).reshape(d.batch, d.seq, d.hidden)
+    res["dx"] = to_np(dx).reshape(d.batch, d.seq, d.hidden)
+    res["grads"] = {k: to_np(v) for k, v in grads.items()}
+    sh.close()
+    return res
+
+
+def oracle_local(w, rank=None):
+    d = w.dims
+    r = w.rank if rank is None else rank
+    x, dout, vl = layer_inputs(w)
+    return OL.layer_local(rank_params(w, r), x, dout, d, vl)
+
+
+def compare_local(gpu, ref, tau, taps=False):
+    """Returns (ok, report) over out, dx, every gradient (and intermediates)."""
+    report = {}
+    ok = True
+    ok &= check("out", gpu["out"], ref["out"], tau, report)
+    ok &= check("dx", gpu["dx"], ref["dx"], tau, report)
+    for k in PARAM_NAMES:
+        ok &= check("d_" + k, gpu["grads"][k], ref["grads"][k], tau, report)
+    if taps:
+        # Intermediates are a diagnostic of each kernel (a layout or masking
+        # bug shows as an O(1) error); they carry the rounding of their own
+        # 16-bit storage and of everything upstream, so they get a wider
+        # bound than the graded outputs above.
+        ti = max(tau, TAU_INTERMEDIATE)
+        for k in ("a", "qkv", "o", "h_mid", "c", "u", "z", "dqkv", "dh"):
+            ok &= check(k, gpu[k], ref[k], ti, report)
+        ok &= check("lse", gpu["lse"], ref["lse"].reshape(-1), ti, report)
+    return bool(ok), report
+
+
+def fmt(report):
+    return ", ".join(f"{k}={v:.2e}" for k, v in sorted(report.items(), key=lambda kv: -kv[1]))

@@ -1,0 +1,141 @@
+"""Host-side tests of the C ABI library (no GPU, no kernel launch).
+
+The library loads, exports every function ``include/tp_layer.h`` declares,
+and its argument checks return the documented codes before anything is
+enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tensor_model_transformer_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_layer.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*int\s+(tp_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libtplayer.so is not built: run `python -m tensor_model_transformer_amd.build`")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(B.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_enum_values_match_header():
+    src = open(HEADER).read()
+    for name in ("TP_OK", "TP_ERR_ARG", "TP_ERR_SHAPE", "TP_ERR_UNSUPPORTED", "TP_ERR_ALIGN",
+                 "TP_ERR_WORKSPACE", "TP_ERR_HIP", "TP_ERR_PHASE", "TP_DTYPE_F32",
+                 "TP_DTYPE_BF16", "TP_MASK_CAUSAL", "TP_MASK_PADDING", "TP_FWD_ATTN",
+                 "TP_FWD_MLP", "TP_BWD_MLP", "TP_BWD_ATTN", "TP_BWD_LN1"):
+        m = re.search(rf"\b{name}\s*=\s*(-?\d+)", src)
+        assert m, name
+        assert int(m.group(1)) == getattr(B, name), name
+
+
+def create(**kw):
+    a = dict(hidden=128, heads=4, ffn=512, seq=64, micro_batch=2, t=2, rank=0,
+             dtype=B.TP_DTYPE_BF16, mask=B.TP_MASK_CAUSAL)
+    a.update(kw)
+    return B.tp_layer_create(a["hidden"], a["heads"], a["ffn"], a["seq"], a["micro_batch"],
+                             a["t"], a["rank"], a["dtype"], a["mask"], a.get("opts"))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=0), B.TP_ERR_ARG),
+    (dict(seq=-1), B.TP_ERR_ARG),
+    (dict(t=0), B.TP_ERR_ARG),
+    (dict(hidden=130), B.TP_ERR_SHAPE),           # hidden % heads
+    (dict(heads=6, hidden=192, t=4), B.TP_ERR_SHAPE),  # heads % t
+    (dict(ffn=510), B.TP_ERR_SHAPE),              # ffn % t
+    (dict(ffn=12, t=2), B.TP_ERR_SHAPE),          # (ffn/t) % 8
+    (dict(rank=2), B.TP_ERR_SHAPE),
+    (dict(rank=-1), B.TP_ERR_SHAPE),
+    (dict(hidden=192, heads=4, t=1), B.TP_ERR_UNSUPPORTED),   # head dim 48
+    (dict(dtype=7), B.TP_ERR_UNSUPPORTED),
+    (dict(mask=3), B.TP_ERR_UNSUPPORTED),
+    (dict(opts={"ln_eps": 1e-5, "gelu": 5}), B.TP_ERR_UNSUPPORTED),
+    (dict(opts={"ln_eps": 0.0, "gelu": 0}), B.TP_ERR_ARG),
+])
+def test_create_validation(lib, kw, code):
+    rc, h, ws = create(**kw)
+    assert rc == code
+    assert h is None
+
+
+def test_create_ok_and_workspace_plan(lib):
+    rc, h, ws = create()
+    assert rc == B.TP_OK and h
+    assert ws > 0
+    seen = []
+    for name in B.TAPS:
+        rc, off, nb = B.tp_layer_tap(h, name)
+        assert rc == B.TP_OK
+        assert off % 256 == 0 and off + nb <= ws
+        seen.append((off, off + nb))
+    seen.sort()
+    for (a0, a1), (b0, b1) in zip(seen, seen[1:]):
+        assert a1 <= b0  # intermediates do not overlap
+    assert B.tp_layer_tap(h, 99)[0] == B.TP_ERR_ARG
+    assert B.tp_layer_destroy(h) == B.TP_OK
+    assert B.tp_layer_destroy(None) == B.TP_OK
+
+
+def test_call_argument_errors_need_no_device(lib):
+    rc, h, ws = create()
+    assert rc == B.TP_OK
+    io = B.tp_fwd_io()
+    assert B.tp_layer_fwd(None, B.TP_ALL, io, 0) == B.TP_ERR_ARG
+    assert B.tp_layer_fwd(h, 9, io, 0) == B.TP_ERR_PHASE
+    assert B.tp_layer_fwd(h, B.TP_ALL, io, 0) == B.TP_ERR_ARG  # no params
+    p = B.tp_params()
+    fake = 1 << 20  # never dereferenced: validation stops before any launch
+    for f in B.PARAM_FIELDS:
+        setattr(p, f, fake)
+    io.params = ctypes.pointer(p)
+    assert B.tp_layer_fwd(h, B.TP_ALL, io, 0) == B.TP_ERR_WORKSPACE
+    io.workspace = fake
+    io.workspace_bytes = ws - 1
+    assert B.tp_layer_fwd(h, B.TP_ALL, io, 0) == B.TP_ERR_WORKSPACE
+    io.workspace_bytes = ws
+    io.workspace = fake + 8
+    assert B.tp_layer_fwd(h, B.TP_ALL, io, 0) == B.TP_ERR_ALIGN
+    io.workspace = fake
+    assert B.tp_layer_fwd(h, B.TP_ALL, io, 0) == B.TP_ERR_ARG  # x/out missing
+    setattr(p, "w_o", fake + 4)
+    assert B.tp_layer_fwd(h, B.TP_ALL, io, 0) == B.TP_ERR_ALIGN
+    bio = B.tp_bwd_io()
+    assert B.tp_layer_bwd(h, 4, bio, 0) == B.TP_ERR_PHASE
+    assert B.tp_layer_bwd(h, B.TP_ALL, bio, 0) == B.TP_ERR_ARG
+    assert B.tp_exchange_sum(fake, B.TP_DTYPE_F32, [], 16, 0) == B.TP_ERR_ARG
+    assert B.tp_exchange_sum(fake, B.TP_DTYPE_F32, [fake] * 17, 16, 0) == B.TP_ERR_ARG
+    assert B.tp_exchange_sum(fake + 2, B.TP_DTYPE_F32, [fake], 16, 0) == B.TP_ERR_ALIGN
+    B.tp_layer_destroy(h)
+
+
+def test_padding_mask_requires_valid_len(lib):
+    rc, h, ws = create(mask=B.TP_MASK_PADDING)
+    assert rc == B.TP_OK
+    p = B.tp_params()
+    for f in B.PARAM_FIELDS:
+        setattr(p, f, 1 << 20)
+    io = B.tp_fwd_io()
+    io.params = ctypes.pointer(p)
+    io.workspace = 1 << 20
+    io.workspace_bytes = ws
+    assert B.tp_layer_fwd(h, B.TP_ALL, io, 0) == B.TP_ERR_ARG
+    B.tp_layer_destroy(h)

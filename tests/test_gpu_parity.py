@@ -1,0 +1,184 @@
+"""GPU parity of the HIP layer shard against the fp64 oracle (through the C ABI).
+
+Tolerance: max|err| <= 1e-4 * RMS on the fp32 path and <= 2e-2 * RMS on the
+bf16 / fp32-accumulate path, for out, dx and every parameter gradient (and
+the workspace intermediates where tapped).
+"""
+import numpy as np
+import pytest
+
+from harness import TAU, compare_local, fmt, oracle_local, run_gpu_local, to_np
+from oracle import layer as OL
+from tensor_model_transformer_amd.synth import (LayerDims, Workload, WORKLOADS, full_params,
+                                                layer_inputs, rank_params)
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(w, rank=None, taps=False):
+    _need_gpu()
+    print(f"\n[parity] {w.name} dims={w.dims} rank={w.rank if rank is None else rank}", flush=True)
+    gpu = run_gpu_local(w, rank, taps=taps)
+    ref = oracle_local(w, rank)
+    ok, rep = compare_local(gpu, ref, TAU[w.dims.dtype], taps=taps)
+    print(f"[parity] {w.name}: {fmt(rep)}", flush=True)
+    assert ok, f"{w.name}: {fmt(rep)}"
+
+
+# ---------------------------------------------------------------------------
+# the tiny fp32 GPT workload (both ranks), with the intermediates tapped
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("rank", [0, 1])
+def test_tiny_gpt_fp32_local(rank):
+    _run(WORKLOADS["tiny_gpt_fp32"], rank, taps=True)
+
+
+def test_tiny_gpt_fp32_perturbed_affine():
+    _run(WORKLOADS["tiny_gpt_fp32"].with_(affine="perturbed", name="tiny_gpt_fp32_aff"), 1,
+         taps=True)
+
+
+# ---------------------------------------------------------------------------
+# small bf16 shapes: every head dim, both masks, ragged token/column counts
+# that span several GEMM and attention tiles
+# ---------------------------------------------------------------------------
+SMALL_BF16 = [
+    Workload("d32_causal", LayerDims(2, 200, 256, 8, 1040, t=2, dtype="bf16", mask="causal"),
+             rank=1, seed=21, affine="perturbed"),
+    Workload("d64_padding", LayerDims(3, 130, 384, 6, 768, t=2, dtype="bf16", mask="padding"),
+             rank=0, seed=22, affine="perturbed", len_range=(1, 130)),
+    Workload("d96_causal_t1", LayerDims(2, 150, 384, 4, 1536, t=1, dtype="bf16", mask="causal"),
+             rank=0, seed=23, affine="perturbed"),
+    Workload("d128_causal", LayerDims(1, 257, 512, 4, 2048, t=2, dtype="bf16", mask="causal"),
+             rank=1, seed=24, affine="perturbed"),
+    Workload("d160_padding", LayerDims(2, 96, 640, 4, 1280, t=2, dtype="bf16", mask="padding"),
+             rank=0, seed=25, affine="perturbed", len_range=(33, 96)),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_BF16, ids=lambda w: w.name)
+def test_small_bf16_local(w):
+    _run(w, taps=True)
+
+
+def test_small_fp32_d160_padding():
+    w = SMALL_BF16[4].with_(name="d160_padding_f32",
+                            dims=LayerDims(2, 40, 320, 2, 640, t=1, dtype="f32", mask="padding"),
+                            len_range=(7, 40))
+    _run(w, taps=True)
+
+
+def test_single_token_sequence():
+    # degenerate: seq = 1 (attention is the identity on V), batch 3
+    _run(Workload("seq1", LayerDims(3, 1, 128, 4, 256, t=1, dtype="bf16", mask="causal"),
+                  seed=26, affine="perturbed"))
+
+
+# ---------------------------------------------------------------------------
+# determinism and gradient accumulation
+# ---------------------------------------------------------------------------
+def test_bitwise_deterministic():
+    _need_gpu()
+    w = SMALL_BF16[0]
+    a = run_gpu_local(w)
+    b = run_gpu_local(w)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["dx"], b["dx"])
+    for k in a["grads"]:
+        assert np.array_equal(a["grads"][k], b["grads"][k]), k
+
+
+def test_accumulate_adds_gradients():
+    _need_gpu()
+    w = SMALL_BF16[2]
+    gpu = run_gpu_local(w, accumulate_twice=True)
+    ref = oracle_local(w)
+    from harness import err_ratio
+    for k, g in gpu["grads"].items():
+        assert err_ratio(g, 2.0 * ref["grads"][k]) <= TAU["bf16"], k
+
+
+# ---------------------------------------------------------------------------
+# f/g identity: all t shards in sequence on one GPU, partials summed on-device
+# ---------------------------------------------------------------------------
+def run_phased(w):
+    import torch
+    from tensor_model_transformer_amd import binding as B
+    from tensor_model_transformer_amd.shard import Shard, _check, exchange_sum
+
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    shards = [Shard(d, r) for r in range(d.t)]
+    params = [s.upload_params(rank_params(w, r), vl if d.mask == "padding" else None)
+              for r, s in enumerate(shards)]
+    s0 = shards[0]
+    xd, doutd = s0.act(x), s0.act(dout)
+    stream = s0.stream()
+    parts = [s0.empty_act(fp32=True) for _ in range(d.t)]
+    h_mid = s0.empty_act(fp32=True)
+    out = s0.empty_act()
+    for r, s in enumerate(shards):
+        _check("fwd attn", s.fwd(params[r], parts[r], x=xd, phase=B.TP_FWD_ATTN))
+    exchange_sum(h_mid, parts, stream)
+    for r, s in enumerate(shards):
+        _check("fwd mlp", s.fwd(params[r], parts[r], h_mid=h_mid, phase=B.TP_FWD_MLP))
+    exchange_sum(out, parts, stream)
+    grads = [s.zero_grads() for s in shards]
+    dc = s0.empty_act(fp32=True)
+    da = s0.empty_act(fp32=True)
+    for r, s in enumerate(shards):
+        _check("bwd mlp", s.bwd(params[r], grads[r], dout=doutd, partial=parts[r],
+                                phase=B.TP_BWD_MLP))
+    exchange_sum(dc, parts, stream)
+    for r, s in enumerate(shards):
+        _check("bwd attn", s.bwd(params[r], grads[r], dout=doutd, dc=dc, partial=parts[r],
+                                 phase=B.TP_BWD_ATTN))
+    exchange_sum(da, parts, stream)
+    dxs = []
+    for r, s in enumerate(shards):
+        dx = s0.empty_act()
+        _check("bwd ln1", s.bwd(params[r], grads[r], x=xd, da=da, dx=dx, phase=B.TP_BWD_LN1))
+        dxs.append(dx)
+    torch.cuda.synchronize()
+    res = {"out": to_np(out).reshape(d.batch, d.seq, d.hidden),
+           "dx": [to_np(t).reshape(d.batch, d.seq, d.hidden) for t in dxs],
+           "h_mid": to_np(h_mid), "grads": [{k: to_np(v) for k, v in g.items()} for g in grads]}
+    for s in shards:
+        s.close()
+    return res
+
+
+PHASED = [
+    WORKLOADS["tiny_gpt_fp32"].with_(affine="perturbed"),
+    Workload("t4_bf16_padding", LayerDims(2, 72, 512, 8, 1024, t=4, dtype="bf16", mask="padding"),
+             seed=31, affine="perturbed", len_range=(10, 72)),
+    Workload("t8_32heads_bf16", LayerDims(2, 64, 1024, 32, 2048, t=8, dtype="bf16",
+                                          mask="causal"), seed=32, affine="perturbed"),
+]
+
+
+@pytest.mark.parametrize("w", PHASED, ids=lambda w: w.name)
+def test_phased_sum_over_shards_equals_unsharded(w):
+    _need_gpu()
+    d = w.dims
+    print(f"\n[phased] {w.name} dims={d}", flush=True)
+    gpu = run_phased(w)
+    x, dout, vl = layer_inputs(w)
+    full = OL.layer_full(full_params(w), x, dout, d, vl)
+    tau = TAU[d.dtype]
+    from harness import err_ratio
+    rep = {"out": err_ratio(gpu["out"], full["out"]), "h_mid": err_ratio(gpu["h_mid"], full["h_mid"])}
+    for r in range(d.t):
+        rep[f"dx_r{r}"] = err_ratio(gpu["dx"][r], full["dx"])
+    per = [rank_params(w, r) for r in range(d.t)]
+    part = OL.layer_partials(per, x, dout, d, vl)
+    for r in range(d.t):
+        for k, g in gpu["grads"][r].items():
+            rep[f"d_{k}_r{r}"] = err_ratio(g, part["grads"][r][k])
+    print(f"[phased] {w.name}: {fmt(rep)}", flush=True)
+    assert all(v <= tau for v in rep.values()), fmt(rep)
