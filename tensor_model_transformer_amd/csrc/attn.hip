@@ -17,10 +17,11 @@
 // the running max / sum of the online softmax stay in registers and the
 // 32x32 accumulator of S^T feeds the P^T operand of the next MFMA directly.
 // Within each 16-key slice the accumulator holds keys in the order
-// {4h..4h+3, 8+4h..8+4h+3} for lane half h; V^T is written to LDS in that
-// same order so both MFMA operands agree. Scores are kept in the log2 domain
-// (scale * log2(e) folded into S) and the per-row normaliser is saved as
-// lse2 = max + log2(sum).
+// {4h..4h+3, 8+4h..8+4h+3} for lane half h; the V^T operand is read in that
+// same order straight from the row-major V tile with ds_read_b64_tr_b16
+// (gfx950's transposing LDS read), so no transposed copy is ever built.
+// Scores are kept in the log2 domain (scale * log2(e) folded into S) and the
+// per-row normaliser is saved as lse2 = max + log2(sum).
 //
 // Backward (deterministic, no atomics): delta = rowsum(dO * O); one kernel
 // owns a block of keys and sweeps the queries (dK, dV); another owns a block
@@ -52,75 +53,79 @@ __device__ __forceinline__ f16x8 pack8(const float* v) {
   return __builtin_bit_cast(f16x8, u);
 }
 
-__device__ __forceinline__ void transpose8x8_b16(const uint4 r[8], uint4 w[8]) {
+// 8 consecutive accumulator values starting at `off` (0 or 8), packed to fp16.
+__device__ __forceinline__ f16x8 pack8v(const f32x16& a, int off) {
+  float v[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t o[4];
+  for (int i = 0; i < 8; ++i) v[i] = a[off + i];
+  return pack8(v);
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define LDS_V4S(p) ((__attribute__((address_space(3))) v4s*)(p))
+
+// Four 16-bit values of one column of a row-major LDS tile T (pitch P
+// elements), read transposed with ds_read_b64_tr_b16: within each 16-lane
+// group, lane j receives T[k0 + i][mb + j] for i = 0..3 when input lane L
+// points at T[k0 + L/4][mb + 4*(L%4)].
+__device__ __forceinline__ uint2 tr4(const f16* T, int P, int k0, int mb, int L) {
+  const f16* p = T + (k0 + (L >> 2)) * P + mb + 4 * (L & 3);
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_V4S(p)));
+}
+
+// MFMA operand whose rows are columns m0 .. m0+31 of the row-major tile T
+// (this lane's column m0 + lane%32) and whose 8 reduction slots are the tile
+// rows kA + 0..3 then kB + 0..3, with (kA, kB) given for lane half h.
+__device__ __forceinline__ f16x8 tr_frag(const f16* T, int P, int m0, int kA, int kB, int lane) {
+  const int g = lane >> 4, L = lane & 15;
+  const int mb = m0 + 16 * (g & 1);
+  const uint2 a = tr4(T, P, kA, mb, L), b = tr4(T, P, kB, mb, L);
+  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Register staging for a [R][D] row-major slice of global memory (row stride
+// ld), rows >= nrows read as zero; stored into an LDS tile of pitch P.
+template <int R, int D, int NT>
+struct RowTile {
+  static constexpr int kChunks = R * (D / 8);
+  static constexpr int kPer = (kChunks + NT - 1) / NT;
+  uint4 st[kPer];
+  __device__ __forceinline__ void load(const f16* __restrict__ src, long ld, int r0, int nrows,
+                                       int tid) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t* lo = reinterpret_cast<const uint32_t*>(&r[2 * p]);
-      const uint32_t* hi = reinterpret_cast<const uint32_t*>(&r[2 * p + 1]);
-      o[p] = __builtin_amdgcn_perm(hi[j >> 1], lo[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / (D / 8), dc = c % (D / 8);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if ((kChunks % NT == 0 || c < kChunks) && r0 + row < nrows)
+        v = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + row) * ld + 8 * dc);
+      st[i] = v;
     }
-    w[j] = make_uint4(o[0], o[1], o[2], o[3]);
   }
-}
-
-// Row (within a block of rows) stored at LDS position 8*g + s of a transposed
-// tile: position p = 16c + 8h + s holds row 16c + 4h + s (s < 4) or
-// 16c + 8 + 4h + (s - 4) (s >= 4) -- the order a 32x32 accumulator column
-// holds its rows in, two 16-row MFMA steps per 32 rows.
-__device__ __forceinline__ int perm_row(int g, int s) {
-  const int c = g >> 1, h = g & 1;
-  return 16 * c + (s < 4 ? 4 * h + s : 8 + 4 * h + (s - 4));
-}
-
-// Stores rows [r0, r0+R) x D of a row-major 16-bit matrix (row stride ld) into
-// LDS transposed: dst[d * ldt + position]. Rows >= nrows are zero. One 8x8
-// block per thread-iteration.
-template <int R, int D>
-__device__ __forceinline__ void load_transposed(const f16* __restrict__ src, long ld, int r0,
-                                                int nrows, f16* dst, int ldt, int tid, int nt) {
-  constexpr int nblk = (R / 8) * (D / 8);
-  for (int bidx = tid; bidx < nblk; bidx += nt) {
-    const int g = bidx % (R / 8), dg = bidx / (R / 8);
-    uint4 r[8], w[8];
+  __device__ __forceinline__ void store(f16* dst, int P, int tid) const {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int row = r0 + perm_row(g, s);
-      r[s] = row < nrows ? *reinterpret_cast<const uint4*>(src + (size_t)row * ld + 8 * dg)
-                         : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / (D / 8), dc = c % (D / 8);
+      if (kChunks % NT == 0 || c < kChunks)
+        *reinterpret_cast<uint4*>(dst + row * P + 8 * dc) = st[i];
     }
-    transpose8x8_b16(r, w);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dst + (8 * dg + e) * ldt + 8 * g) = w[e];
   }
-}
-
-// Row-major copy of rows [r0, r0+R) x D into LDS (row stride ldr).
-template <int R, int D>
-__device__ __forceinline__ void load_rows(const f16* __restrict__ src, long ld, int r0, int nrows,
-                                          f16* dst, int ldr, int tid, int nt) {
-  constexpr int nch = R * (D / 8);
-  for (int c = tid; c < nch; c += nt) {
-    const int row = c / (D / 8), dc = c % (D / 8);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + row < nrows) v = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + row) * ld + 8 * dc);
-    *reinterpret_cast<uint4*>(dst + row * ldr + 8 * dc) = v;
-  }
-}
+};
 
 // ============================================================================
 // fp16 forward
 // ============================================================================
+// A workgroup owns 128 queries (32 per wave) of one (sequence, head) and
+// sweeps 64-key blocks; K and V tiles are double-buffered in LDS through
+// registers (the next block's loads are in flight during the current MFMAs).
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
     const f16* __restrict__ qkv, f16* __restrict__ o, float* __restrict__ lse2,
     const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2) {
-  constexpr int KB = 64, LDK = D + 8, LDV = KB + 8;
+  constexpr int KB = 64, P = D + 8, TILE = KB * P;
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* Ks = reinterpret_cast<f16*>(smem);  // [KB][LDK]
-  f16* Vt = Ks + KB * LDK;                   // [D][LDV]
+  f16* lds = reinterpret_cast<f16*>(smem);  // [2][K tile, V tile]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -151,62 +156,81 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
     for (int e = 0; e < 16; ++e) O[t][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int kb0 = 0; kb0 < kv_end; kb0 += KB) {
-    __syncthreads();
-    load_rows<KB, D>(Kp, ldq, kb0, seq, Ks, LDK, tid, 256);
-    load_transposed<KB, D>(Vp, ldq, kb0, seq, Vt, LDV, tid, 256);
-    __syncthreads();
-    if (causal && kb0 > qw0 + 31) continue;  // every key after every query of this wave
-
-    f32x16 S[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) S[st][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        S[st] = mfma32(ld8(Ks + (32 * st + l32) * LDK + 16 * ks + 8 * hh), qf[ks], S[st]);
+  RowTile<KB, D, 256> kt, vt;
+  const int nblk = (kv_end + KB - 1) / KB;
+  if (nblk > 0) {
+    kt.load(Kp, ldq, 0, seq, tid);
+    vt.load(Vp, ldq, 0, seq, tid);
+    kt.store(lds, P, tid);
+    vt.store(lds + TILE, P, tid);
+  }
+  __syncthreads();
+  for (int ib = 0; ib < nblk; ++ib) {
+    const int kb0 = ib * KB;
+    const bool more = ib + 1 < nblk;
+    if (more) {
+      kt.load(Kp, ldq, kb0 + KB, seq, tid);
+      vt.load(Vp, ldq, kb0 + KB, seq, tid);
     }
-    // S[st][4*jj+ii]: key kb0 + 32*st + 8*jj + 4*hh + ii, query q
-    float mx = -INFINITY;
+    const f16* Ks = lds + (ib & 1) * 2 * TILE;
+    const f16* Vs = Ks + TILE;
+    if (!(causal && kb0 > qw0 + 31)) {  // some key of this block precedes a query of this wave
+      f32x16 S[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const float s = key < lim ? S[st][e] * sl2 : -INFINITY;
-        S[st][e] = s;
-        mx = fmaxf(mx, s);
+        for (int e = 0; e < 16; ++e) S[st][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          S[st] = mfma32(ld8(Ks + (32 * st + l32) * P + 16 * ks + 8 * hh), qf[ks], S[st]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float ls = 0.f;
+      // S[st][4*jj+ii]: key kb0 + 32*st + 8*jj + 4*hh + ii, query q
+      float mx = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(S[st][e] - m_new);
-        S[st][e] = p;
-        ls += p;
-      }
-    ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const float s = key < lim ? S[st][e] * sl2 : -INFINITY;
+          S[st][e] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      float ls = 0.f;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) O[t][e] *= alpha;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float pv[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) pv[s] = S[c >> 1][8 * (c & 1) + s];
-      const f16x8 pf = pack8(pv);
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(S[st][e] - m_new);
+          S[st][e] = p;
+          ls += p;
+        }
+      ls += __shfl_xor(ls, 32, 64);
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
-        O[t] = mfma32(ld8(Vt + (32 * t + l32) * LDV + 16 * c + 8 * hh), pf, O[t]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) O[t][e] *= alpha;
+      // O^T[d][q] += sum_key V[key][d] P[q][key]; 16 keys per MFMA, slot order
+      // {4h..4h+3, 8+4h..8+4h+3} within the 16 (the accumulator's row order)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f16x8 pf = pack8v(S[c >> 1], 8 * (c & 1));
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+          O[t] = mfma32(tr_frag(Vs, P, 32 * t, 16 * c + 4 * hh, 16 * c + 8 + 4 * hh, lane), pf,
+                        O[t]);
+      }
     }
+    if (more) {
+      f16* nxt = lds + ((ib + 1) & 1) * 2 * TILE;
+      kt.store(nxt, P, tid);
+      vt.store(nxt + TILE, P, tid);
+    }
+    __syncthreads();
   }
 
   if (q < seq) {
@@ -253,19 +277,19 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 // ============================================================================
 // fp16 backward: dK, dV (a workgroup owns 128 keys, 32 per wave)
 // ============================================================================
+// Sweeps 64-query blocks (two 32-query halves per MFMA step); Q and dO tiles
+// are double-buffered in LDS through registers. Q^T and dO^T operands are
+// read from the row-major tiles with transposing LDS reads.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ dO, const float* __restrict__ lse2,
     const float* __restrict__ delta, f16* __restrict__ dqkv, const int* __restrict__ valid_len,
     int seq, int Hl, int causal, float sl2, float scale) {
-  constexpr int QB = 32, LDR = D + 8, LDT = QB + 8;
+  constexpr int QB = 64, P = D + 8, TILE = QB * P;
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* Qs = reinterpret_cast<f16*>(smem);  // [QB][LDR]
-  f16* dOs = Qs + QB * LDR;                  // [QB][LDR]
-  f16* Qt = dOs + QB * LDR;                  // [D][LDT]
-  f16* dOt = Qt + D * LDT;                   // [D][LDT]
-  float* ls = reinterpret_cast<float*>(dOt + D * LDT);  // [QB]
-  float* dl = ls + QB;                                   // [QB]
+  f16* lds = reinterpret_cast<f16*>(smem);                          // [2][Q, dO]
+  float* ls = reinterpret_cast<float*>(lds + 4 * TILE);             // [2][QB]
+  float* dl = ls + 2 * QB;                                          // [2][QB]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -301,49 +325,77 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
 
   const bool wave_keys_valid = kw0 < (causal ? seq : L);
   const int q_begin = causal ? kblk * 128 : 0;
-  for (int q0 = q_begin; q0 < seq; q0 += QB) {
-    __syncthreads();
-    load_rows<QB, D>(Qp, ldq, q0, seq, Qs, LDR, tid, 256);
-    load_rows<QB, D>(dOp, ldo, q0, seq, dOs, LDR, tid, 256);
-    load_transposed<QB, D>(Qp, ldq, q0, seq, Qt, LDT, tid, 256);
-    load_transposed<QB, D>(dOp, ldo, q0, seq, dOt, LDT, tid, 256);
+  const int nblk = (seq - q_begin + QB - 1) / QB;
+  RowTile<QB, D, 256> qt, gt;
+  float lsr = 0.f, dlr = 0.f;
+  auto fetch = [&](int q0) {
+    qt.load(Qp, ldq, q0, seq, tid);
+    gt.load(dOp, ldo, q0, seq, tid);
     if (tid < QB) {
       const int qq = q0 + tid;
-      ls[tid] = qq < seq ? lsp[qq] : 0.f;
-      dl[tid] = qq < seq ? dlp[qq] : 0.f;
+      lsr = qq < seq ? lsp[qq] : 0.f;
+      dlr = qq < seq ? dlp[qq] : 0.f;
     }
-    __syncthreads();
-    if (!wave_keys_valid || (causal && q0 + QB - 1 < kw0)) continue;
-
-    f32x16 S, dP;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      S = mfma32(ld8(Qs + l32 * LDR + 16 * ks + 8 * hh), kf[ks], S);
-      dP = mfma32(ld8(dOs + l32 * LDR + 16 * ks + 8 * hh), vf[ks], dP);
+  };
+  auto put = [&](int buf) {
+    f16* base = lds + buf * 2 * TILE;
+    qt.store(base, P, tid);
+    gt.store(base + TILE, P, tid);
+    if (tid < QB) {
+      ls[buf * QB + tid] = lsr;
+      dl[buf * QB + tid] = dlr;
     }
-    // element e: query q0 + 8*(e>>2) + 4*hh + (e&3), key = this lane's key
-    float P[16], dS[16];
+  };
+  if (nblk > 0) {
+    fetch(q_begin);
+    put(0);
+  }
+  __syncthreads();
+  for (int ib = 0; ib < nblk; ++ib) {
+    const int q0 = q_begin + ib * QB;
+    const bool more = ib + 1 < nblk;
+    if (more) fetch(q0 + QB);
+    const f16* Qs = lds + (ib & 1) * 2 * TILE;
+    const f16* Gs = Qs + TILE;
+    const float* lsb = ls + (ib & 1) * QB;
+    const float* dlb = dl + (ib & 1) * QB;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int qr = 8 * (e >> 2) + 4 * hh + (e & 3);
-      const int qq = q0 + qr;
-      const bool ok = qq < seq && key < L && (!causal || key <= qq);
-      const float p = ok ? exp2f(S[e] * sl2 - ls[qr]) : 0.f;
-      P[e] = p;
-      dS[e] = p * (dP[e] - dl[qr]);
-    }
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qh0 = q0 + 32 * qs;  // first query of this half
+      if (!wave_keys_valid || (causal && qh0 + 31 < kw0)) continue;
+      f32x16 S, dP;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const f16x8 pf = pack8(P + 8 * c);
-      const f16x8 sf = pack8(dS + 8 * c);
+      for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        dV[t] = mfma32(ld8(dOt + (32 * t + l32) * LDT + 16 * c + 8 * hh), pf, dV[t]);
-        dK[t] = mfma32(ld8(Qt + (32 * t + l32) * LDT + 16 * c + 8 * hh), sf, dK[t]);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        S = mfma32(ld8(Qs + (32 * qs + l32) * P + 16 * ks + 8 * hh), kf[ks], S);
+        dP = mfma32(ld8(Gs + (32 * qs + l32) * P + 16 * ks + 8 * hh), vf[ks], dP);
+      }
+      // element e: query qh0 + 8*(e>>2) + 4*hh + (e&3), key = this lane's key
+      float Pv[16], dS[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int qr = 32 * qs + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const int qq = q0 + qr;
+        const bool ok = qq < seq && key < L && (!causal || key <= qq);
+        const float p = ok ? exp2f(S[e] * sl2 - lsb[qr]) : 0.f;
+        Pv[e] = p;
+        dS[e] = p * (dP[e] - dlb[qr]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const f16x8 pf = pack8(Pv + 8 * c);
+        const f16x8 sf = pack8(dS + 8 * c);
+        const int kA = 32 * qs + 16 * c + 4 * hh, kB = kA + 8;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          dV[t] = mfma32(tr_frag(Gs, P, 32 * t, kA, kB, lane), pf, dV[t]);
+          dK[t] = mfma32(tr_frag(Qs, P, 32 * t, kA, kB, lane), sf, dK[t]);
+        }
       }
     }
+    if (more) put((ib + 1) & 1);
+    __syncthreads();
   }
 
   if (key < seq) {
@@ -373,11 +425,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ dO, const float* __restrict__ lse2,
     const float* __restrict__ delta, f16* __restrict__ dqkv, const int* __restrict__ valid_len,
     int seq, int Hl, int causal, float sl2, float scale) {
-  constexpr int KB = 64, LDR = D + 8, LDT = KB + 8;
+  constexpr int KB = 64, P = D + 8, TILE = KB * P;
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* Ks = reinterpret_cast<f16*>(smem);  // [KB][LDR]
-  f16* Vs = Ks + KB * LDR;                   // [KB][LDR]
-  f16* Kt = Vs + KB * LDR;                   // [D][LDT]
+  f16* lds = reinterpret_cast<f16*>(smem);  // [2][K tile, V tile]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -415,39 +465,58 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dQ[t][e] = 0.f;
 
-  for (int kb0 = 0; kb0 < kv_end; kb0 += KB) {
-    __syncthreads();
-    load_rows<KB, D>(Kp, ldq, kb0, seq, Ks, LDR, tid, 256);
-    load_rows<KB, D>(Vp, ldq, kb0, seq, Vs, LDR, tid, 256);
-    load_transposed<KB, D>(Kp, ldq, kb0, seq, Kt, LDT, tid, 256);
-    __syncthreads();
-    if (causal && kb0 > qw0 + 31) continue;
-
-    float dS[2][16];
+  RowTile<KB, D, 256> kt, vt;
+  const int nblk = (kv_end + KB - 1) / KB;
+  if (nblk > 0) {
+    kt.load(Kp, ldq, 0, seq, tid);
+    vt.load(Vp, ldq, 0, seq, tid);
+    kt.store(lds, P, tid);
+    vt.store(lds + TILE, P, tid);
+  }
+  __syncthreads();
+  for (int ib = 0; ib < nblk; ++ib) {
+    const int kb0 = ib * KB;
+    const bool more = ib + 1 < nblk;
+    if (more) {
+      kt.load(Kp, ldq, kb0 + KB, seq, tid);
+      vt.load(Vp, ldq, kb0 + KB, seq, tid);
+    }
+    const f16* Ks = lds + (ib & 1) * 2 * TILE;
+    const f16* Vs = Ks + TILE;
+    if (!(causal && kb0 > qw0 + 31)) {
+      float dS[2][16];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f32x16 S, dP;
+      for (int st = 0; st < 2; ++st) {
+        f32x16 S, dP;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
+        for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        S = mfma32(ld8(Ks + (32 * st + l32) * LDR + 16 * ks + 8 * hh), qf[ks], S);
-        dP = mfma32(ld8(Vs + (32 * st + l32) * LDR + 16 * ks + 8 * hh), gf[ks], dP);
+        for (int ks = 0; ks < D / 16; ++ks) {
+          S = mfma32(ld8(Ks + (32 * st + l32) * P + 16 * ks + 8 * hh), qf[ks], S);
+          dP = mfma32(ld8(Vs + (32 * st + l32) * P + 16 * ks + 8 * hh), gf[ks], dP);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int k = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const float p = (qok && k < lim) ? exp2f(S[e] * sl2 - lq) : 0.f;
+          dS[st][e] = p * (dP[e] - dq_);
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const float p = (qok && key < lim) ? exp2f(S[e] * sl2 - lq) : 0.f;
-        dS[st][e] = p * (dP[e] - dq_);
+      for (int c = 0; c < 4; ++c) {
+        const f16x8 sf = pack8(&dS[c >> 1][8 * (c & 1)]);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+          dQ[t] = mfma32(tr_frag(Ks, P, 32 * t, 16 * c + 4 * hh, 16 * c + 8 + 4 * hh, lane), sf,
+                         dQ[t]);
       }
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f16x8 sf = pack8(&dS[c >> 1][8 * (c & 1)]);
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-        dQ[t] = mfma32(ld8(Kt + (32 * t + l32) * LDT + 16 * c + 8 * hh), sf, dQ[t]);
+    if (more) {
+      f16* nxt = lds + ((ib + 1) & 1) * 2 * TILE;
+      kt.store(nxt, P, tid);
+      vt.store(nxt + TILE, P, tid);
     }
+    __syncthreads();
   }
 
   if (qok) {
@@ -605,11 +674,11 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(
 // Host launchers
 // ============================================================================
 template <int D>
-static size_t fwd_lds() { return (size_t)(64 * (D + 8) + D * 72) * 2; }
+static size_t fwd_lds() { return (size_t)4 * 64 * (D + 8) * 2; }
 template <int D>
-static size_t dkdv_lds() { return (size_t)(2 * 32 * (D + 8) + 2 * D * 40) * 2 + 2 * 32 * 4; }
+static size_t dkdv_lds() { return (size_t)4 * 64 * (D + 8) * 2 + 4 * 64 * 4; }
 template <int D>
-static size_t dq_lds() { return (size_t)(2 * 64 * (D + 8) + D * 72) * 2; }
+static size_t dq_lds() { return (size_t)4 * 64 * (D + 8) * 2; }
 
 template <typename K>
 static hipError_t set_lds(K kern, size_t bytes) {
