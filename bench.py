@@ -38,14 +38,15 @@ def algorithmic_flops(d, valid_len):
     return 3 * (gemm + 4 * d.head_dim * d.heads_local * pairs)
 
 
-def cpu_baseline(w, seqs):
+def cpu_baseline(w, seqs, min_seconds):
     """The fp64 oracle timed on the host on a bounded sample: the same layer
-    shard with `seqs` sequences instead of the full micro-batch."""
-    import numpy as np
+    shard with `seqs` sequences (default: the whole micro-batch), forward +
+    backward, repeated until `min_seconds` of CPU work have run."""
     from oracle import layer as OL
     from tensor_model_transformer_amd.synth import layer_inputs, rank_params
 
     d = w.dims
+    seqs = min(seqs or d.batch, d.batch)
     ws = w.with_(dims=d.__class__(seqs, d.seq, d.hidden, d.heads, d.ffn, d.t, d.dtype, d.mask))
     params = rank_params(ws)
     x, dout, vl = layer_inputs(ws)
@@ -54,14 +55,75 @@ def cpu_baseline(w, seqs):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    OL.layer_local(params, x, dout, ws.dims, vl)
-    dt = time.perf_counter() - t0
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        OL.layer_local(params, x, dout, ws.dims, vl)
+        dt += time.perf_counter() - t0
+        reps += 1
     f = algorithmic_flops(ws.dims, vl)
-    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": reps * f / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": dt,
-            "sample": f"{seqs} of {d.batch} sequences of the same shard (fp64 NumPy, LOCAL mode, "
-                      f"fwd+bwd, {f / 1e9:.1f} GFLOP)"}
+            "sample": f"{seqs} of {d.batch} sequences of the {w.name} shard, fp64 NumPy oracle "
+                      f"(LOCAL mode, fwd+bwd, {f / 1e9:.1f} GFLOP), run {reps}x"}
+
+
+def source_digest(paths):
+    """sha256 over the given kernel sources, in order; ties a stored counter
+    reading to the code it was taken from."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+# Kernel sources whose counter readings a traffic summary holds, per kernel class.
+TRAFFIC_SOURCES = {"gemm": ["tensor_model_transformer_amd/csrc/gemm.hip",
+                            "tensor_model_transformer_amd/csrc/common.hpp"]}
+
+
+def stored_traffic(kclass, workload):
+    """HBM bytes per launch of `kclass` on `workload`, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, already scaled by the copy-kernel
+    calibration; None when there is no summary or the kernel source changed
+    since the counters were read."""
+    path = os.path.join(ROOT, "profiles", f"{kclass}_traffic_{workload}.md")
+    if kclass not in TRAFFIC_SOURCES or not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                kv[k.strip("` ")] = v.strip().strip("`")
+    if kv.get("source_sha256") != source_digest(TRAFFIC_SOURCES[kclass]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes, reps):
+    """A plain copy of known size through the library's own exchange kernel
+    (one fp32 part in, fp32 out): the calibration run for the FETCH_SIZE and
+    WRITE_SIZE counters."""
+    import torch
+    from tensor_model_transformer_amd import binding as B
+    from tensor_model_transformer_amd.shard import exchange_sum
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(reps):
+        exchange_sum(dst, [src], stream)
+    torch.cuda.synchronize()
+    assert bool((dst == 1).all()), "copy probe produced wrong values"
+    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                      "reps": reps, "kernel": "tp_exchange_sum(1 part, f32)",
+                      "dtype_code": B.TP_DTYPE_F32}))
 
 
 def main():
@@ -70,8 +132,12 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt_1p2b_t1")
-    ap.add_argument("--cpu-seqs", type=int, default=1)
+    ap.add_argument("--cpu-seqs", type=int, default=0,
+                    help="sequences in the oracle sample (default: the whole micro-batch)")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU only (asked for --gpus {args.gpus}); "
@@ -87,6 +153,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 10)
+        return
     w = WORKLOADS[args.workload]
     d = w.dims
     params = rank_params(w)
@@ -141,17 +210,20 @@ def main():
         achieved = bd["gflop_per_step"] / bd["ms_per_step"]  # GFLOP/ms = TFLOP/s
         roof = {"kernel": dom, "bound": "mfma" if d.dtype == "bf16" else "alu",
                 "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-                "traffic": None}
+                "traffic": stored_traffic(dom, w.name),
+                "algorithmic_bytes_per_launch": bd["gbyte_per_step"] * 1e9 / bd["launches_per_step"]}
     else:
         achieved = bd["gbyte_per_step"] / bd["ms_per_step"] * 1e3  # GB/s
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": stored_traffic(dom, w.name),
+                "algorithmic_bytes_per_launch": bd["gbyte_per_step"] * 1e9 / bd["launches_per_step"]}
     roof["launches_per_step"] = bd["launches_per_step"]
     roof["avg_launch_ms"] = bd["ms_per_step"] / bd["launches_per_step"]
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seqs)
+        cpu = cpu_baseline(w, args.cpu_seqs, args.cpu_min_seconds)
         print(f"[bench] cpu oracle: {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['cores']} threads "
               f"({cpu['seconds']:.1f} s)", file=sys.stderr, flush=True)
 
