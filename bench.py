@@ -163,7 +163,7 @@ def main():
     sh = Shard(d, w.rank)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
-    out, dx = sh.empty_act(), sh.empty_act()
+    out, dx = sh.empty_act(), sh.empty_dx()
     grads = sh.zero_grads()
     del params
 

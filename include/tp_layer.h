@@ -42,8 +42,11 @@
  *      w_o   [h_l, h]                   (rows r*h_l ... of the full tensor)
  *      w_fc1 [h, f_l],   b_fc1 [f_l]
  *      w_fc2 [f_l, h]
- *  - Storage dtype (TP_DTYPE_F32 or TP_DTYPE_BF16) applies to x, dout, dx,
+ *  - Storage dtype (TP_DTYPE_F32 or TP_DTYPE_BF16) applies to x, dout,
  *    out (TP_ALL) and every parameter. Accumulation and statistics are fp32.
+ *    dx, the gradient of the residual stream handed to the layer below, is
+ *    fp32 by default (tp_layer_opts.dx_dtype selects the storage dtype
+ *    instead), as are the other residual-stream tensors crossing phases.
  *    Every gradient of a parameter is written in fp32. With TP_DTYPE_BF16
  *    the activations and gradients kept inside the layer (LayerNorm outputs,
  *    qkv, attention output, FC1 pre/post activation and their gradients) are
@@ -100,6 +103,8 @@ typedef struct tp_layer tp_layer;
 typedef struct {
   float ln_eps;     /* LayerNorm epsilon (default 1e-5) */
   int gelu;         /* TP_GELU_ERF (default) or TP_GELU_TANH */
+  int dx_dtype;     /* dtype of tp_bwd_io.dx: TP_DTYPE_F32 (default, also the
+                       value of a zeroed struct) or the layer's storage dtype */
 } tp_layer_opts;
 
 /* Parameters of rank r (shapes above) and, for TP_MASK_PADDING, the number
@@ -141,7 +146,8 @@ typedef struct {
                               of LN2's output, du @ W_fc1,r^T (first f exchange input);
                             TP_BWD_ATTN: fp32 [n, h] <- this rank's term of the gradient
                               of LN1's output, dqkv @ W_qkv,r^T (second f exchange input) */
-  void *dx;              /* TP_ALL, TP_BWD_LN1: [n, h] storage dtype */
+  void *dx;              /* TP_ALL, TP_BWD_LN1: [n, h], fp32 or (opts.dx_dtype)
+                            the storage dtype */
   /* fp32 gradients, shapes of the matching parameters. Written by:
    *   TP_BWD_MLP : d_w_fc2, d_b_fc2, d_w_fc1, d_b_fc1
    *   TP_BWD_ATTN: d_ln2_gamma, d_ln2_beta, d_w_o, d_b_o, d_w_qkv, d_b_qkv
@@ -162,7 +168,8 @@ typedef struct {
  * size `hidden`, `heads` attention heads, FFN size `ffn`, sequence length
  * `seq` and micro-batch `micro_batch`.
  *   dtype: TP_DTYPE_F32 or TP_DTYPE_BF16. mask: TP_MASK_CAUSAL/TP_MASK_PADDING.
- *   opts: NULL for the defaults (eps 1e-5, exact-erf GeLU).
+ *   opts: NULL for the defaults (eps 1e-5, exact-erf GeLU, fp32 dx);
+ *     opts->dx_dtype other than TP_DTYPE_F32 or `dtype` is TP_ERR_UNSUPPORTED.
  * Checks: every size > 0; hidden % heads == 0; heads % t == 0; ffn % t == 0;
  * (ffn/t) % 8 == 0; 0 <= rank < t; head dim in {32, 64, 96, 128, 160}
  * (TP_ERR_UNSUPPORTED otherwise). Allocates no device memory. On success

@@ -45,7 +45,7 @@ KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce")
 
 
 class tp_layer_opts(Structure):
-    _fields_ = [("ln_eps", c_float), ("gelu", c_int)]
+    _fields_ = [("ln_eps", c_float), ("gelu", c_int), ("dx_dtype", c_int)]
 
 
 class tp_params(Structure):
@@ -106,7 +106,8 @@ def tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, 
     ws = c_size_t()
     o = None
     if opts is not None:
-        o = ctypes.byref(tp_layer_opts(float(opts.get("ln_eps", 1e-5)), int(opts.get("gelu", 0))))
+        o = ctypes.byref(tp_layer_opts(float(opts.get("ln_eps", 1e-5)), int(opts.get("gelu", 0)),
+                                       int(opts.get("dx_dtype", TP_DTYPE_F32))))
     rc = lib().tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, o,
                                ctypes.byref(h), ctypes.byref(ws))
     return rc, h.value, ws.value

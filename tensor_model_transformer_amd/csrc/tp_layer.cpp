@@ -49,6 +49,7 @@ struct tp_layer {
   int hidden, heads, ffn, seq, batch, t, rank, dtype, mask;
   float eps;
   int gelu_tanh;
+  bool dx_f32;  // dx written in fp32 (else in the storage dtype)
   // derived
   int n, dh, Hl, hl, fl, esz;
   int sdt;   // storage type at the boundary (x, params, out, dx): DT_BF16 or DT_F32
@@ -426,8 +427,10 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
 // da (summed) -> dx (+ dh), LN1 grads.
 int bwd_ln1(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* da, void* ws,
             hipStream_t s) {
+  float* dx32 = L->dx_f32 ? static_cast<float*>(io->dx) : nullptr;
+  void* dxst = L->dx_f32 ? nullptr : io->dx;
   return ln_backward(L, da, L->sdt, io->x, at<float>(ws, L->mean1), at<float>(ws, L->rstd1),
-                     p->ln1_gamma, DT_F32, at<void>(ws, L->dh_f), nullptr, L->sdt, io->dx,
+                     p->ln1_gamma, DT_F32, at<void>(ws, L->dh_f), dx32, L->sdt, dxst,
                      io->d_ln1_gamma, io->d_ln1_beta, nullptr, io->accumulate, ws, s);
 }
 
@@ -469,17 +472,21 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   if (n > (1L << 30) / 4) return TP_ERR_UNSUPPORTED;
   float eps = 1e-5f;
   int gelu = TP_GELU_ERF;
+  int dx_dtype = TP_DTYPE_F32;
   if (opts) {
     eps = opts->ln_eps;
     gelu = opts->gelu;
+    dx_dtype = opts->dx_dtype;
     if (!(eps > 0.f)) return TP_ERR_ARG;
     if (gelu != TP_GELU_ERF && gelu != TP_GELU_TANH) return TP_ERR_UNSUPPORTED;
+    if (dx_dtype != TP_DTYPE_F32 && dx_dtype != dtype) return TP_ERR_UNSUPPORTED;
   }
   tp_layer* L = new (std::nothrow) tp_layer();
   if (!L) return TP_ERR_ARG;
   L->hidden = hidden; L->heads = heads; L->ffn = ffn; L->seq = seq; L->batch = micro_batch;
   L->t = t; L->rank = rank; L->dtype = dtype; L->mask = mask;
   L->eps = eps; L->gelu_tanh = gelu == TP_GELU_TANH;
+  L->dx_f32 = dx_dtype == TP_DTYPE_F32;
   L->n = (int)n; L->dh = dh; L->Hl = heads / t; L->hl = L->Hl * dh; L->fl = ffn / t;
   L->esz = dtype == TP_DTYPE_BF16 ? 2 : 4;
   L->sdt = dtype == TP_DTYPE_BF16 ? DT_BF16 : DT_F32;

@@ -39,7 +39,7 @@ class Shard:
     """One handle of the library plus its workspace."""
 
     def __init__(self, dims: LayerDims, rank: int, device="cuda:0", gelu: int = B.TP_GELU_ERF,
-                 eps: float = 1e-5):
+                 eps: float = 1e-5, dx_fp32: bool = True):
         self.dims = dims
         self.rank = rank
         self.device = torch.device(device)
@@ -48,7 +48,9 @@ class Shard:
             dims.hidden, dims.heads, dims.ffn, dims.seq, dims.batch, dims.t, rank,
             B.TP_DTYPE_BF16 if dims.dtype == "bf16" else B.TP_DTYPE_F32,
             B.TP_MASK_PADDING if dims.mask == "padding" else B.TP_MASK_CAUSAL,
-            {"ln_eps": eps, "gelu": gelu})
+            {"ln_eps": eps, "gelu": gelu,
+             "dx_dtype": B.TP_DTYPE_F32 if dx_fp32 or dims.dtype == "f32" else B.TP_DTYPE_BF16})
+        self.dx_fp32 = dx_fp32
         _check("tp_layer_create", rc)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
 
@@ -77,6 +79,9 @@ class Shard:
     def empty_act(self, fp32=False) -> torch.Tensor:
         return torch.empty(self.dims.tokens, self.dims.hidden,
                            dtype=torch.float32 if fp32 else self.dtype, device=self.device)
+
+    def empty_dx(self) -> torch.Tensor:
+        return self.empty_act(fp32=self.dx_fp32)
 
     def zero_grads(self) -> Dict[str, torch.Tensor]:
         shapes = self.dims.shapes()

@@ -43,7 +43,7 @@ def to_np(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False):
+def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True):
     """TP_ALL forward + backward of one rank on the GPU. Returns numpy dict."""
     import torch
     from tensor_model_transformer_amd.shard import Shard, _check
@@ -52,10 +52,10 @@ def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False):
     r = w.rank if rank is None else rank
     params = rank_params(w, r)
     x, dout, vl = layer_inputs(w)
-    sh = Shard(d, r)
+    sh = Shard(d, r, dx_fp32=dx_fp32)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
-    out, dx = sh.empty_act(), sh.empty_act()
+    out, dx = sh.empty_act(), sh.empty_dx()
     grads = sh.zero_grads()
     _check("tp_layer_fwd", sh.fwd(p, out, x=xd))
     res = {}
@@ -81,6 +81,7 @@ def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False):
         res["dh"] = to_np(sh.tap("dh").view(torch.float32).reshape(d.tokens, d.hidden))
     res["out"] = to_np(out).reshape(d.batch, d.seq, d.hidden)
     res["dx"] = to_np(dx).reshape(d.batch, d.seq, d.hidden)
+    res["dx_dtype"] = str(dx.dtype).replace("torch.", "")
     res["grads"] = {k: to_np(v) for k, v in grads.items()}
     sh.close()
     return res

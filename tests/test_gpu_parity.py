@@ -74,6 +74,18 @@ def test_small_fp32_d160_padding():
     _run(w, taps=True)
 
 
+def test_dx_in_storage_dtype():
+    # opts.dx_dtype = bf16: the residual-stream gradient rounded to bf16 on output
+    _need_gpu()
+    w = SMALL_BF16[3]
+    gpu = run_gpu_local(w, dx_fp32=False)
+    ref = oracle_local(w)
+    ok, rep = compare_local(gpu, ref, TAU["bf16"])
+    print(f"[parity] {w.name} dx bf16: {fmt(rep)}", flush=True)
+    assert ok, fmt(rep)
+    assert gpu["dx_dtype"] == "bfloat16"
+
+
 def test_single_token_sequence():
     # degenerate: seq = 1 (attention is the identity on V), batch 3
     _run(Workload("seq1", LayerDims(3, 1, 128, 4, 256, t=1, dtype="bf16", mask="causal"),
@@ -141,7 +153,7 @@ def run_phased(w):
     exchange_sum(da, parts, stream)
     dxs = []
     for r, s in enumerate(shards):
-        dx = s0.empty_act()
+        dx = s0.empty_dx()
         _check("bwd ln1", s.bwd(params[r], grads[r], x=xd, da=da, dx=dx, phase=B.TP_BWD_LN1))
         dxs.append(dx)
     torch.cuda.synchronize()
