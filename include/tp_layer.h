@@ -89,6 +89,13 @@ enum {
 enum { TP_DTYPE_F32 = 0, TP_DTYPE_BF16 = 1 };
 enum { TP_MASK_CAUSAL = 0, TP_MASK_PADDING = 1 };
 enum { TP_GELU_ERF = 0, TP_GELU_TANH = 1 };
+/* How the 16-bit path forms the attention scores Q K^T (TP_DTYPE_BF16 only):
+ * TP_SCORES_FP16 uses the fp16 Q and K; TP_SCORES_SPLIT also keeps the fp16
+ * rounding residuals Ql, Kl of the QKV projection and sums
+ * Q K^T as Qh Kh^T + Qh Kl^T + Ql Kh^T (about fp32-accurate
+ * scores, three times the score MFMAs); TP_SCORES_AUTO picks SPLIT for
+ * hidden >= 8192. */
+enum { TP_SCORES_AUTO = 0, TP_SCORES_FP16 = 1, TP_SCORES_SPLIT = 2 };
 
 /* Forward phases. TP_ALL runs the whole shard with both g exchanges taken as
  * the identity: the rank's own partial stands in for the sum (exactly the
@@ -105,6 +112,7 @@ typedef struct {
   int gelu;         /* TP_GELU_ERF (default) or TP_GELU_TANH */
   int dx_dtype;     /* dtype of tp_bwd_io.dx: TP_DTYPE_F32 (default, also the
                        value of a zeroed struct) or the layer's storage dtype */
+  int scores;       /* TP_SCORES_AUTO (default), TP_SCORES_FP16 or TP_SCORES_SPLIT */
 } tp_layer_opts;
 
 /* Parameters of rank r (shapes above) and, for TP_MASK_PADDING, the number
@@ -168,8 +176,10 @@ typedef struct {
  * size `hidden`, `heads` attention heads, FFN size `ffn`, sequence length
  * `seq` and micro-batch `micro_batch`.
  *   dtype: TP_DTYPE_F32 or TP_DTYPE_BF16. mask: TP_MASK_CAUSAL/TP_MASK_PADDING.
- *   opts: NULL for the defaults (eps 1e-5, exact-erf GeLU, fp32 dx);
- *     opts->dx_dtype other than TP_DTYPE_F32 or `dtype` is TP_ERR_UNSUPPORTED.
+ *   opts: NULL for the defaults (eps 1e-5, exact-erf GeLU, fp32 dx, automatic
+ *     score precision); opts->dx_dtype other than TP_DTYPE_F32 or `dtype`,
+ *     an unknown opts->scores, or TP_SCORES_SPLIT with TP_DTYPE_F32 are
+ *     TP_ERR_UNSUPPORTED.
  * Checks: every size > 0; hidden % heads == 0; heads % t == 0; ffn % t == 0;
  * (ffn/t) % 8 == 0; 0 <= rank < t; head dim in {32, 64, 96, 128, 160}
  * (TP_ERR_UNSUPPORTED otherwise). Allocates no device memory. On success

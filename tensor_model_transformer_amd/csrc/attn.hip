@@ -119,13 +119,14 @@ struct RowTile {
 // A workgroup owns 128 queries (32 per wave) of one (sequence, head) and
 // sweeps 64-key blocks; K and V tiles are double-buffered in LDS through
 // registers (the next block's loads are in flight during the current MFMAs).
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
-    const f16* __restrict__ qkv, f16* __restrict__ o, float* __restrict__ lse2,
-    const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2) {
-  constexpr int KB = 64, P = D + 8, TILE = KB * P;
+    const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, f16* __restrict__ o,
+    float* __restrict__ lse2, const int* __restrict__ valid_len, int seq, int Hl, int causal,
+    float sl2) {
+  constexpr int KB = 64, P = D + 8, TILE = KB * P, NT = SPLIT ? 3 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* lds = reinterpret_cast<f16*>(smem);  // [2][K tile, V tile]
+  f16* lds = reinterpret_cast<f16*>(smem);  // [2][K tile, V tile (, K residual tile)]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -138,16 +139,23 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
   const f16* Qp = qkv + tok0 * ldq + (size_t)head * 3 * D;
   const f16* Kp = Qp + D;
   const f16* Vp = Qp + 2 * D;
+  const f16* Qlp = SPLIT ? qkv_lo + tok0 * ldq + (size_t)head * 3 * D : nullptr;
+  const f16* Klp = SPLIT ? Qlp + D : nullptr;
   const int L = causal ? seq : min(max(valid_len[b], 0), seq);
   const int kv_end = causal ? min(seq, qb * 128 + 128) : L;
   const int lim = causal ? min(q + 1, seq) : L;  // this lane's keys are [0, lim)
 
-  f16x8 qf[D / 16];
+  f16x8 qf[D / 16], ql[SPLIT ? D / 16 : 1];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     uint4 v = make_uint4(0, 0, 0, 0);
     if (q < seq) v = *reinterpret_cast<const uint4*>(Qp + (size_t)q * ldq + 16 * ks + 8 * hh);
     qf[ks] = __builtin_bit_cast(f16x8, v);
+    if constexpr (SPLIT) {
+      uint4 r = make_uint4(0, 0, 0, 0);
+      if (q < seq) r = *reinterpret_cast<const uint4*>(Qlp + (size_t)q * ldq + 16 * ks + 8 * hh);
+      ql[ks] = __builtin_bit_cast(f16x8, r);
+    }
   }
   f32x16 O[D / 32];
 #pragma unroll
@@ -156,13 +164,15 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
     for (int e = 0; e < 16; ++e) O[t][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  RowTile<KB, D, 256> kt, vt;
+  RowTile<KB, D, 256> kt, vt, klt;
   const int nblk = (kv_end + KB - 1) / KB;
   if (nblk > 0) {
     kt.load(Kp, ldq, 0, seq, tid);
     vt.load(Vp, ldq, 0, seq, tid);
+    if constexpr (SPLIT) klt.load(Klp, ldq, 0, seq, tid);
     kt.store(lds, P, tid);
     vt.store(lds + TILE, P, tid);
+    if constexpr (SPLIT) klt.store(lds + 2 * TILE, P, tid);
   }
   __syncthreads();
   for (int ib = 0; ib < nblk; ++ib) {
@@ -171,9 +181,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
     if (more) {
       kt.load(Kp, ldq, kb0 + KB, seq, tid);
       vt.load(Vp, ldq, kb0 + KB, seq, tid);
+      if constexpr (SPLIT) klt.load(Klp, ldq, kb0 + KB, seq, tid);
     }
-    const f16* Ks = lds + (ib & 1) * 2 * TILE;
+    const f16* Ks = lds + (ib & 1) * NT * TILE;
     const f16* Vs = Ks + TILE;
+    const f16* Kls = Ks + 2 * TILE;  // residual tile (SPLIT only)
     if (!(causal && kb0 > qw0 + 31)) {  // some key of this block precedes a query of this wave
       f32x16 S[2];
 #pragma unroll
@@ -181,8 +193,15 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) S[st][e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          S[st] = mfma32(ld8(Ks + (32 * st + l32) * P + 16 * ks + 8 * hh), qf[ks], S[st]);
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int off = (32 * st + l32) * P + 16 * ks + 8 * hh;
+          const f16x8 kh = ld8(Ks + off);
+          S[st] = mfma32(kh, qf[ks], S[st]);
+          if constexpr (SPLIT) {
+            S[st] = mfma32(ld8(Kls + off), qf[ks], S[st]);
+            S[st] = mfma32(kh, ql[ks], S[st]);
+          }
+        }
       }
       // S[st][4*jj+ii]: key kb0 + 32*st + 8*jj + 4*hh + ii, query q
       float mx = -INFINITY;
@@ -226,9 +245,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
       }
     }
     if (more) {
-      f16* nxt = lds + ((ib + 1) & 1) * 2 * TILE;
+      f16* nxt = lds + ((ib + 1) & 1) * NT * TILE;
       kt.store(nxt, P, tid);
       vt.store(nxt + TILE, P, tid);
+      if constexpr (SPLIT) klt.store(nxt + 2 * TILE, P, tid);
     }
     __syncthreads();
   }
@@ -280,15 +300,15 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 // Sweeps 64-query blocks (two 32-query halves per MFMA step); Q and dO tiles
 // are double-buffered in LDS through registers. Q^T and dO^T operands are
 // read from the row-major tiles with transposing LDS reads.
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
-    const f16* __restrict__ qkv, const f16* __restrict__ dO, const float* __restrict__ lse2,
-    const float* __restrict__ delta, f16* __restrict__ dqkv, const int* __restrict__ valid_len,
-    int seq, int Hl, int causal, float sl2, float scale) {
-  constexpr int QB = 64, P = D + 8, TILE = QB * P;
+    const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
+    const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
+    const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale) {
+  constexpr int QB = 64, P = D + 8, TILE = QB * P, NT = SPLIT ? 3 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* lds = reinterpret_cast<f16*>(smem);                          // [2][Q, dO]
-  float* ls = reinterpret_cast<float*>(lds + 4 * TILE);             // [2][QB]
+  f16* lds = reinterpret_cast<f16*>(smem);                          // [2][Q, dO (, Q residual)]
+  float* ls = reinterpret_cast<float*>(lds + 2 * NT * TILE);        // [2][QB]
   float* dl = ls + 2 * QB;                                          // [2][QB]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -302,11 +322,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
   const f16* Kp = Qp + D;
   const f16* Vp = Qp + 2 * D;
   const f16* dOp = dO + tok0 * ldo + (size_t)head * D;
+  const f16* Qlp = SPLIT ? qkv_lo + tok0 * ldq + (size_t)head * 3 * D : nullptr;
   const float* lsp = lse2 + ((size_t)b * Hl + head) * seq;
   const float* dlp = delta + ((size_t)b * Hl + head) * seq;
   const int L = causal ? seq : min(max(valid_len[b], 0), seq);
 
-  f16x8 kf[D / 16], vf[D / 16];
+  f16x8 kf[D / 16], vf[D / 16], kl[SPLIT ? D / 16 : 1];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
@@ -316,6 +337,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
     }
     kf[ks] = __builtin_bit_cast(f16x8, kv);
     vf[ks] = __builtin_bit_cast(f16x8, vv);
+    if constexpr (SPLIT) {
+      uint4 r = make_uint4(0, 0, 0, 0);
+      if (key < seq)
+        r = *reinterpret_cast<const uint4*>(Qlp + D + (size_t)key * ldq + 16 * ks + 8 * hh);
+      kl[ks] = __builtin_bit_cast(f16x8, r);
+    }
   }
   f32x16 dK[D / 32], dV[D / 32];
 #pragma unroll
@@ -326,11 +353,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
   const bool wave_keys_valid = kw0 < (causal ? seq : L);
   const int q_begin = causal ? kblk * 128 : 0;
   const int nblk = (seq - q_begin + QB - 1) / QB;
-  RowTile<QB, D, 256> qt, gt;
+  RowTile<QB, D, 256> qt, gt, qlt;
   float lsr = 0.f, dlr = 0.f;
   auto fetch = [&](int q0) {
     qt.load(Qp, ldq, q0, seq, tid);
     gt.load(dOp, ldo, q0, seq, tid);
+    if constexpr (SPLIT) qlt.load(Qlp, ldq, q0, seq, tid);
     if (tid < QB) {
       const int qq = q0 + tid;
       lsr = qq < seq ? lsp[qq] : 0.f;
@@ -338,9 +366,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
     }
   };
   auto put = [&](int buf) {
-    f16* base = lds + buf * 2 * TILE;
+    f16* base = lds + buf * NT * TILE;
     qt.store(base, P, tid);
     gt.store(base + TILE, P, tid);
+    if constexpr (SPLIT) qlt.store(base + 2 * TILE, P, tid);
     if (tid < QB) {
       ls[buf * QB + tid] = lsr;
       dl[buf * QB + tid] = dlr;
@@ -355,8 +384,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
     const int q0 = q_begin + ib * QB;
     const bool more = ib + 1 < nblk;
     if (more) fetch(q0 + QB);
-    const f16* Qs = lds + (ib & 1) * 2 * TILE;
+    const f16* Qs = lds + (ib & 1) * NT * TILE;
     const f16* Gs = Qs + TILE;
+    const f16* Qls = Qs + 2 * TILE;  // residual tile (SPLIT only)
     const float* lsb = ls + (ib & 1) * QB;
     const float* dlb = dl + (ib & 1) * QB;
 #pragma unroll
@@ -368,8 +398,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
       for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        S = mfma32(ld8(Qs + (32 * qs + l32) * P + 16 * ks + 8 * hh), kf[ks], S);
-        dP = mfma32(ld8(Gs + (32 * qs + l32) * P + 16 * ks + 8 * hh), vf[ks], dP);
+        const int off = (32 * qs + l32) * P + 16 * ks + 8 * hh;
+        const f16x8 qh = ld8(Qs + off);
+        S = mfma32(qh, kf[ks], S);
+        if constexpr (SPLIT) {
+          S = mfma32(ld8(Qls + off), kf[ks], S);
+          S = mfma32(qh, kl[ks], S);
+        }
+        dP = mfma32(ld8(Gs + off), vf[ks], dP);
       }
       // element e: query qh0 + 8*(e>>2) + 4*hh + (e&3), key = this lane's key
       float Pv[16], dS[16];
@@ -420,14 +456,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
 // ============================================================================
 // fp16 backward: dQ (a workgroup owns 128 queries, 32 per wave)
 // ============================================================================
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
-    const f16* __restrict__ qkv, const f16* __restrict__ dO, const float* __restrict__ lse2,
-    const float* __restrict__ delta, f16* __restrict__ dqkv, const int* __restrict__ valid_len,
-    int seq, int Hl, int causal, float sl2, float scale) {
-  constexpr int KB = 64, P = D + 8, TILE = KB * P;
+    const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
+    const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
+    const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale) {
+  constexpr int KB = 64, P = D + 8, TILE = KB * P, NT = SPLIT ? 3 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* lds = reinterpret_cast<f16*>(smem);  // [2][K tile, V tile]
+  f16* lds = reinterpret_cast<f16*>(smem);  // [2][K tile, V tile (, K residual tile)]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -447,8 +483,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
   const bool qok = q < seq;
   const float lq = qok ? lse2[((size_t)b * Hl + head) * seq + q] : 0.f;
   const float dq_ = qok ? delta[((size_t)b * Hl + head) * seq + q] : 0.f;
+  const f16* Qlp = SPLIT ? qkv_lo + tok0 * ldq + (size_t)head * 3 * D : nullptr;
+  const f16* Klp = SPLIT ? Qlp + D : nullptr;
 
-  f16x8 qf[D / 16], gf[D / 16];
+  f16x8 qf[D / 16], gf[D / 16], ql[SPLIT ? D / 16 : 1];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
@@ -458,6 +496,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
     }
     qf[ks] = __builtin_bit_cast(f16x8, a);
     gf[ks] = __builtin_bit_cast(f16x8, c);
+    if constexpr (SPLIT) {
+      uint4 r = make_uint4(0, 0, 0, 0);
+      if (qok) r = *reinterpret_cast<const uint4*>(Qlp + (size_t)q * ldq + 16 * ks + 8 * hh);
+      ql[ks] = __builtin_bit_cast(f16x8, r);
+    }
   }
   f32x16 dQ[D / 32];
 #pragma unroll
@@ -465,13 +508,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dQ[t][e] = 0.f;
 
-  RowTile<KB, D, 256> kt, vt;
+  RowTile<KB, D, 256> kt, vt, klt;
   const int nblk = (kv_end + KB - 1) / KB;
   if (nblk > 0) {
     kt.load(Kp, ldq, 0, seq, tid);
     vt.load(Vp, ldq, 0, seq, tid);
+    if constexpr (SPLIT) klt.load(Klp, ldq, 0, seq, tid);
     kt.store(lds, P, tid);
     vt.store(lds + TILE, P, tid);
+    if constexpr (SPLIT) klt.store(lds + 2 * TILE, P, tid);
   }
   __syncthreads();
   for (int ib = 0; ib < nblk; ++ib) {
@@ -480,9 +525,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
     if (more) {
       kt.load(Kp, ldq, kb0 + KB, seq, tid);
       vt.load(Vp, ldq, kb0 + KB, seq, tid);
+      if constexpr (SPLIT) klt.load(Klp, ldq, kb0 + KB, seq, tid);
     }
-    const f16* Ks = lds + (ib & 1) * 2 * TILE;
+    const f16* Ks = lds + (ib & 1) * NT * TILE;
     const f16* Vs = Ks + TILE;
+    const f16* Kls = Ks + 2 * TILE;  // residual tile (SPLIT only)
     if (!(causal && kb0 > qw0 + 31)) {
       float dS[2][16];
 #pragma unroll
@@ -492,8 +539,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
         for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          S = mfma32(ld8(Ks + (32 * st + l32) * P + 16 * ks + 8 * hh), qf[ks], S);
-          dP = mfma32(ld8(Vs + (32 * st + l32) * P + 16 * ks + 8 * hh), gf[ks], dP);
+          const int off = (32 * st + l32) * P + 16 * ks + 8 * hh;
+          const f16x8 kh = ld8(Ks + off);
+          S = mfma32(kh, qf[ks], S);
+          if constexpr (SPLIT) {
+            S = mfma32(ld8(Kls + off), qf[ks], S);
+            S = mfma32(kh, ql[ks], S);
+          }
+          dP = mfma32(ld8(Vs + off), gf[ks], dP);
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -512,9 +565,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
       }
     }
     if (more) {
-      f16* nxt = lds + ((ib + 1) & 1) * 2 * TILE;
+      f16* nxt = lds + ((ib + 1) & 1) * NT * TILE;
       kt.store(nxt, P, tid);
       vt.store(nxt + TILE, P, tid);
+      if constexpr (SPLIT) klt.store(nxt + 2 * TILE, P, tid);
     }
     __syncthreads();
   }
@@ -673,12 +727,13 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(
 // ============================================================================
 // Host launchers
 // ============================================================================
-template <int D>
-static size_t fwd_lds() { return (size_t)4 * 64 * (D + 8) * 2; }
-template <int D>
-static size_t dkdv_lds() { return (size_t)4 * 64 * (D + 8) * 2 + 4 * 64 * 4; }
-template <int D>
-static size_t dq_lds() { return (size_t)4 * 64 * (D + 8) * 2; }
+// Two buffers of two 64-row tiles (three with the score residuals).
+template <int D, bool SPLIT>
+static size_t fwd_lds() { return (size_t)(SPLIT ? 6 : 4) * 64 * (D + 8) * 2; }
+template <int D, bool SPLIT>
+static size_t dkdv_lds() { return (size_t)(SPLIT ? 6 : 4) * 64 * (D + 8) * 2 + 4 * 64 * 4; }
+template <int D, bool SPLIT>
+static size_t dq_lds() { return (size_t)(SPLIT ? 6 : 4) * 64 * (D + 8) * 2; }
 
 template <typename K>
 static hipError_t set_lds(K kern, size_t bytes) {
@@ -687,16 +742,49 @@ static hipError_t set_lds(K kern, size_t bytes) {
                              (int)bytes);
 }
 
+template <int D, bool SPLIT>
+static hipError_t fwd_f16(const void* qkv, const void* qkv_lo, void* o, float* lse2,
+                          const int* vl, int batch, int seq, int Hl, int causal, float sl2,
+                          hipStream_t s) {
+  auto k = attn_fwd_f16_kernel<D, SPLIT>;
+  const size_t lds = fwd_lds<D, SPLIT>();
+  hipError_t e = set_lds(k, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid((seq + 127) / 128, Hl, batch);
+  hipLaunchKernelGGL(k, grid, dim3(256), lds, s, (const f16*)qkv,
+                     (const f16*)qkv_lo, (f16*)o, lse2, vl, seq, Hl, causal, sl2);
+  return hipGetLastError();
+}
+
+template <int D, bool SPLIT>
+static hipError_t bwd_f16(const void* qkv, const void* qkv_lo, const void* dO, const float* lse2,
+                          const float* delta, void* dqkv, const int* vl, int batch, int seq,
+                          int Hl, int causal, float sl2, float scale, hipStream_t s) {
+  auto k1 = attn_bwd_dkdv_f16_kernel<D, SPLIT>;
+  auto k2 = attn_bwd_dq_f16_kernel<D, SPLIT>;
+  const size_t lds1 = dkdv_lds<D, SPLIT>(), lds2 = dq_lds<D, SPLIT>();
+  hipError_t e = set_lds(k1, lds1);
+  if (e == hipSuccess) e = set_lds(k2, lds2);
+  if (e != hipSuccess) return e;
+  dim3 grid((seq + 127) / 128, Hl, batch);
+  hipLaunchKernelGGL(k1, grid, dim3(256), lds1, s, (const f16*)qkv,
+                     (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, seq, Hl,
+                     causal, sl2, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k2, grid, dim3(256), lds2, s, (const f16*)qkv,
+                     (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, seq, Hl,
+                     causal, sl2, scale);
+  return hipGetLastError();
+}
+
 template <int D>
-static hipError_t fwd_d(int dtype, const void* qkv, void* o, float* lse2, const int* vl,
-                        int batch, int seq, int Hl, int causal, float sl2, hipStream_t s) {
+static hipError_t fwd_d(int dtype, const void* qkv, const void* qkv_lo, void* o, float* lse2,
+                        const int* vl, int batch, int seq, int Hl, int causal, float sl2,
+                        hipStream_t s) {
   if (dtype == DT_F16) {
-    auto k = attn_fwd_f16_kernel<D>;
-    hipError_t e = set_lds(k, fwd_lds<D>());
-    if (e != hipSuccess) return e;
-    dim3 grid((seq + 127) / 128, Hl, batch);
-    hipLaunchKernelGGL(k, grid, dim3(256), fwd_lds<D>(), s, (const f16*)qkv, (f16*)o, lse2, vl,
-                       seq, Hl, causal, sl2);
+    if (qkv_lo) return fwd_f16<D, true>(qkv, qkv_lo, o, lse2, vl, batch, seq, Hl, causal, sl2, s);
+    return fwd_f16<D, false>(qkv, nullptr, o, lse2, vl, batch, seq, Hl, causal, sl2, s);
   } else {
     const long n = (long)batch * Hl * seq;
     attn_fwd_f32_kernel<D><<<(unsigned)((n + 63) / 64), 64, 0, s>>>(
@@ -706,22 +794,16 @@ static hipError_t fwd_d(int dtype, const void* qkv, void* o, float* lse2, const 
 }
 
 template <int D>
-static hipError_t bwd_d(int dtype, const void* qkv, const void* dO, const float* lse2,
-                        const float* delta, void* dqkv, const int* vl, int batch, int seq, int Hl,
-                        int causal, float sl2, float scale, hipStream_t s) {
+static hipError_t bwd_d(int dtype, const void* qkv, const void* qkv_lo, const void* dO,
+                        const float* lse2, const float* delta, void* dqkv, const int* vl,
+                        int batch, int seq, int Hl, int causal, float sl2, float scale,
+                        hipStream_t s) {
   if (dtype == DT_F16) {
-    auto k1 = attn_bwd_dkdv_f16_kernel<D>;
-    auto k2 = attn_bwd_dq_f16_kernel<D>;
-    hipError_t e = set_lds(k1, dkdv_lds<D>());
-    if (e == hipSuccess) e = set_lds(k2, dq_lds<D>());
-    if (e != hipSuccess) return e;
-    dim3 grid((seq + 127) / 128, Hl, batch);
-    hipLaunchKernelGGL(k1, grid, dim3(256), dkdv_lds<D>(), s, (const f16*)qkv, (const f16*)dO,
-                       lse2, delta, (f16*)dqkv, vl, seq, Hl, causal, sl2, scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k2, grid, dim3(256), dq_lds<D>(), s, (const f16*)qkv, (const f16*)dO,
-                       lse2, delta, (f16*)dqkv, vl, seq, Hl, causal, sl2, scale);
+    if (qkv_lo)
+      return bwd_f16<D, true>(qkv, qkv_lo, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal,
+                              sl2, scale, s);
+    return bwd_f16<D, false>(qkv, nullptr, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal,
+                             sl2, scale, s);
   } else {
     const long n = (long)batch * Hl * seq;
     const unsigned g = (unsigned)((n + 63) / 64);
@@ -737,25 +819,28 @@ static hipError_t bwd_d(int dtype, const void* qkv, const void* dO, const float*
   return hipGetLastError();
 }
 
-hipError_t attn_fwd(int dtype, const void* qkv, void* o, float* lse2, const int* valid_len,
-                    int batch, int seq, int Hl, int D, int mask, hipStream_t s) {
+hipError_t attn_fwd(int dtype, const void* qkv, const void* qkv_lo, void* o, float* lse2,
+                    const int* valid_len, int batch, int seq, int Hl, int D, int mask,
+                    hipStream_t s) {
   if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
+  if (qkv_lo && dtype != DT_F16) return hipErrorInvalidValue;
   const int causal = mask == 0;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
   switch (D) {
-    case 32: return fwd_d<32>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
-    case 64: return fwd_d<64>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
-    case 96: return fwd_d<96>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
-    case 128: return fwd_d<128>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
-    case 160: return fwd_d<160>(dtype, qkv, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 32: return fwd_d<32>(dtype, qkv, qkv_lo, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 64: return fwd_d<64>(dtype, qkv, qkv_lo, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 96: return fwd_d<96>(dtype, qkv, qkv_lo, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 128: return fwd_d<128>(dtype, qkv, qkv_lo, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
+    case 160: return fwd_d<160>(dtype, qkv, qkv_lo, o, lse2, valid_len, batch, seq, Hl, causal, sl2, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, const float* lse2,
-                    float* delta, void* dqkv, const int* valid_len, int batch, int seq, int Hl,
-                    int D, int mask, hipStream_t s) {
+hipError_t attn_bwd(int dtype, const void* qkv, const void* qkv_lo, const void* o, const void* dO,
+                    const float* lse2, float* delta, void* dqkv, const int* valid_len, int batch,
+                    int seq, int Hl, int D, int mask, hipStream_t s) {
   if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
+  if (qkv_lo && dtype != DT_F16) return hipErrorInvalidValue;
   const long ntasks = (long)batch * seq * Hl;
   if (dtype == DT_F16)
     attn_delta_kernel<f16><<<(unsigned)((ntasks + 255) / 256), 256, 0, s>>>(
@@ -769,11 +854,11 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO, c
   const double sc = 1.0 / sqrt((double)D);
   const float sl2 = (float)(1.4426950408889634 * sc), scale = (float)sc;
   switch (D) {
-    case 32: return bwd_d<32>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
-    case 64: return bwd_d<64>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
-    case 96: return bwd_d<96>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
-    case 128: return bwd_d<128>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
-    case 160: return bwd_d<160>(dtype, qkv, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 32: return bwd_d<32>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 64: return bwd_d<64>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 96: return bwd_d<96>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 128: return bwd_d<128>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 160: return bwd_d<160>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
     default: return hipErrorInvalidValue;
   }
 }

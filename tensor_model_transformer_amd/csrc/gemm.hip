@@ -54,6 +54,17 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float
     load4_dt(g.aux, g.aux_dtype, (size_t)m * g.ldaux + n, u);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e], g.gelu_tanh);
+  } else if (g.epi == EPI_SPLIT16) {
+    // hi = fp16(v) goes to C below (exactly representable, so stored as is);
+    // lo = v - hi is exact in fp32 and rounded once more to fp16 in C2.
+    float lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float hi = (float)(f16)v[e];
+      lo[e] = v[e] - hi;
+      v[e] = hi;
+    }
+    store4_dt(g.C2, DT_F16, (size_t)m * g.ldc2 + n, lo);
   }
   const size_t off = (size_t)m * g.ldc + n;
   if (g.accumulate && g.c_dtype == DT_F32) {

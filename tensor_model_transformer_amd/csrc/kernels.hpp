@@ -56,7 +56,7 @@ hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts,
 // ---------------------------------------------------------------------------
 // GEMM (gemm.hip): C[M,N] = A[M,K] @ B[K,N] with a fused epilogue.
 // ---------------------------------------------------------------------------
-enum { EPI_STORE = 0, EPI_BIAS_GELU = 1, EPI_DGELU = 2 };
+enum { EPI_STORE = 0, EPI_BIAS_GELU = 1, EPI_DGELU = 2, EPI_SPLIT16 = 3 };
 
 struct GemmArgs {
   // Arithmetic: DT_F32 (fp32 FMA) or DT_F16 (fp16 MFMA, fp32 accumulate;
@@ -69,6 +69,8 @@ struct GemmArgs {
   const void* B; long ldb; int b_kmajor; int b_dtype;
   // epilogue, per element: v = acc (+ bias[n]) (+ resid[m,n]);
   //   EPI_BIAS_GELU: C = v, C2 = GeLU(v);  EPI_DGELU: C = v * GeLU'(aux[m,n]);
+  //   EPI_SPLIT16: C = fp16(v), C2 = fp16(v - fp16(v)) (both fp16; v = C + C2
+  //   to about 2^-22 relative);
   //   accumulate: C (fp32) += v.
   int epi;
   const void* bias; int bias_dtype;    // [N]
@@ -90,12 +92,14 @@ int gemm_choose_split(const GemmArgs& g);
 // o, dO: [batch*seq, Hl*D]; lse2, delta: [batch, Hl, seq] fp32.
 // dtype: DT_F32 (fp32 kernels) or DT_F16 (fp16 operands, MFMA, fp32 accumulate).
 // mask: 0 causal, 1 padding (valid_len[batch] keys).
+// qkv_lo (DT_F16 only, may be null): the fp16 rounding residuals of qkv, same
+// layout; when given, the scores use Q K^T ~ Qh Kh^T + Qh Kl^T + Ql Kh^T.
 // ---------------------------------------------------------------------------
-hipError_t attn_fwd(int dtype, const void* qkv, void* o, float* lse2,
+hipError_t attn_fwd(int dtype, const void* qkv, const void* qkv_lo, void* o, float* lse2,
                     const int* valid_len, int batch, int seq, int Hl, int D,
                     int mask, hipStream_t s);
-hipError_t attn_bwd(int dtype, const void* qkv, const void* o, const void* dO,
-                    const float* lse2, float* delta, void* dqkv,
+hipError_t attn_bwd(int dtype, const void* qkv, const void* qkv_lo, const void* o,
+                    const void* dO, const float* lse2, float* delta, void* dqkv,
                     const int* valid_len, int batch, int seq, int Hl, int D,
                     int mask, hipStream_t s);
 

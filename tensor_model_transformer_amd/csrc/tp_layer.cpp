@@ -23,6 +23,13 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
+// TP_SCORES_AUTO keeps the fp16 residuals of Q and K from this hidden size
+// on. With N(0, 0.02) weights the scores' spread grows like hidden * 0.02^2,
+// and at hidden 25600 (spread about 10) the fp16 rounding of Q and K alone
+// moves softmax outputs by several tenths of a percent, visible in the
+// gradient of W_qkv; at hidden <= 3072 the spread is about 1.
+constexpr int kSplitScoresHidden = 8192;
+
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Region {
@@ -50,12 +57,13 @@ struct tp_layer {
   float eps;
   int gelu_tanh;
   bool dx_f32;  // dx written in fp32 (else in the storage dtype)
+  bool split_scores;  // qkv also kept as fp16 residuals; scores from three products
   // derived
   int n, dh, Hl, hl, fl, esz;
   int sdt;   // storage type at the boundary (x, params, out, dx): DT_BF16 or DT_F32
   int adt;   // internal activations and their gradients: DT_F16 or DT_F32
   // workspace regions
-  Region mean1, rstd1, a, qkv, o, lse2, h_mid, mean2, rstd2, c, u, z;
+  Region mean1, rstd1, a, qkv, qkv_lo, o, lse2, h_mid, mean2, rstd2, c, u, z;
   Region du, dc, dh_f, dh_s, dO, delta, dqkv, da, part, splitk;
   size_t ws_bytes;
   int split_w2, split_w1, split_wo, split_wqkv;
@@ -109,6 +117,7 @@ void plan(tp_layer* L) {
   take(L->rstd1, n * 4);
   take(L->a, n * h * e);
   take(L->qkv, n * 3 * L->hl * e);
+  take(L->qkv_lo, L->split_scores ? n * 3 * L->hl * 2 : 0);
   take(L->o, n * L->hl * e);
   take(L->lse2, stats);
   take(L->h_mid, n * h * 4);
@@ -159,6 +168,9 @@ template <typename T>
 T* at(void* ws, const Region& r) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + r.off);
 }
+
+// The fp16 residuals of qkv, or null when scores use qkv alone.
+void* qkv_lo(tp_layer* L, void* ws) { return L->split_scores ? at<void>(ws, L->qkv_lo) : nullptr; }
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -259,12 +271,17 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   g.B = p->w_qkv; g.ldb = 3 * hl; g.b_kmajor = 0; g.b_dtype = L->sdt;
   g.bias = p->b_qkv;
   g.C = at<void>(ws, L->qkv); g.ldc = 3 * hl;
+  if (L->split_scores) {
+    g.epi = EPI_SPLIT16;
+    g.C2 = qkv_lo(L, ws); g.ldc2 = 3 * hl; g.c2_dtype = DT_F16;
+  }
   if ((e = run_gemm(L, g, s))) return e;
   {
   Scope ps(L, s, TP_K_ATTN_FWD, 4.0 * L->dh * L->Hl * L->attn_pairs,
            (double)n * 4 * hl * L->esz + 4.0 * n * L->Hl);
-  HIP_TRY(attn_fwd(L->adt, at<void>(ws, L->qkv), at<void>(ws, L->o), at<float>(ws, L->lse2),
-                   p->valid_len, L->batch, L->seq, L->Hl, L->dh, L->mask, s));
+  HIP_TRY(attn_fwd(L->adt, at<void>(ws, L->qkv), qkv_lo(L, ws), at<void>(ws, L->o),
+                   at<float>(ws, L->lse2), p->valid_len, L->batch, L->seq, L->Hl, L->dh, L->mask,
+                   s));
   }
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = hl;
@@ -405,7 +422,8 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
   {
     Scope ps(L, s, TP_K_ATTN_BWD, 8.0 * L->dh * L->Hl * L->attn_pairs,
              (double)n * 8 * hl * L->esz + 8.0 * n * L->Hl);
-    HIP_TRY(attn_bwd(L->adt, at<void>(ws, L->qkv), at<void>(ws, L->o), at<void>(ws, L->dO),
+    HIP_TRY(attn_bwd(L->adt, at<void>(ws, L->qkv), qkv_lo(L, ws), at<void>(ws, L->o),
+                     at<void>(ws, L->dO),
                      at<float>(ws, L->lse2), at<float>(ws, L->delta), at<void>(ws, L->dqkv),
                      p->valid_len, L->batch, L->seq, L->Hl, L->dh, L->mask, s));
   }
@@ -473,13 +491,18 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   float eps = 1e-5f;
   int gelu = TP_GELU_ERF;
   int dx_dtype = TP_DTYPE_F32;
+  int scores = TP_SCORES_AUTO;
   if (opts) {
     eps = opts->ln_eps;
     gelu = opts->gelu;
     dx_dtype = opts->dx_dtype;
+    scores = opts->scores;
     if (!(eps > 0.f)) return TP_ERR_ARG;
     if (gelu != TP_GELU_ERF && gelu != TP_GELU_TANH) return TP_ERR_UNSUPPORTED;
     if (dx_dtype != TP_DTYPE_F32 && dx_dtype != dtype) return TP_ERR_UNSUPPORTED;
+    if (scores != TP_SCORES_AUTO && scores != TP_SCORES_FP16 && scores != TP_SCORES_SPLIT)
+      return TP_ERR_UNSUPPORTED;
+    if (scores == TP_SCORES_SPLIT && dtype != TP_DTYPE_BF16) return TP_ERR_UNSUPPORTED;
   }
   tp_layer* L = new (std::nothrow) tp_layer();
   if (!L) return TP_ERR_ARG;
@@ -487,6 +510,9 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   L->t = t; L->rank = rank; L->dtype = dtype; L->mask = mask;
   L->eps = eps; L->gelu_tanh = gelu == TP_GELU_TANH;
   L->dx_f32 = dx_dtype == TP_DTYPE_F32;
+  L->split_scores = dtype == TP_DTYPE_BF16 &&
+                    (scores == TP_SCORES_SPLIT ||
+                     (scores == TP_SCORES_AUTO && hidden >= kSplitScoresHidden));
   L->n = (int)n; L->dh = dh; L->Hl = heads / t; L->hl = L->Hl * dh; L->fl = ffn / t;
   L->esz = dtype == TP_DTYPE_BF16 ? 2 : 4;
   L->sdt = dtype == TP_DTYPE_BF16 ? DT_BF16 : DT_F32;

@@ -39,7 +39,7 @@ class Shard:
     """One handle of the library plus its workspace."""
 
     def __init__(self, dims: LayerDims, rank: int, device="cuda:0", gelu: int = B.TP_GELU_ERF,
-                 eps: float = 1e-5, dx_fp32: bool = True):
+                 eps: float = 1e-5, dx_fp32: bool = True, scores: int = B.TP_SCORES_AUTO):
         self.dims = dims
         self.rank = rank
         self.device = torch.device(device)
@@ -49,7 +49,8 @@ class Shard:
             B.TP_DTYPE_BF16 if dims.dtype == "bf16" else B.TP_DTYPE_F32,
             B.TP_MASK_PADDING if dims.mask == "padding" else B.TP_MASK_CAUSAL,
             {"ln_eps": eps, "gelu": gelu,
-             "dx_dtype": B.TP_DTYPE_F32 if dx_fp32 or dims.dtype == "f32" else B.TP_DTYPE_BF16})
+             "dx_dtype": B.TP_DTYPE_F32 if dx_fp32 or dims.dtype == "f32" else B.TP_DTYPE_BF16,
+             "scores": scores})
         self.dx_fp32 = dx_fp32
         _check("tp_layer_create", rc)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)

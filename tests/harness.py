@@ -43,7 +43,7 @@ def to_np(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True):
+def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True, scores=0):
     """TP_ALL forward + backward of one rank on the GPU. Returns numpy dict."""
     import torch
     from tensor_model_transformer_amd.shard import Shard, _check
@@ -52,7 +52,7 @@ def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True
     r = w.rank if rank is None else rank
     params = rank_params(w, r)
     x, dout, vl = layer_inputs(w)
-    sh = Shard(d, r, dx_fp32=dx_fp32)
+    sh = Shard(d, r, dx_fp32=dx_fp32, scores=scores)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()

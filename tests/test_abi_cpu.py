@@ -70,6 +70,10 @@ def create(**kw):
     (dict(mask=3), B.TP_ERR_UNSUPPORTED),
     (dict(opts={"ln_eps": 1e-5, "gelu": 5}), B.TP_ERR_UNSUPPORTED),
     (dict(opts={"ln_eps": 0.0, "gelu": 0}), B.TP_ERR_ARG),
+    (dict(opts={"dx_dtype": 7}), B.TP_ERR_UNSUPPORTED),
+    (dict(dtype=B.TP_DTYPE_F32, opts={"dx_dtype": B.TP_DTYPE_BF16}), B.TP_ERR_UNSUPPORTED),
+    (dict(opts={"scores": 3}), B.TP_ERR_UNSUPPORTED),
+    (dict(dtype=B.TP_DTYPE_F32, opts={"scores": B.TP_SCORES_SPLIT}), B.TP_ERR_UNSUPPORTED),
 ])
 def test_create_validation(lib, kw, code):
     rc, h, ws = create(**kw)
@@ -93,6 +97,26 @@ def test_create_ok_and_workspace_plan(lib):
     assert B.tp_layer_tap(h, 99)[0] == B.TP_ERR_ARG
     assert B.tp_layer_destroy(h) == B.TP_OK
     assert B.tp_layer_destroy(None) == B.TP_OK
+
+
+def test_split_scores_workspace(lib):
+    # the score residuals take one more fp16 [n, 3*h_l] region; AUTO keeps
+    # them only from hidden 8192 on
+    n, hl = 2 * 64, 64
+    sizes = {}
+    for mode in (B.TP_SCORES_AUTO, B.TP_SCORES_FP16, B.TP_SCORES_SPLIT):
+        rc, h, ws = create(opts={"scores": mode})
+        assert rc == B.TP_OK
+        sizes[mode] = ws
+        B.tp_layer_destroy(h)
+    assert sizes[B.TP_SCORES_AUTO] == sizes[B.TP_SCORES_FP16]
+    assert sizes[B.TP_SCORES_SPLIT] - sizes[B.TP_SCORES_FP16] >= n * 3 * hl * 2
+    big = dict(hidden=8192, heads=64, ffn=512, seq=8, micro_batch=1, t=8)
+    rc, h, ws_auto = create(**big)
+    B.tp_layer_destroy(h)
+    rc, h, ws_fp16 = create(opts={"scores": B.TP_SCORES_FP16}, **big)
+    B.tp_layer_destroy(h)
+    assert ws_auto - ws_fp16 >= 8 * 3 * 1024 * 2
 
 
 def test_call_argument_errors_need_no_device(lib):

@@ -21,10 +21,11 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _run(w, rank=None, taps=False):
+def _run(w, rank=None, taps=False, scores=0):
     _need_gpu()
-    print(f"\n[parity] {w.name} dims={w.dims} rank={w.rank if rank is None else rank}", flush=True)
-    gpu = run_gpu_local(w, rank, taps=taps)
+    print(f"\n[parity] {w.name} dims={w.dims} rank={w.rank if rank is None else rank} "
+          f"scores={scores}", flush=True)
+    gpu = run_gpu_local(w, rank, taps=taps, scores=scores)
     ref = oracle_local(w, rank)
     ok, rep = compare_local(gpu, ref, TAU[w.dims.dtype], taps=taps)
     print(f"[parity] {w.name}: {fmt(rep)}", flush=True)
@@ -65,6 +66,13 @@ SMALL_BF16 = [
 @pytest.mark.parametrize("w", SMALL_BF16, ids=lambda w: w.name)
 def test_small_bf16_local(w):
     _run(w, taps=True)
+
+
+@pytest.mark.parametrize("w", [SMALL_BF16[i] for i in (1, 3, 4)], ids=lambda w: w.name)
+def test_small_bf16_split_scores(w):
+    # scores from the fp16 Q, K plus their rounding residuals
+    from tensor_model_transformer_amd import binding as B
+    _run(w, taps=True, scores=B.TP_SCORES_SPLIT)
 
 
 def test_small_fp32_d160_padding():
