@@ -180,12 +180,29 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* red) {
 }
 
 // ---- GeLU (exact erf form, or the tanh approximation) ---------------------------
+// erf(x) for x >= 0 from Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (rational approximation in t = 1/(1 + p x) times
+// exp(-x^2), absolute error at most 1.5e-7), given ex2 = exp(-x^2). Branch
+// free, and the exponential is shared with the GeLU derivative.
+__device__ __forceinline__ float erf_as7126(float ax, float ex2) {
+  const float t = __builtin_amdgcn_rcpf(1.f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f +
+           t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  return 1.f - poly * ex2;
+}
+
+// Exact-form GeLU, u * Phi(u) with Phi(u) = (1 + erf(u / sqrt 2)) / 2, and
+// its derivative Phi(u) + u phi(u), phi(u) = exp(-u^2 / 2) / sqrt(2 pi).
 __device__ __forceinline__ float gelu_f(float u, int tanh_form) {
   if (tanh_form) {
     const float c = 0.7978845608028654f;  // sqrt(2/pi)
     return 0.5f * u * (1.f + tanhf(c * (u + 0.044715f * u * u * u)));
   }
-  return 0.5f * u * (1.f + erff(u * 0.7071067811865476f));
+  const float ax = fabsf(u) * 0.7071067811865476f;
+  const float ex2 = exp2f(-1.4426950408889634f * ax * ax);  // exp(-u^2/2)
+  const float er = copysignf(erf_as7126(ax, ex2), u);
+  return 0.5f * u * (1.f + er);
 }
 __device__ __forceinline__ float gelu_grad_f(float u, int tanh_form) {
   if (tanh_form) {
@@ -193,9 +210,10 @@ __device__ __forceinline__ float gelu_grad_f(float u, int tanh_form) {
     float th = tanhf(c * (u + 0.044715f * u * u * u));
     return 0.5f * (1.f + th) + 0.5f * u * (1.f - th * th) * c * (1.f + 0.134145f * u * u);
   }
-  // Phi(u) + u * phi(u)
-  return 0.5f * (1.f + erff(u * 0.7071067811865476f)) +
-         u * 0.3989422804014327f * expf(-0.5f * u * u);
+  const float ax = fabsf(u) * 0.7071067811865476f;
+  const float ex2 = exp2f(-1.4426950408889634f * ax * ax);
+  const float er = copysignf(erf_as7126(ax, ex2), u);
+  return 0.5f * (1.f + er) + u * 0.3989422804014327f * ex2;
 }
 
 }  // namespace tpl

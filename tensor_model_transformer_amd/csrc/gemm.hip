@@ -76,6 +76,26 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float
   store4_dt(g.C, g.c_dtype, off, v);
 }
 
+// Output tile of this workgroup. Workgroups are dealt to the 8 XCDs round
+// robin (workgroup w runs on XCD w % 8), and each XCD has its own L2. The
+// linear tile order is therefore regrouped so that XCD x receives the
+// contiguous range [x*T/8, (x+1)*T/8) of a grouped order (bands of kGroupM
+// tile rows, column by column inside a band): the tiles resident on one XCD
+// at a time form a compact block that shares A row panels and B column
+// panels in that XCD's L2.
+constexpr int kXCDs = 8, kGroupM = 8;
+__device__ __forceinline__ void tile_coords(int M, int N, int BM, int BN, int* tm, int* tn) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if (total % kXCDs == 0) t = (t % kXCDs) * (total / kXCDs) + t / kXCDs;
+  const int band = kGroupM * tiles_n;
+  const int b = t / band, r = t % band;
+  const int rows = min(kGroupM, tiles_m - b * kGroupM);  // rows in this (maybe short) band
+  *tm = b * kGroupM + r % rows;
+  *tn = r / rows;
+}
+
 // Split-K partial (raw accumulator) store.
 __device__ __forceinline__ void partial4(const GemmArgs& g, int split_idx, int m, int n,
                                          const float v[4]) {
@@ -194,11 +214,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
   uint16_t* Bs = As + 2 * BM * LDK;                       // [2][BN*LDK] fp16
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / WN, wn = wid % WN;
-  const int tiles_n = (g.N + BN - 1) / BN;
-  const int tile = blockIdx.x;
-  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  int tm, tn;
+  tile_coords(g.M, g.N, BM, BN, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int split_idx = blockIdx.y;
   const int ktiles = (g.K + BK - 1) / BK;
   const int kt0 = split_idx * ktiles_per_split;
@@ -258,21 +278,36 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
     __syncthreads();
   }
 
-  // acc[i][j][4*jj + e] = C[m][n] with m = row of this lane, n = 8*jj + 4*(lane/32) + e
+  // Epilogue through LDS, one 32-row slice of the wave's tile at a time.
+  // acc[i][j][4*jj + e] = C[m][n] with m = this lane's row and n = 8*jj +
+  // 4*(lane/32) + e, i.e. each lane holds a column strip of one row. The
+  // wave writes its slice to a private LDS region and then walks it row by
+  // row, 4 consecutive columns per lane, so every output row segment is
+  // written by adjacent lanes (coalesced) and acc is only ever indexed by
+  // constants.
+  constexpr int CP = WTN + 4;  // fp32 pitch of a slice row
+  static_assert(2 * (BM + BN) * LDK * 2 >= WM * WN * 32 * CP * 4, "epilogue slices fit in LDS");
+  float* cs = reinterpret_cast<float*>(smem) + wid * 32 * CP;
   const int half = lane >> 5;
+  __syncthreads();  // every wave is done with the operand tiles
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + lrow;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * jj + 4 * half;
-        float v[4] = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
-                      acc[i][j][4 * jj + 3]};
-        if (gridDim.y > 1) partial4(g, split_idx, m, n, v);
-        else epilogue4(g, m, n, v);
-      }
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(cs + lrow * CP + j * 32 + 8 * jj + 4 * half) =
+            make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
+                        acc[i][j][4 * jj + 3]);
+    constexpr int LPR = WTN / 4;  // lanes per slice row
+#pragma unroll 1
+    for (int r = lane / LPR; r < 32; r += 64 / LPR) {
+      const int c = 4 * (lane % LPR);
+      const float4 q = *reinterpret_cast<const float4*>(cs + r * CP + c);
+      float v[4] = {q.x, q.y, q.z, q.w};
+      const int m = m0 + wm * WTM + i * 32 + r, n = n0 + wn * WTN + c;
+      if (gridDim.y > 1) partial4(g, split_idx, m, n, v);
+      else epilogue4(g, m, n, v);
     }
   }
 }
@@ -365,20 +400,34 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
 // ----------------------------------------------------------------------------
 struct TileCfg {
   int bm, bn;
+  int per_cu;       // workgroups resident per CU (LDS bound)
+  double eff;       // relative MFMA efficiency of the tile shape
 };
-static constexpr TileCfg kBig = {256, 256};
-static constexpr TileCfg kSmall = {128, 128};
+static constexpr TileCfg kBig = {256, 256, 1, 1.0};
+static constexpr TileCfg kWide = {256, 192, 1, 0.95};
+static constexpr TileCfg kSmall = {128, 128, 2, 0.8};
 static constexpr int kCUs = 256;
 
 static long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
+// Time model: rounds of resident workgroups times the work of one tile.
+static double tile_cost(const TileCfg& t, int M, int N, int split) {
+  const long tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn) * split;
+  const long rounds = ceil_div(tiles, (long)kCUs * t.per_cu);
+  return (double)rounds * t.per_cu * t.bm * t.bn / t.eff;
+}
+
 static TileCfg choose_tile(int M, int N, int split) {
-  const long tb = ceil_div(M, kBig.bm) * ceil_div(N, kBig.bn) * split;
-  const long ts = ceil_div(M, kSmall.bm) * ceil_div(N, kSmall.bn) * split;
-  // one 256x256 workgroup per CU (LDS); two 128x128 ones, ~20% less efficient
-  const double cost_big = (double)ceil_div(tb, kCUs) * 65536.0;
-  const double cost_small = (double)ceil_div(ts, 2 * kCUs) * 2.0 * 16384.0 / 0.8;
-  return cost_big <= cost_small ? kBig : kSmall;
+  TileCfg best = kBig;
+  double bc = tile_cost(kBig, M, N, split);
+  for (const TileCfg& t : {kWide, kSmall}) {
+    const double c = tile_cost(t, M, N, split);
+    if (c < bc) {
+      bc = c;
+      best = t;
+    }
+  }
+  return best;
 }
 
 int gemm_choose_split(const GemmArgs& g) {
@@ -431,7 +480,8 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
 template <bool AK, bool BKM>
 static hipError_t dispatch_f16(const GemmArgs& g, int split, hipStream_t s) {
   const TileCfg t = choose_tile(g.M, g.N, split);
-  if (t.bm == 256) return launch_f16<256, 256, 2, 4, AK, BKM>(g, split, s);
+  if (t.bm == 256 && t.bn == 256) return launch_f16<256, 256, 2, 4, AK, BKM>(g, split, s);
+  if (t.bm == 256) return launch_f16<256, 192, 4, 2, AK, BKM>(g, split, s);
   return launch_f16<128, 128, 2, 2, AK, BKM>(g, split, s);
 }
 
