@@ -40,6 +40,11 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// 2^x with the hardware exponential (v_exp_f32, about 1 ulp; results below
+// the fp32 normal range flush to zero, which is below anything the softmax
+// can resolve next to its row maximum).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f16x8 ld8(const f16* p) {
   return *reinterpret_cast<const f16x8*>(p);
 }
@@ -84,7 +89,8 @@ __device__ __forceinline__ f16x8 tr_frag(const f16* T, int P, int m0, int kA, in
 }
 
 // Register staging for a [R][D] row-major slice of global memory (row stride
-// ld), rows >= nrows read as zero; stored into an LDS tile of pitch P.
+// ld), rows >= nrows read as zero; stored into an LDS tile of pitch P. The
+// address is clamped to the last row (nrows >= 1) and the value selected.
 template <int R, int D, int NT>
 struct RowTile {
   static constexpr int kChunks = R * (D / 8);
@@ -96,10 +102,11 @@ struct RowTile {
     for (int i = 0; i < kPer; ++i) {
       const int c = tid + i * NT;
       const int row = c / (D / 8), dc = c % (D / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if ((kChunks % NT == 0 || c < kChunks) && r0 + row < nrows)
-        v = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + row) * ld + 8 * dc);
-      st[i] = v;
+      const bool ok = (kChunks % NT == 0 || c < kChunks) & (r0 + row < nrows);
+      const int rr = min(r0 + row, nrows - 1);
+      const int cc = (kChunks % NT == 0 || c < kChunks) ? dc : 0;
+      const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)rr * ld + 8 * cc);
+      st[i] = ok ? v : make_uint4(0, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void store(f16* dst, int P, int tid) const {
@@ -112,6 +119,72 @@ struct RowTile {
     }
   }
 };
+
+// Workgroup barrier that leaves global loads in flight: this wave's LDS
+// traffic is drained (lgkmcnt(0)) but vmcnt is not waited, so tiles fetched
+// into registers for later blocks keep streaming across it. The empty asm
+// statements keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// K and V (and the K residual) tiles of one 64-key block, staged in registers.
+template <int D, bool SPLIT>
+struct KVRegs {
+  RowTile<64, D, 256> k, v, kl;
+  __device__ __forceinline__ void load(const f16* Kp, const f16* Vp, const f16* Klp, long ldq,
+                                       int r0, int seq, int tid) {
+    k.load(Kp, ldq, r0, seq, tid);
+    v.load(Vp, ldq, r0, seq, tid);
+    if constexpr (SPLIT) kl.load(Klp, ldq, r0, seq, tid);
+  }
+  __device__ __forceinline__ void store(f16* base, int P, int TILE, int tid) const {
+    k.store(base, P, tid);
+    v.store(base + TILE, P, tid);
+    if constexpr (SPLIT) kl.store(base + 2 * TILE, P, tid);
+  }
+};
+
+// Block pipeline shared by the kernels that stream 64-row tiles through two
+// LDS buffers. Memory latency on this part runs to microseconds, longer than
+// one block's MFMA work, so when registers allow (DEEP) the tile of block
+// ib+1 is fetched two blocks ahead, at ib-2, into one of two register
+// stages; otherwise one block ahead. `fetch(stage, blk)` issues the global
+// loads, `put(stage, buf)` writes a staged tile to LDS buffer `buf`, and
+// `compute(ib)` consumes LDS buffer ib & 1.
+template <bool DEEP, typename Stage, typename Fetch, typename Put, typename Compute>
+__device__ __forceinline__ void block_pipeline(int nblk, Stage& sa, Stage& sb, Fetch fetch, Put put,
+                                               Compute compute) {
+  if (nblk <= 0) return;
+  fetch(sa, 0);
+  put(sa, 0);
+  if constexpr (DEEP) {
+    if (nblk > 1) fetch(sa, 1);
+    if (nblk > 2) fetch(sb, 2);
+    lds_barrier();
+    auto step = [&](int ib, Stage& st) {
+      compute(ib);
+      if (ib + 1 < nblk) put(st, (ib + 1) & 1);
+      if (ib + 3 < nblk) fetch(st, ib + 3);
+      lds_barrier();
+    };
+    for (int ib = 0; ib < nblk; ib += 2) {
+      step(ib, sa);
+      if (ib + 1 < nblk) step(ib + 1, sb);
+    }
+  } else {
+    lds_barrier();
+    for (int ib = 0; ib < nblk; ++ib) {
+      if (ib + 1 < nblk) fetch(sa, ib + 1);
+      compute(ib);
+      if (ib + 1 < nblk) put(sa, (ib + 1) & 1);
+      lds_barrier();
+    }
+  }
+}
 
 // ============================================================================
 // fp16 forward
@@ -164,25 +237,14 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
     for (int e = 0; e < 16; ++e) O[t][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  RowTile<KB, D, 256> kt, vt, klt;
   const int nblk = (kv_end + KB - 1) / KB;
-  if (nblk > 0) {
-    kt.load(Kp, ldq, 0, seq, tid);
-    vt.load(Vp, ldq, 0, seq, tid);
-    if constexpr (SPLIT) klt.load(Klp, ldq, 0, seq, tid);
-    kt.store(lds, P, tid);
-    vt.store(lds + TILE, P, tid);
-    if constexpr (SPLIT) klt.store(lds + 2 * TILE, P, tid);
-  }
-  __syncthreads();
-  for (int ib = 0; ib < nblk; ++ib) {
+  KVRegs<D, SPLIT> sa, sb;
+  auto fetch = [&](KVRegs<D, SPLIT>& st, int blk) {
+    st.load(Kp, Vp, Klp, ldq, blk * KB, seq, tid);
+  };
+  auto put = [&](const KVRegs<D, SPLIT>& st, int buf) { st.store(lds + buf * NT * TILE, P, TILE, tid); };
+  auto compute = [&](int ib) {
     const int kb0 = ib * KB;
-    const bool more = ib + 1 < nblk;
-    if (more) {
-      kt.load(Kp, ldq, kb0 + KB, seq, tid);
-      vt.load(Vp, ldq, kb0 + KB, seq, tid);
-      if constexpr (SPLIT) klt.load(Klp, ldq, kb0 + KB, seq, tid);
-    }
     const f16* Ks = lds + (ib & 1) * NT * TILE;
     const f16* Vs = Ks + TILE;
     const f16* Kls = Ks + 2 * TILE;  // residual tile (SPLIT only)
@@ -216,13 +278,13 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = exp2_fast(m_run - m_new);
       float ls = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(S[st][e] - m_new);
+          const float p = exp2_fast(S[st][e] - m_new);
           S[st][e] = p;
           ls += p;
         }
@@ -244,14 +306,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
                         O[t]);
       }
     }
-    if (more) {
-      f16* nxt = lds + ((ib + 1) & 1) * NT * TILE;
-      kt.store(nxt, P, tid);
-      vt.store(nxt + TILE, P, tid);
-      if constexpr (SPLIT) klt.store(nxt + 2 * TILE, P, tid);
-    }
-    __syncthreads();
-  }
+  };
+  block_pipeline<(D <= 128)>(nblk, sa, sb, fetch, put, compute);
 
   if (q < seq) {
     const float inv = 1.f / l_run;
@@ -353,37 +409,34 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
   const bool wave_keys_valid = kw0 < (causal ? seq : L);
   const int q_begin = causal ? kblk * 128 : 0;
   const int nblk = (seq - q_begin + QB - 1) / QB;
-  RowTile<QB, D, 256> qt, gt, qlt;
-  float lsr = 0.f, dlr = 0.f;
-  auto fetch = [&](int q0) {
-    qt.load(Qp, ldq, q0, seq, tid);
-    gt.load(dOp, ldo, q0, seq, tid);
-    if constexpr (SPLIT) qlt.load(Qlp, ldq, q0, seq, tid);
+  struct QGRegs {
+    RowTile<QB, D, 256> q, g, ql;
+    float ls, dl;
+  };
+  QGRegs sa, sb;
+  auto fetch = [&](QGRegs& st, int blk) {
+    const int q0 = q_begin + blk * QB;
+    st.q.load(Qp, ldq, q0, seq, tid);
+    st.g.load(dOp, ldo, q0, seq, tid);
+    if constexpr (SPLIT) st.ql.load(Qlp, ldq, q0, seq, tid);
     if (tid < QB) {
       const int qq = q0 + tid;
-      lsr = qq < seq ? lsp[qq] : 0.f;
-      dlr = qq < seq ? dlp[qq] : 0.f;
+      st.ls = qq < seq ? lsp[qq] : 0.f;
+      st.dl = qq < seq ? dlp[qq] : 0.f;
     }
   };
-  auto put = [&](int buf) {
+  auto put = [&](const QGRegs& st, int buf) {
     f16* base = lds + buf * NT * TILE;
-    qt.store(base, P, tid);
-    gt.store(base + TILE, P, tid);
-    if constexpr (SPLIT) qlt.store(base + 2 * TILE, P, tid);
+    st.q.store(base, P, tid);
+    st.g.store(base + TILE, P, tid);
+    if constexpr (SPLIT) st.ql.store(base + 2 * TILE, P, tid);
     if (tid < QB) {
-      ls[buf * QB + tid] = lsr;
-      dl[buf * QB + tid] = dlr;
+      ls[buf * QB + tid] = st.ls;
+      dl[buf * QB + tid] = st.dl;
     }
   };
-  if (nblk > 0) {
-    fetch(q_begin);
-    put(0);
-  }
-  __syncthreads();
-  for (int ib = 0; ib < nblk; ++ib) {
+  auto compute = [&](int ib) {
     const int q0 = q_begin + ib * QB;
-    const bool more = ib + 1 < nblk;
-    if (more) fetch(q0 + QB);
     const f16* Qs = lds + (ib & 1) * NT * TILE;
     const f16* Gs = Qs + TILE;
     const f16* Qls = Qs + 2 * TILE;  // residual tile (SPLIT only)
@@ -407,16 +460,26 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
         }
         dP = mfma32(ld8(Gs + off), vf[ks], dP);
       }
-      // element e: query qh0 + 8*(e>>2) + 4*hh + (e&3), key = this lane's key
+      // element e: query qh0 + 8*(e>>2) + 4*hh + (e&3), key = this lane's key.
+      // The lse / delta of those rows come as 4 vector reads; every element
+      // is evaluated and masked by a select, so the loop has no branches.
+      float lsv[16], dlv[16];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float4 a = *reinterpret_cast<const float4*>(lsb + 32 * qs + 8 * jj + 4 * hh);
+        const float4 b = *reinterpret_cast<const float4*>(dlb + 32 * qs + 8 * jj + 4 * hh);
+        lsv[4 * jj] = a.x; lsv[4 * jj + 1] = a.y; lsv[4 * jj + 2] = a.z; lsv[4 * jj + 3] = a.w;
+        dlv[4 * jj] = b.x; dlv[4 * jj + 1] = b.y; dlv[4 * jj + 2] = b.z; dlv[4 * jj + 3] = b.w;
+      }
       float Pv[16], dS[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int qr = 32 * qs + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const int qq = q0 + qr;
-        const bool ok = qq < seq && key < L && (!causal || key <= qq);
-        const float p = ok ? exp2f(S[e] * sl2 - lsb[qr]) : 0.f;
+        const int qq = qh0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+        // bitwise & / |: no short-circuit, hence no branch per element
+        const bool ok = (qq < seq) & (key < L) & (!causal | (key <= qq));
+        const float p = exp2_fast(ok ? S[e] * sl2 - lsv[e] : -INFINITY);  // 0 when masked
         Pv[e] = p;
-        dS[e] = p * (dP[e] - dlb[qr]);
+        dS[e] = p * (dP[e] - dlv[e]);
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -430,9 +493,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
         }
       }
     }
-    if (more) put((ib + 1) & 1);
-    __syncthreads();
-  }
+  };
+  block_pipeline<(D <= 96 || (D <= 128 && !SPLIT))>(nblk, sa, sb, fetch, put, compute);
 
   if (key < seq) {
     f16* dk = dqkv + (tok0 + key) * ldq + (size_t)head * 3 * D + D;
@@ -508,25 +570,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dQ[t][e] = 0.f;
 
-  RowTile<KB, D, 256> kt, vt, klt;
   const int nblk = (kv_end + KB - 1) / KB;
-  if (nblk > 0) {
-    kt.load(Kp, ldq, 0, seq, tid);
-    vt.load(Vp, ldq, 0, seq, tid);
-    if constexpr (SPLIT) klt.load(Klp, ldq, 0, seq, tid);
-    kt.store(lds, P, tid);
-    vt.store(lds + TILE, P, tid);
-    if constexpr (SPLIT) klt.store(lds + 2 * TILE, P, tid);
-  }
-  __syncthreads();
-  for (int ib = 0; ib < nblk; ++ib) {
+  KVRegs<D, SPLIT> sa, sb;
+  auto fetch = [&](KVRegs<D, SPLIT>& st, int blk) {
+    st.load(Kp, Vp, Klp, ldq, blk * KB, seq, tid);
+  };
+  auto put = [&](const KVRegs<D, SPLIT>& st, int buf) { st.store(lds + buf * NT * TILE, P, TILE, tid); };
+  auto compute = [&](int ib) {
     const int kb0 = ib * KB;
-    const bool more = ib + 1 < nblk;
-    if (more) {
-      kt.load(Kp, ldq, kb0 + KB, seq, tid);
-      vt.load(Vp, ldq, kb0 + KB, seq, tid);
-      if constexpr (SPLIT) klt.load(Klp, ldq, kb0 + KB, seq, tid);
-    }
     const f16* Ks = lds + (ib & 1) * NT * TILE;
     const f16* Vs = Ks + TILE;
     const f16* Kls = Ks + 2 * TILE;  // residual tile (SPLIT only)
@@ -551,7 +602,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int k = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const float p = (qok && k < lim) ? exp2f(S[e] * sl2 - lq) : 0.f;
+          const float p = exp2_fast((qok & (k < lim)) ? S[e] * sl2 - lq : -INFINITY);
           dS[st][e] = p * (dP[e] - dq_);
         }
       }
@@ -564,14 +615,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
                          dQ[t]);
       }
     }
-    if (more) {
-      f16* nxt = lds + ((ib + 1) & 1) * NT * TILE;
-      kt.store(nxt, P, tid);
-      vt.store(nxt + TILE, P, tid);
-      if constexpr (SPLIT) klt.store(nxt + 2 * TILE, P, tid);
-    }
-    __syncthreads();
-  }
+  };
+  block_pipeline<(D <= 128)>(nblk, sa, sb, fetch, put, compute);
 
   if (qok) {
     f16* dq = dqkv + (tok0 + q) * ldq + (size_t)head * 3 * D;
