@@ -136,6 +136,8 @@ def main():
                     help="sequences in the oracle sample (default: the whole micro-batch)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="recompute the FC1 pre-activation in backward (TP_RECOMPUTE_FC1)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -160,7 +162,7 @@ def main():
     d = w.dims
     params = rank_params(w)
     x, dout, vl = layer_inputs(w)
-    sh = Shard(d, w.rank)
+    sh = Shard(d, w.rank, recompute=B.TP_RECOMPUTE_FC1 if args.recompute else B.TP_RECOMPUTE_NONE)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()
@@ -236,7 +238,9 @@ def main():
         "pct_of_peak": 100.0 * value / peak,
         "config": {"workload": w.name, "micro_batch": d.batch, "seq_len": d.seq,
                    "hidden": d.hidden, "heads": d.heads, "ffn": d.ffn, "t": d.t,
-                   "rank": w.rank, "mask": d.mask, "gflop_per_step": flops / 1e9},
+                   "rank": w.rank, "mask": d.mask, "gflop_per_step": flops / 1e9,
+                   "recompute": "fc1" if args.recompute else "none",
+                   "workspace_bytes": sh.ws_bytes},
         "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown,
     }
     print(json.dumps(line))

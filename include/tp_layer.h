@@ -96,6 +96,15 @@ enum { TP_GELU_ERF = 0, TP_GELU_TANH = 1 };
  * scores, three times the score MFMAs); TP_SCORES_AUTO picks SPLIT for
  * hidden >= 8192. */
 enum { TP_SCORES_AUTO = 0, TP_SCORES_FP16 = 1, TP_SCORES_SPLIT = 2 };
+/* Activation recomputation (selective recomputation, "Megatron-LM:
+ * GPU-Cluster Training Parallelism", section "Microbatch and Activation
+ * Memory Tradeoff"). TP_RECOMPUTE_NONE keeps the FC1 pre-activation u
+ * [n, f_l] from forward to backward. TP_RECOMPUTE_FC1 does not keep it: the
+ * backward recomputes u = c @ W_fc1,r + b_fc1,r (one more FC1 GEMM) and the
+ * workspace shrinks by n*f_l elements. The attention probabilities are never
+ * kept in either mode (the backward recomputes them from the saved
+ * log-sum-exp). */
+enum { TP_RECOMPUTE_NONE = 0, TP_RECOMPUTE_FC1 = 1 };
 
 /* Forward phases. TP_ALL runs the whole shard with both g exchanges taken as
  * the identity: the rank's own partial stands in for the sum (exactly the
@@ -113,6 +122,7 @@ typedef struct {
   int dx_dtype;     /* dtype of tp_bwd_io.dx: TP_DTYPE_F32 (default, also the
                        value of a zeroed struct) or the layer's storage dtype */
   int scores;       /* TP_SCORES_AUTO (default), TP_SCORES_FP16 or TP_SCORES_SPLIT */
+  int recompute;    /* TP_RECOMPUTE_NONE (default) or TP_RECOMPUTE_FC1 */
 } tp_layer_opts;
 
 /* Parameters of rank r (shapes above) and, for TP_MASK_PADDING, the number
@@ -178,8 +188,8 @@ typedef struct {
  *   dtype: TP_DTYPE_F32 or TP_DTYPE_BF16. mask: TP_MASK_CAUSAL/TP_MASK_PADDING.
  *   opts: NULL for the defaults (eps 1e-5, exact-erf GeLU, fp32 dx, automatic
  *     score precision); opts->dx_dtype other than TP_DTYPE_F32 or `dtype`,
- *     an unknown opts->scores, or TP_SCORES_SPLIT with TP_DTYPE_F32 are
- *     TP_ERR_UNSUPPORTED.
+ *     an unknown opts->scores or opts->recompute, or TP_SCORES_SPLIT with
+ *     TP_DTYPE_F32 are TP_ERR_UNSUPPORTED.
  * Checks: every size > 0; hidden % heads == 0; heads % t == 0; ffn % t == 0;
  * (ffn/t) % 8 == 0; 0 <= rank < t; head dim in {32, 64, 96, 128, 160}
  * (TP_ERR_UNSUPPORTED otherwise). Allocates no device memory. On success
@@ -220,7 +230,8 @@ int tp_exchange_sum(void *dst, int dst_dtype, const float *const *parts,
  *                   log2(sum_k exp(S_ik)) with S the scaled scores
  *   TP_TAP_H_MID    h_mid  [n, h]      fp32
  *   TP_TAP_LN2_OUT  c      [n, h]      act
- *   TP_TAP_FC1_PRE  u      [n, f_l]    act (FC1 output before GeLU)
+ *   TP_TAP_FC1_PRE  u      [n, f_l]    act (FC1 output before GeLU;
+ *                                      TP_ERR_UNSUPPORTED with TP_RECOMPUTE_FC1)
  *   TP_TAP_FC1_OUT  z      [n, f_l]    act
  *   TP_TAP_DQKV     dqkv   [n, 3*h_l]  act (after a backward)
  *   TP_TAP_DH       dh     [n, h]      fp32 (residual-stream grad, after TP_BWD_ATTN)

@@ -28,6 +28,7 @@ ERROR_NAMES = {0: "TP_OK", -1: "TP_ERR_ARG", -2: "TP_ERR_SHAPE", -3: "TP_ERR_UNS
 
 TP_DTYPE_F32, TP_DTYPE_BF16 = 0, 1
 TP_SCORES_AUTO, TP_SCORES_FP16, TP_SCORES_SPLIT = 0, 1, 2
+TP_RECOMPUTE_NONE, TP_RECOMPUTE_FC1 = 0, 1
 TP_MASK_CAUSAL, TP_MASK_PADDING = 0, 1
 TP_GELU_ERF, TP_GELU_TANH = 0, 1
 TP_ALL, TP_FWD_ATTN, TP_FWD_MLP = 0, 1, 2
@@ -46,7 +47,8 @@ KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce")
 
 
 class tp_layer_opts(Structure):
-    _fields_ = [("ln_eps", c_float), ("gelu", c_int), ("dx_dtype", c_int), ("scores", c_int)]
+    _fields_ = [("ln_eps", c_float), ("gelu", c_int), ("dx_dtype", c_int), ("scores", c_int),
+                ("recompute", c_int)]
 
 
 class tp_params(Structure):
@@ -109,7 +111,8 @@ def tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, 
     if opts is not None:
         o = ctypes.byref(tp_layer_opts(float(opts.get("ln_eps", 1e-5)), int(opts.get("gelu", 0)),
                                        int(opts.get("dx_dtype", TP_DTYPE_F32)),
-                                       int(opts.get("scores", TP_SCORES_AUTO))))
+                                       int(opts.get("scores", TP_SCORES_AUTO)),
+                                       int(opts.get("recompute", TP_RECOMPUTE_NONE))))
     rc = lib().tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, o,
                                ctypes.byref(h), ctypes.byref(ws))
     return rc, h.value, ws.value

@@ -66,6 +66,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float
     }
     store4_dt(g.C2, DT_F16, (size_t)m * g.ldc2 + n, lo);
   }
+  if (!g.C) return;  // only C2 wanted (the FC1 pre-activation is not kept)
   const size_t off = (size_t)m * g.ldc + n;
   if (g.accumulate && g.c_dtype == DT_F32) {
     float o[4];

@@ -58,6 +58,7 @@ struct tp_layer {
   int gelu_tanh;
   bool dx_f32;  // dx written in fp32 (else in the storage dtype)
   bool split_scores;  // qkv also kept as fp16 residuals; scores from three products
+  bool recompute_fc1;  // FC1 pre-activation recomputed in backward, not kept
   // derived
   int n, dh, Hl, hl, fl, esz;
   int sdt;   // storage type at the boundary (x, params, out, dx): DT_BF16 or DT_F32
@@ -124,9 +125,14 @@ void plan(tp_layer* L) {
   take(L->mean2, n * 4);
   take(L->rstd2, n * 4);
   take(L->c, n * h * e);
-  take(L->u, n * L->fl * e);
+  // u (FC1 pre-activation) is kept from forward unless it is recomputed in
+  // backward. du has its own buffer, so a backward leaves the forward's saved
+  // tensors intact (it can be run again, e.g. to accumulate); with recompute,
+  // du and the recomputed u share one buffer placed over the attention-
+  // backward buffers, which are not yet live while du is.
+  take(L->u, L->recompute_fc1 ? 0 : n * L->fl * e);
   take(L->z, n * L->fl * e);
-  take(L->du, n * L->fl * e);
+  if (!L->recompute_fc1) take(L->du, n * L->fl * e);
   take(L->dc, n * h * 4);
   take(L->dh_f, n * h * 4);
   take(L->dh_s, n * h * e);
@@ -134,6 +140,15 @@ void plan(tp_layer* L) {
   take(L->delta, stats);
   take(L->dqkv, n * 3 * L->hl * e);
   take(L->da, n * h * 4);
+  if (L->recompute_fc1) {
+    const size_t need = n * L->fl * e, span = off - L->dh_f.off;
+    if (need > span) {
+      Region pad;
+      take(pad, need - span);
+    }
+    L->du.off = L->dh_f.off;
+    L->du.bytes = need;
+  }
   // reduction partials: LayerNorm [nblk][3][h]; column sums [nblk][cols]
   int rpb;
   size_t part = reduce_scratch_floats(ln_bwd_blocks(L->n, L->hidden, &rpb), 3, L->hidden);
@@ -315,7 +330,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 0; g.b_dtype = L->sdt;
   g.bias = p->b_fc1;
   g.epi = EPI_BIAS_GELU;
-  g.C = at<void>(ws, L->u); g.ldc = fl;
+  g.C = L->recompute_fc1 ? nullptr : at<void>(ws, L->u); g.ldc = fl;
   g.C2 = at<void>(ws, L->z); g.ldc2 = fl;
   if ((e = run_gemm(L, g, s))) return e;
   g = gemm_base(L);
@@ -372,12 +387,26 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
   float* skw = at<float>(ws, L->splitk);
-  GemmArgs g = gemm_base(L);
+  GemmArgs g;
+  if (L->recompute_fc1) {
+    // u = c @ W_fc1,r + b_fc1,r again, straight into the du buffer
+    g = gemm_base(L);
+    g.M = n; g.N = fl; g.K = h;
+    g.A = at<void>(ws, L->c); g.lda = h; g.a_kmajor = 1;
+    g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 0; g.b_dtype = L->sdt;
+    g.bias = p->b_fc1;
+    g.C = at<void>(ws, L->du); g.ldc = fl;
+    if ((e = run_gemm(L, g, s))) return e;
+  }
+  // du = (dout @ W_fc2,r^T) * GeLU'(u); with recompute u is in the du buffer
+  // and is overwritten in place (each element is read, then written, by the
+  // same thread of the epilogue)
+  g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
   g.A = io->dout; g.lda = h; g.a_kmajor = 1; g.a_dtype = L->sdt;
   g.B = p->w_fc2; g.ldb = h; g.b_kmajor = 1; g.b_dtype = L->sdt;
   g.epi = EPI_DGELU;
-  g.aux = at<void>(ws, L->u); g.ldaux = fl;
+  g.aux = at<void>(ws, L->recompute_fc1 ? L->du : L->u); g.ldaux = fl;
   g.C = at<void>(ws, L->du); g.ldc = fl;
   if ((e = run_gemm(L, g, s))) return e;
   if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s))) return e;
@@ -492,17 +521,20 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   int gelu = TP_GELU_ERF;
   int dx_dtype = TP_DTYPE_F32;
   int scores = TP_SCORES_AUTO;
+  int recompute = TP_RECOMPUTE_NONE;
   if (opts) {
     eps = opts->ln_eps;
     gelu = opts->gelu;
     dx_dtype = opts->dx_dtype;
     scores = opts->scores;
+    recompute = opts->recompute;
     if (!(eps > 0.f)) return TP_ERR_ARG;
     if (gelu != TP_GELU_ERF && gelu != TP_GELU_TANH) return TP_ERR_UNSUPPORTED;
     if (dx_dtype != TP_DTYPE_F32 && dx_dtype != dtype) return TP_ERR_UNSUPPORTED;
     if (scores != TP_SCORES_AUTO && scores != TP_SCORES_FP16 && scores != TP_SCORES_SPLIT)
       return TP_ERR_UNSUPPORTED;
     if (scores == TP_SCORES_SPLIT && dtype != TP_DTYPE_BF16) return TP_ERR_UNSUPPORTED;
+    if (recompute != TP_RECOMPUTE_NONE && recompute != TP_RECOMPUTE_FC1) return TP_ERR_UNSUPPORTED;
   }
   tp_layer* L = new (std::nothrow) tp_layer();
   if (!L) return TP_ERR_ARG;
@@ -510,6 +542,7 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   L->t = t; L->rank = rank; L->dtype = dtype; L->mask = mask;
   L->eps = eps; L->gelu_tanh = gelu == TP_GELU_TANH;
   L->dx_f32 = dx_dtype == TP_DTYPE_F32;
+  L->recompute_fc1 = recompute == TP_RECOMPUTE_FC1;
   L->split_scores = dtype == TP_DTYPE_BF16 &&
                     (scores == TP_SCORES_SPLIT ||
                      (scores == TP_SCORES_AUTO && hidden >= kSplitScoresHidden));
@@ -639,7 +672,10 @@ int tp_layer_tap(const tp_layer* L, int tap, size_t* offset, size_t* bytes) {
     case TP_TAP_LSE: r = &L->lse2; break;
     case TP_TAP_H_MID: r = &L->h_mid; break;
     case TP_TAP_LN2_OUT: r = &L->c; break;
-    case TP_TAP_FC1_PRE: r = &L->u; break;
+    case TP_TAP_FC1_PRE:
+      if (L->recompute_fc1) return TP_ERR_UNSUPPORTED;  // not kept
+      r = &L->u;
+      break;
     case TP_TAP_FC1_OUT: r = &L->z; break;
     case TP_TAP_DQKV: r = &L->dqkv; break;
     case TP_TAP_DH: r = &L->dh_f; break;

@@ -39,7 +39,8 @@ class Shard:
     """One handle of the library plus its workspace."""
 
     def __init__(self, dims: LayerDims, rank: int, device="cuda:0", gelu: int = B.TP_GELU_ERF,
-                 eps: float = 1e-5, dx_fp32: bool = True, scores: int = B.TP_SCORES_AUTO):
+                 eps: float = 1e-5, dx_fp32: bool = True, scores: int = B.TP_SCORES_AUTO,
+                 recompute: int = B.TP_RECOMPUTE_NONE):
         self.dims = dims
         self.rank = rank
         self.device = torch.device(device)
@@ -50,7 +51,7 @@ class Shard:
             B.TP_MASK_PADDING if dims.mask == "padding" else B.TP_MASK_CAUSAL,
             {"ln_eps": eps, "gelu": gelu,
              "dx_dtype": B.TP_DTYPE_F32 if dx_fp32 or dims.dtype == "f32" else B.TP_DTYPE_BF16,
-             "scores": scores})
+             "scores": scores, "recompute": recompute})
         self.dx_fp32 = dx_fp32
         _check("tp_layer_create", rc)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)

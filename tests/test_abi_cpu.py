@@ -73,6 +73,7 @@ def create(**kw):
     (dict(opts={"dx_dtype": 7}), B.TP_ERR_UNSUPPORTED),
     (dict(dtype=B.TP_DTYPE_F32, opts={"dx_dtype": B.TP_DTYPE_BF16}), B.TP_ERR_UNSUPPORTED),
     (dict(opts={"scores": 3}), B.TP_ERR_UNSUPPORTED),
+    (dict(opts={"recompute": 2}), B.TP_ERR_UNSUPPORTED),
     (dict(dtype=B.TP_DTYPE_F32, opts={"scores": B.TP_SCORES_SPLIT}), B.TP_ERR_UNSUPPORTED),
 ])
 def test_create_validation(lib, kw, code):
@@ -117,6 +118,22 @@ def test_split_scores_workspace(lib):
     rc, h, ws_fp16 = create(opts={"scores": B.TP_SCORES_FP16}, **big)
     B.tp_layer_destroy(h)
     assert ws_auto - ws_fp16 >= 8 * 3 * 1024 * 2
+
+
+def test_recompute_fc1_workspace(lib):
+    # without the kept FC1 pre-activation the workspace shrinks by n*f_l
+    # 16-bit elements; du then lives in the attention-backward buffers
+    kw = dict(hidden=256, heads=4, ffn=1024, seq=64, micro_batch=2, t=1)
+    n, fl = 128, 1024
+    rc, h0, ws0 = create(**kw)
+    assert rc == B.TP_OK
+    rc, h1, ws1 = create(opts={"recompute": B.TP_RECOMPUTE_FC1}, **kw)
+    assert rc == B.TP_OK
+    assert ws0 - ws1 >= n * fl * 2
+    assert B.tp_layer_tap(h1, B.TAPS["u"])[0] == B.TP_ERR_UNSUPPORTED
+    assert B.tp_layer_tap(h0, B.TAPS["u"])[0] == B.TP_OK
+    B.tp_layer_destroy(h0)
+    B.tp_layer_destroy(h1)
 
 
 def test_call_argument_errors_need_no_device(lib):

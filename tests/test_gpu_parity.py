@@ -94,6 +94,30 @@ def test_dx_in_storage_dtype():
     assert gpu["dx_dtype"] == "bfloat16"
 
 
+@pytest.mark.parametrize("w", [SMALL_BF16[0], SMALL_BF16[4]], ids=lambda w: w.name)
+def test_recompute_fc1_is_bitwise_equal(w):
+    # TP_RECOMPUTE_FC1 recomputes u = c @ W_fc1 + b_fc1 in backward with the same
+    # kernel and inputs as the forward, so every result is bitwise unchanged
+    _need_gpu()
+    from tensor_model_transformer_amd import binding as B
+    a = run_gpu_local(w)
+    b = run_gpu_local(w, recompute=B.TP_RECOMPUTE_FC1)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["dx"], b["dx"])
+    for k in a["grads"]:
+        assert np.array_equal(a["grads"][k], b["grads"][k]), k
+
+
+def test_recompute_fc1_fp32_parity():
+    _need_gpu()
+    from tensor_model_transformer_amd import binding as B
+    w = WORKLOADS["tiny_gpt_fp32"]
+    gpu = run_gpu_local(w, 1, taps=True, recompute=B.TP_RECOMPUTE_FC1)
+    ref = oracle_local(w, 1)
+    ok, rep = compare_local(gpu, ref, TAU["f32"], taps=True)
+    print(f"[parity] tiny fp32 recompute: {fmt(rep)}", flush=True)
+    assert ok, fmt(rep)
+
+
 def test_single_token_sequence():
     # degenerate: seq = 1 (attention is the identity on V), batch 3
     _run(Workload("seq1", LayerDims(3, 1, 128, 4, 256, t=1, dtype="bf16", mask="causal"),
