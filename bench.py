@@ -136,6 +136,9 @@ def main():
                     help="sequences in the oracle sample (default: the whole micro-batch)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("tp", "sp"), default="tp",
+                    help="tp: TP_ALL forward + backward of one rank; sp: one rank's share of the "
+                         "sequence-parallel phases (its kernels only, exchanges excluded)")
     ap.add_argument("--recompute", action="store_true",
                     help="recompute the FC1 pre-activation in backward (TP_RECOMPUTE_FC1)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -162,7 +165,9 @@ def main():
     d = w.dims
     params = rank_params(w)
     x, dout, vl = layer_inputs(w)
-    sh = Shard(d, w.rank, recompute=B.TP_RECOMPUTE_FC1 if args.recompute else B.TP_RECOMPUTE_NONE)
+    sp = args.layout == "sp"
+    sh = Shard(d, w.rank, recompute=B.TP_RECOMPUTE_FC1 if args.recompute else B.TP_RECOMPUTE_NONE,
+               sequence_parallel=sp)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()
@@ -172,6 +177,38 @@ def main():
     def step():
         _check("tp_layer_fwd", sh.fwd(p, out, x=xd))
         _check("tp_layer_bwd", sh.bwd(p, grads, x=xd, dout=doutd, dx=dx))
+
+    if sp:
+        # One rank's sequence-parallel share: LayerNorms, biases and residuals on
+        # its n/t rows, GEMMs and attention on all n rows. The gathered and
+        # reduced tensors the collectives would deliver are stand-ins here
+        # (their values do not change the work); the collectives themselves
+        # are not part of one rank's kernels and are not timed.
+        nc = d.tokens // d.t
+        rows = slice(w.rank * nc, (w.rank + 1) * nc)
+        act = torch.float16 if d.dtype == "bf16" else torch.float32
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        g_a = torch.randn(d.tokens, d.hidden, generator=gen, device="cuda").to(act)
+        g_c = torch.randn(d.tokens, d.hidden, generator=gen, device="cuda").to(act)
+        g_dh = torch.randn(d.tokens, d.hidden, generator=gen, device="cuda").to(act)
+        red = torch.randn(nc, d.hidden, generator=gen, device="cuda")
+        part = sh.empty_act(fp32=True)
+        x_r, dout_r, out_r, dx_r = xd[rows], doutd[rows], out[rows], dx[rows]
+
+        def step():  # noqa: F811
+            F, Bw = sh.fwd, sh.bwd
+            _check("sp ln1", F(p, None, x=x_r, gathered=g_a, phase=B.TP_FWD_SP_LN1))
+            _check("sp attn", F(p, part, gathered=g_a, phase=B.TP_FWD_SP_ATTN))
+            _check("sp ln2", F(p, None, x=x_r, reduced=red, gathered=g_c, phase=B.TP_FWD_SP_LN2))
+            _check("sp mlp", F(p, part, gathered=g_c, phase=B.TP_FWD_SP_MLP))
+            _check("sp out", F(p, out_r, reduced=red, phase=B.TP_FWD_SP_OUT))
+            _check("sp bwd mlp", Bw(p, grads, dout=dout_r, gathered_grad=doutd, gathered_act=g_c,
+                                    partial=part, phase=B.TP_BWD_SP_MLP))
+            _check("sp bwd ln2", Bw(p, grads, dc=red, dout=dout_r, gathered_grad=g_dh,
+                                    phase=B.TP_BWD_SP_LN2))
+            _check("sp bwd attn", Bw(p, grads, gathered_grad=g_dh, gathered_act=g_a, partial=part,
+                                     phase=B.TP_BWD_SP_ATTN))
+            _check("sp bwd ln1", Bw(p, grads, da=red, x=x_r, dx=dx_r, phase=B.TP_BWD_SP_LN1))
 
     for _ in range(args.warmup):
         step()
@@ -239,7 +276,7 @@ def main():
         "config": {"workload": w.name, "micro_batch": d.batch, "seq_len": d.seq,
                    "hidden": d.hidden, "heads": d.heads, "ffn": d.ffn, "t": d.t,
                    "rank": w.rank, "mask": d.mask, "gflop_per_step": flops / 1e9,
-                   "recompute": "fc1" if args.recompute else "none",
+                   "recompute": "fc1" if args.recompute else "none", "layout": args.layout,
                    "workspace_bytes": sh.ws_bytes},
         "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown,
     }

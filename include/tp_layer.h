@@ -114,6 +114,54 @@ enum { TP_ALL = 0, TP_FWD_ATTN = 1, TP_FWD_MLP = 2 };
 /* Backward phases (TP_ALL = 0 as above), split at the two f exchanges. */
 enum { TP_BWD_MLP = 1, TP_BWD_ATTN = 2, TP_BWD_LN1 = 3 };
 
+/* Sequence-parallel layout (opts->sequence_parallel = 1): the sequence
+ * parallelism that the megatron-core package description recommends with
+ * tensor parallelism (section "Tensor Parallelism (TP)"), applied to the f
+ * and g of "Megatron-LM: GPU-Cluster Training Parallelism", section "Paper 1:
+ * The f/g Conjugate Operators". Rank r owns the token rows
+ * [r*n/t, (r+1)*n/t) of the [n, h] token matrix ((batch*seq) % t == 0) for
+ * everything outside the tensor-parallel GEMMs and attention: both
+ * LayerNorms, the residual adds and the replicated biases b_o and b_fc2. In
+ * the [batch, seq, h] layout those rows are a contiguous block of tokens; in
+ * a [seq, batch, h] layout the same block is a slice of the sequence. Every
+ * g all-reduce becomes a reduce-scatter to those rows; every f becomes an
+ * all-gather of them. A gathered buffer is a caller-owned [n, h] tensor. A
+ * phase that produces rows writes only its own rows [r*n/t, (r+1)*n/t) into
+ * it; the all-gather fills the other ranks' rows; on one device the t ranks
+ * can share one gathered buffer and need no copy at all. A phase that
+ * consumes it reads all n rows. "act" is the internal dtype (fp16 for
+ * TP_DTYPE_BF16, fp32 for TP_DTYPE_F32).
+ * Forward, in order (reduce-scatters and all-gathers between them):
+ *   TP_FWD_SP_LN1 : x = this rank's rows of x            -> gathered rows = LN1 (act)
+ *   TP_FWD_SP_ATTN: gathered = all of LN1's output       -> out = fp32 [n, h] partial o @ W_o,r
+ *   TP_FWD_SP_LN2 : reduced = this rank's rows of the summed partial (fp32 [n/t, h]),
+ *                   x = this rank's rows of x            -> h_mid = reduced + b_o + x (kept),
+ *                                                           gathered rows = LN2(h_mid) (act)
+ *   TP_FWD_SP_MLP : gathered = all of LN2's output       -> out = fp32 [n, h] partial z @ W_fc2,r
+ *   TP_FWD_SP_OUT : reduced = this rank's rows of the summed partial
+ *                                                        -> out = reduced + b_fc2 + h_mid
+ *                                                           ([n/t, h], storage dtype)
+ * Backward, in order:
+ *   TP_BWD_SP_MLP : dout = this rank's rows of the output gradient, gathered_grad = all
+ *                   of it (storage dtype), gathered_act = the gathered LN2 output of the
+ *                   forward            -> partial = fp32 [n, h] du @ W_fc1,r^T; d_w_fc1,
+ *                                         d_b_fc1, d_w_fc2 and (this rank's rows) d_b_fc2
+ *   TP_BWD_SP_LN2 : dc = this rank's rows of the summed partial, dout as above
+ *                                      -> gathered_grad rows = dh (act; dh kept); d_ln2_*,
+ *                                         d_b_o over this rank's rows
+ *   TP_BWD_SP_ATTN: gathered_grad = all of dh, gathered_act = the gathered LN1 output
+ *                                      -> partial = fp32 [n, h] dqkv @ W_qkv,r^T; d_w_o,
+ *                                         d_w_qkv, d_b_qkv
+ *   TP_BWD_SP_LN1 : da = this rank's rows of the summed partial, x = this rank's rows
+ *                                      -> dx rows ([n/t, h]); d_ln1_* over this rank's rows
+ * Gradients of the replicated LayerNorm parameters and of b_o, b_fc2 cover
+ * this rank's rows only: their sum over the ranks is the full gradient. A
+ * handle in this layout accepts only these phases (TP_ERR_PHASE otherwise). */
+enum {
+  TP_FWD_SP_LN1 = 3, TP_FWD_SP_ATTN = 4, TP_FWD_SP_LN2 = 5, TP_FWD_SP_MLP = 6, TP_FWD_SP_OUT = 7
+};
+enum { TP_BWD_SP_MLP = 4, TP_BWD_SP_LN2 = 5, TP_BWD_SP_ATTN = 6, TP_BWD_SP_LN1 = 7 };
+
 typedef struct tp_layer tp_layer;
 
 typedef struct {
@@ -123,6 +171,7 @@ typedef struct {
                        value of a zeroed struct) or the layer's storage dtype */
   int scores;       /* TP_SCORES_AUTO (default), TP_SCORES_FP16 or TP_SCORES_SPLIT */
   int recompute;    /* TP_RECOMPUTE_NONE (default) or TP_RECOMPUTE_FC1 */
+  int sequence_parallel;  /* 0 (default) or 1: the TP_*_SP_* phases below */
 } tp_layer_opts;
 
 /* Parameters of rank r (shapes above) and, for TP_MASK_PADDING, the number
@@ -152,6 +201,9 @@ typedef struct {
   void *workspace;       /* tp_layer_create's workspace_bytes, same buffer for
                             the matching backward and untouched in between */
   size_t workspace_bytes;
+  const float *reduced;  /* sequence-parallel phases: this rank's rows of a summed
+                            fp32 partial, [n/t, h] */
+  void *gathered;        /* sequence-parallel phases: [n, h] act buffer (see above) */
 } tp_fwd_io;
 
 typedef struct {
@@ -180,6 +232,8 @@ typedef struct {
   int accumulate;        /* 0: overwrite the parameter gradients; 1: add to them */
   void *workspace;
   size_t workspace_bytes;
+  const void *gathered_act;  /* sequence-parallel phases: gathered LN output [n, h] act */
+  void *gathered_grad;       /* sequence-parallel phases: gathered gradient [n, h] */
 } tp_bwd_io;
 
 /* Create a handle for rank `rank` of a t-way split of a layer with hidden
@@ -189,7 +243,8 @@ typedef struct {
  *   opts: NULL for the defaults (eps 1e-5, exact-erf GeLU, fp32 dx, automatic
  *     score precision); opts->dx_dtype other than TP_DTYPE_F32 or `dtype`,
  *     an unknown opts->scores or opts->recompute, or TP_SCORES_SPLIT with
- *     TP_DTYPE_F32 are TP_ERR_UNSUPPORTED.
+ *     TP_DTYPE_F32 are TP_ERR_UNSUPPORTED; opts->sequence_parallel = 1 with
+ *     (micro_batch*seq) % t != 0 is TP_ERR_SHAPE.
  * Checks: every size > 0; hidden % heads == 0; heads % t == 0; ffn % t == 0;
  * (ffn/t) % 8 == 0; 0 <= rank < t; head dim in {32, 64, 96, 128, 160}
  * (TP_ERR_UNSUPPORTED otherwise). Allocates no device memory. On success

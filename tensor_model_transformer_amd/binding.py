@@ -29,6 +29,8 @@ ERROR_NAMES = {0: "TP_OK", -1: "TP_ERR_ARG", -2: "TP_ERR_SHAPE", -3: "TP_ERR_UNS
 TP_DTYPE_F32, TP_DTYPE_BF16 = 0, 1
 TP_SCORES_AUTO, TP_SCORES_FP16, TP_SCORES_SPLIT = 0, 1, 2
 TP_RECOMPUTE_NONE, TP_RECOMPUTE_FC1 = 0, 1
+TP_FWD_SP_LN1, TP_FWD_SP_ATTN, TP_FWD_SP_LN2, TP_FWD_SP_MLP, TP_FWD_SP_OUT = 3, 4, 5, 6, 7
+TP_BWD_SP_MLP, TP_BWD_SP_LN2, TP_BWD_SP_ATTN, TP_BWD_SP_LN1 = 4, 5, 6, 7
 TP_MASK_CAUSAL, TP_MASK_PADDING = 0, 1
 TP_GELU_ERF, TP_GELU_TANH = 0, 1
 TP_ALL, TP_FWD_ATTN, TP_FWD_MLP = 0, 1, 2
@@ -48,7 +50,7 @@ KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce")
 
 class tp_layer_opts(Structure):
     _fields_ = [("ln_eps", c_float), ("gelu", c_int), ("dx_dtype", c_int), ("scores", c_int),
-                ("recompute", c_int)]
+                ("recompute", c_int), ("sequence_parallel", c_int)]
 
 
 class tp_params(Structure):
@@ -57,14 +59,16 @@ class tp_params(Structure):
 
 class tp_fwd_io(Structure):
     _fields_ = [("params", POINTER(tp_params)), ("x", c_void_p), ("h_mid", c_void_p),
-                ("out", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
+                ("out", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+                ("reduced", c_void_p), ("gathered", c_void_p)]
 
 
 class tp_bwd_io(Structure):
     _fields_ = ([("params", POINTER(tp_params)), ("x", c_void_p), ("dout", c_void_p),
                  ("dc", c_void_p), ("da", c_void_p), ("partial", c_void_p), ("dx", c_void_p)]
                 + [(f, c_void_p) for f in GRAD_FIELDS]
-                + [("accumulate", c_int), ("workspace", c_void_p), ("workspace_bytes", c_size_t)])
+                + [("accumulate", c_int), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+                   ("gathered_act", c_void_p), ("gathered_grad", c_void_p)])
 
 
 _lib = None
@@ -112,7 +116,8 @@ def tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, 
         o = ctypes.byref(tp_layer_opts(float(opts.get("ln_eps", 1e-5)), int(opts.get("gelu", 0)),
                                        int(opts.get("dx_dtype", TP_DTYPE_F32)),
                                        int(opts.get("scores", TP_SCORES_AUTO)),
-                                       int(opts.get("recompute", TP_RECOMPUTE_NONE))))
+                                       int(opts.get("recompute", TP_RECOMPUTE_NONE)),
+                                       int(opts.get("sequence_parallel", 0))))
     rc = lib().tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, o,
                                ctypes.byref(h), ctypes.byref(ws))
     return rc, h.value, ws.value

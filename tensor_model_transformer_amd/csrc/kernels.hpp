@@ -40,6 +40,12 @@ int ln_bwd_blocks(int rows, int h, int* rows_per_blk);
 hipError_t colsum_partial(int y_dtype, const void* y, int rows, int cols, int ld,
                           float* part, int rows_per_blk, hipStream_t s);
 int colsum_blocks(int rows, int cols, int* rows_per_blk);
+// out[rows, h] = a (fp32) + bias[h] + r; dtypes DT_F32 / DT_BF16 as listed in
+// norm.hip (fp32 bias/r/out, or bf16 bias with bf16 r -> fp32 out, or bf16
+// bias with fp32 r -> bf16 out).
+hipError_t residual_add(const float* a, int bias_dtype, const void* bias, int r_dtype,
+                        const void* r, int out_dtype, void* out, int rows, int h,
+                        hipStream_t s);
 
 // out_k[j] (+)= sum_b part[b][k][j] for k < nout (part is [nblk][nout][width]).
 // The buffer must hold reduce_scratch_floats(nblk, nout, width) floats: the

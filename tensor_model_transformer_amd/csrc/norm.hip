@@ -393,4 +393,45 @@ hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts, int
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------
+// out = a + bias (per column) + r over a [rows, h] block: the bias and
+// residual that the sequence-parallel layout adds after a reduce-scatter.
+// a is fp32; bias, r and out take the dtype codes. 8 elements per thread.
+// ----------------------------------------------------------------------------
+template <typename TB, typename TR, typename TO>
+__global__ __launch_bounds__(256) void residual_add_kernel(const float* __restrict__ a,
+                                                           const TB* __restrict__ bias,
+                                                           const TR* __restrict__ r,
+                                                           TO* __restrict__ out, size_t nvec,
+                                                           int h) {
+  const size_t j = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= nvec) return;
+  const int col = (int)((8 * j) % (size_t)h);
+  float v[8], b[8], x[8];
+  Vec8<float>::load(a + 8 * j, v);
+  Vec8<TB>::load(bias + col, b);
+  Vec8<TR>::load(r + 8 * j, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] += b[e] + x[e];
+  Vec8<TO>::store(out + 8 * j, v);
+}
+
+hipError_t residual_add(const float* a, int bias_dtype, const void* bias, int r_dtype,
+                        const void* r, int out_dtype, void* out, int rows, int h,
+                        hipStream_t s) {
+  if (h % 8) return hipErrorInvalidValue;
+  const size_t nvec = (size_t)rows * h / 8;
+  if (!nvec) return hipSuccess;
+  const unsigned grid = (unsigned)((nvec + 255) / 256);
+#define TPL_RA(TB, TR, TO)                                                                  \
+  residual_add_kernel<TB, TR, TO><<<grid, 256, 0, s>>>(a, (const TB*)bias, (const TR*)r,  \
+                                                       (TO*)out, nvec, h);                 \
+  return hipGetLastError();
+  if (bias_dtype == DT_F32 && r_dtype == DT_F32 && out_dtype == DT_F32) { TPL_RA(float, float, float) }
+  if (bias_dtype == DT_BF16 && r_dtype == DT_BF16 && out_dtype == DT_F32) { TPL_RA(bf16, bf16, float) }
+  if (bias_dtype == DT_BF16 && r_dtype == DT_F32 && out_dtype == DT_BF16) { TPL_RA(bf16, float, bf16) }
+#undef TPL_RA
+  return hipErrorInvalidValue;
+}
+
 }  // namespace tpl

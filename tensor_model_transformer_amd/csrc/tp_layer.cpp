@@ -59,6 +59,8 @@ struct tp_layer {
   bool dx_f32;  // dx written in fp32 (else in the storage dtype)
   bool split_scores;  // qkv also kept as fp16 residuals; scores from three products
   bool recompute_fc1;  // FC1 pre-activation recomputed in backward, not kept
+  bool sp;             // sequence-parallel layout (phases TP_*_SP_*)
+  int nc;              // rows of this rank's token chunk in that layout (n / t)
   // derived
   int n, dh, Hl, hl, fl, esz;
   int sdt;   // storage type at the boundary (x, params, out, dx): DT_BF16 or DT_F32
@@ -270,19 +272,21 @@ int run_gemm(tp_layer* L, const GemmArgs& g, hipStream_t s) {
 
 // ---- forward pieces --------------------------------------------------------
 // x -> a -> qkv -> o -> (o @ W_o) [+ b_o + x] into `dst` (fp32 [n, h]).
+// With a_in (the sequence-parallel layout) LN1 has run per chunk already and
+// a_in is the gathered [n, h] LayerNorm output.
 int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool designated,
-             void* ws, hipStream_t s) {
+             void* ws, hipStream_t s, const void* a_in = nullptr) {
   const int n = L->n, h = L->hidden, hl = L->hl;
   int e;
   const double nh = (double)n * h;
-  {
+  if (!a_in) {
   Scope ps(L, s, TP_K_LN_FWD, 0, nh * 2 * L->esz + 8.0 * n);
   HIP_TRY(ln_fwd(L->sdt, L->sdt, L->adt, x, p->ln1_gamma, p->ln1_beta, at<void>(ws, L->a),
                  at<float>(ws, L->mean1), at<float>(ws, L->rstd1), nullptr, n, h, L->eps, s));
   }
   GemmArgs g = gemm_base(L);
   g.M = n; g.N = 3 * hl; g.K = h;
-  g.A = at<void>(ws, L->a); g.lda = h; g.a_kmajor = 1;
+  g.A = a_in ? a_in : at<void>(ws, L->a); g.lda = h; g.a_kmajor = 1;
   g.B = p->w_qkv; g.ldb = 3 * hl; g.b_kmajor = 0; g.b_dtype = L->sdt;
   g.bias = p->b_qkv;
   g.C = at<void>(ws, L->qkv); g.ldc = 3 * hl;
@@ -312,12 +316,14 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
 }
 
 // h_mid (fp32) -> c -> u, z -> (z @ W_fc2) [+ b_fc2 + h_mid] into `out`.
+// With c_in (sequence-parallel layout) LN2 has run per chunk already and c_in
+// is the gathered [n, h] LayerNorm output.
 int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, int out_f32,
-            bool designated, void* ws, hipStream_t s) {
+            bool designated, void* ws, hipStream_t s, const void* c_in = nullptr) {
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
   float* h_mid = at<float>(ws, L->h_mid);
-  {
+  if (!c_in) {
   Scope ps(L, s, TP_K_LN_FWD, 0,
            (double)n * h * (4 + L->esz + (h_mid_in == h_mid ? 0 : 4)) + 8.0 * n);
   HIP_TRY(ln_fwd(DT_F32, L->sdt, L->adt, h_mid_in, p->ln2_gamma, p->ln2_beta, at<void>(ws, L->c),
@@ -326,7 +332,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   }
   GemmArgs g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
-  g.A = at<void>(ws, L->c); g.lda = h; g.a_kmajor = 1;
+  g.A = c_in ? c_in : at<void>(ws, L->c); g.lda = h; g.a_kmajor = 1;
   g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 0; g.b_dtype = L->sdt;
   g.bias = p->b_fc1;
   g.epi = EPI_BIAS_GELU;
@@ -349,12 +355,13 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
 // ---- backward pieces -------------------------------------------------------
 // Bias gradient: out (+)= column sums of y [n, cols] (two-stage, deterministic).
 int bias_grad(tp_layer* L, const void* y, int y_dtype, int cols, float* out, int accumulate,
-              void* ws, hipStream_t s) {
-  Scope ps(L, s, TP_K_REDUCE, 0, (double)L->n * cols * L->esz + 4.0 * cols);
+              void* ws, hipStream_t s, int rows = -1) {
+  if (rows < 0) rows = L->n;
+  Scope ps(L, s, TP_K_REDUCE, 0, (double)rows * cols * L->esz + 4.0 * cols);
   float* part = at<float>(ws, L->part);
   int rpb;
-  const int nb = colsum_blocks(L->n, cols, &rpb);
-  HIP_TRY(colsum_partial(y_dtype, y, L->n, cols, cols, part, rpb, s));
+  const int nb = colsum_blocks(rows, cols, &rpb);
+  HIP_TRY(colsum_partial(y_dtype, y, rows, cols, cols, part, rpb, s));
   HIP_TRY(reduce_partials(part, nb, 1, cols, out, nullptr, nullptr, accumulate, s));
   return TP_OK;
 }
@@ -364,8 +371,8 @@ int bias_grad(tp_layer* L, const void* y, int y_dtype, int cols, float* out, int
 int ln_backward(tp_layer* L, const float* dy, int x_dtype, const void* x, const float* mean,
                 const float* rstd, const void* gamma, int dres_dtype, const void* dres,
                 float* dx_f32, int st_dtype, void* dx_st, float* dgamma, float* dbeta,
-                float* dsum, int accumulate, void* ws, hipStream_t s) {
-  const int n = L->n, h = L->hidden;
+                float* dsum, int accumulate, void* ws, hipStream_t s, int rows = -1) {
+  const int n = rows < 0 ? L->n : rows, h = L->hidden;
   float* part = at<float>(ws, L->part);
   int rpb;
   const int nb = ln_bwd_blocks(n, h, &rpb);
@@ -382,17 +389,23 @@ int ln_backward(tp_layer* L, const float* dy, int x_dtype, const void* x, const 
 }
 
 // dout -> du, dW2, db2, dA, db1, dc (fp32 into `dc_out`).
+// Sequence-parallel layout: dout_full is the gathered [n, h] upstream
+// gradient, c_in the gathered LN2 output, and io->dout this rank's chunk of
+// db2_rows rows (the replicated bias b2 was added per chunk).
 int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out, void* ws,
-            hipStream_t s) {
+            hipStream_t s, const void* dout_full = nullptr, const void* c_in = nullptr,
+            int db2_rows = -1) {
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
+  const void* dout = dout_full ? dout_full : io->dout;
+  const void* c_act = c_in ? c_in : at<void>(ws, L->c);
   float* skw = at<float>(ws, L->splitk);
   GemmArgs g;
   if (L->recompute_fc1) {
     // u = c @ W_fc1,r + b_fc1,r again, straight into the du buffer
     g = gemm_base(L);
     g.M = n; g.N = fl; g.K = h;
-    g.A = at<void>(ws, L->c); g.lda = h; g.a_kmajor = 1;
+    g.A = c_act; g.lda = h; g.a_kmajor = 1;
     g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 0; g.b_dtype = L->sdt;
     g.bias = p->b_fc1;
     g.C = at<void>(ws, L->du); g.ldc = fl;
@@ -403,18 +416,19 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   // same thread of the epilogue)
   g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
-  g.A = io->dout; g.lda = h; g.a_kmajor = 1; g.a_dtype = L->sdt;
+  g.A = dout; g.lda = h; g.a_kmajor = 1; g.a_dtype = L->sdt;
   g.B = p->w_fc2; g.ldb = h; g.b_kmajor = 1; g.b_dtype = L->sdt;
   g.epi = EPI_DGELU;
   g.aux = at<void>(ws, L->recompute_fc1 ? L->du : L->u); g.ldaux = fl;
   g.C = at<void>(ws, L->du); g.ldc = fl;
   if ((e = run_gemm(L, g, s))) return e;
-  if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s))) return e;
-  g = wgrad_args(L, fl, h, at<void>(ws, L->z), io->dout, io->d_w_fc2, io->accumulate);
+  if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s, db2_rows)))
+    return e;
+  g = wgrad_args(L, fl, h, at<void>(ws, L->z), dout, io->d_w_fc2, io->accumulate);
   g.b_dtype = L->sdt;
   g.split = L->split_w2; g.ws = skw;
   if ((e = run_gemm(L, g, s))) return e;
-  g = wgrad_args(L, h, fl, at<void>(ws, L->c), at<void>(ws, L->du), io->d_w_fc1, io->accumulate);
+  g = wgrad_args(L, h, fl, c_act, at<void>(ws, L->du), io->d_w_fc1, io->accumulate);
   g.split = L->split_w1; g.ws = skw;
   if ((e = run_gemm(L, g, s))) return e;
   if ((e = bias_grad(L, at<void>(ws, L->du), L->adt, fl, io->d_b_fc1, io->accumulate, ws, s)))
@@ -429,23 +443,30 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
 
 // dc (summed) -> dh, LN2 grads, db_o -> dW_o, do -> attention -> dqkv ->
 // dW_qkv, db_qkv -> da (fp32 into `da_out`).
+// Sequence-parallel layout: LN2's backward has run per chunk already; dh_in
+// is the gathered [n, h] residual-stream gradient (internal dtype) and a_in
+// the gathered LN1 output.
 int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* dc,
-             float* da_out, void* ws, hipStream_t s) {
+             float* da_out, void* ws, hipStream_t s, const void* dh_in = nullptr,
+             const void* a_in = nullptr) {
   const int n = L->n, h = L->hidden, hl = L->hl;
   int e;
   float* skw = at<float>(ws, L->splitk);
-  if ((e = ln_backward(L, dc, DT_F32, at<void>(ws, L->h_mid), at<float>(ws, L->mean2),
+  if (!dh_in &&
+      (e = ln_backward(L, dc, DT_F32, at<void>(ws, L->h_mid), at<float>(ws, L->mean2),
                        at<float>(ws, L->rstd2), p->ln2_gamma, L->sdt, io->dout,
                        at<float>(ws, L->dh_f), L->adt, at<void>(ws, L->dh_s), io->d_ln2_gamma,
                        io->d_ln2_beta, io->d_b_o, io->accumulate, ws, s)))
     return e;
+  const void* dh_s = dh_in ? dh_in : at<void>(ws, L->dh_s);
+  const void* a_act = a_in ? a_in : at<void>(ws, L->a);
   GemmArgs g = gemm_base(L);
   g.M = n; g.N = hl; g.K = h;
-  g.A = at<void>(ws, L->dh_s); g.lda = h; g.a_kmajor = 1;
+  g.A = dh_s; g.lda = h; g.a_kmajor = 1;
   g.B = p->w_o; g.ldb = h; g.b_kmajor = 1; g.b_dtype = L->sdt;
   g.C = at<void>(ws, L->dO); g.ldc = hl;
   if ((e = run_gemm(L, g, s))) return e;
-  g = wgrad_args(L, hl, h, at<void>(ws, L->o), at<void>(ws, L->dh_s), io->d_w_o, io->accumulate);
+  g = wgrad_args(L, hl, h, at<void>(ws, L->o), dh_s, io->d_w_o, io->accumulate);
   g.split = L->split_wo; g.ws = skw;
   if ((e = run_gemm(L, g, s))) return e;
   {
@@ -456,8 +477,7 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
                      at<float>(ws, L->lse2), at<float>(ws, L->delta), at<void>(ws, L->dqkv),
                      p->valid_len, L->batch, L->seq, L->Hl, L->dh, L->mask, s));
   }
-  g = wgrad_args(L, h, 3 * hl, at<void>(ws, L->a), at<void>(ws, L->dqkv), io->d_w_qkv,
-                 io->accumulate);
+  g = wgrad_args(L, h, 3 * hl, a_act, at<void>(ws, L->dqkv), io->d_w_qkv, io->accumulate);
   g.split = L->split_wqkv; g.ws = skw;
   if ((e = run_gemm(L, g, s))) return e;
   if ((e = bias_grad(L, at<void>(ws, L->dqkv), L->adt, 3 * hl, io->d_b_qkv, io->accumulate, ws,
@@ -479,6 +499,89 @@ int bwd_ln1(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* d
   return ln_backward(L, da, L->sdt, io->x, at<float>(ws, L->mean1), at<float>(ws, L->rstd1),
                      p->ln1_gamma, DT_F32, at<void>(ws, L->dh_f), dx32, L->sdt, dxst,
                      io->d_ln1_gamma, io->d_ln1_beta, nullptr, io->accumulate, ws, s);
+}
+
+// ---- sequence-parallel phases ------------------------------------------------
+// Rank r owns the token rows [r*nc, (r+1)*nc) of the [n, h] token matrix for
+// LayerNorm, bias and residual. The all-gather before each column-parallel
+// GEMM is this rank writing its rows into the caller's gathered buffer (the
+// collective fills the other ranks' rows); the reduce-scatter after each
+// row-parallel GEMM hands back this rank's rows of the summed partial.
+char* chunk_rows(void* base, const tp_layer* L) {
+  return static_cast<char*>(base) + (size_t)L->rank * L->nc * L->hidden * L->esz;
+}
+
+int fwd_sp(tp_layer* L, int phase, const tp_params* p, const tp_fwd_io* io, void* ws,
+           hipStream_t s) {
+  const int nc = L->nc, h = L->hidden;
+  int e;
+  float* h_mid = at<float>(ws, L->h_mid);  // first nc rows: this rank's chunk
+  switch (phase) {
+    case TP_FWD_SP_LN1: {
+      if ((e = check_ptrs({io->x, io->gathered}))) return e;
+      Scope ps(L, s, TP_K_LN_FWD, 0, (double)nc * h * 2 * L->esz + 8.0 * nc);
+      HIP_TRY(ln_fwd(L->sdt, L->sdt, L->adt, io->x, p->ln1_gamma, p->ln1_beta,
+                     chunk_rows(io->gathered, L), at<float>(ws, L->mean1),
+                     at<float>(ws, L->rstd1), nullptr, nc, h, L->eps, s));
+      return TP_OK;
+    }
+    case TP_FWD_SP_ATTN:
+      if ((e = check_ptrs({io->gathered, io->out}))) return e;
+      return fwd_attn(L, p, nullptr, static_cast<float*>(io->out), false, ws, s, io->gathered);
+    case TP_FWD_SP_LN2: {
+      if ((e = check_ptrs({io->reduced, io->x, io->gathered}))) return e;
+      Scope ps(L, s, TP_K_LN_FWD, 0, (double)nc * h * (4 + L->esz + 4 + 4 + L->esz) + 8.0 * nc);
+      HIP_TRY(residual_add(io->reduced, L->sdt, p->b_o, L->sdt, io->x, DT_F32, h_mid, nc, h, s));
+      HIP_TRY(ln_fwd(DT_F32, L->sdt, L->adt, h_mid, p->ln2_gamma, p->ln2_beta,
+                     chunk_rows(io->gathered, L), at<float>(ws, L->mean2),
+                     at<float>(ws, L->rstd2), nullptr, nc, h, L->eps, s));
+      return TP_OK;
+    }
+    case TP_FWD_SP_MLP:
+      if ((e = check_ptrs({io->gathered, io->out}))) return e;
+      return fwd_mlp(L, p, nullptr, io->out, 1, false, ws, s, io->gathered);
+    default: {  // TP_FWD_SP_OUT
+      if ((e = check_ptrs({io->reduced, io->out}))) return e;
+      Scope ps(L, s, TP_K_LN_FWD, 0, (double)nc * h * (4 + 4 + L->esz));
+      HIP_TRY(residual_add(io->reduced, L->sdt, p->b_fc2, DT_F32, h_mid, L->sdt, io->out, nc, h,
+                           s));
+      return TP_OK;
+    }
+  }
+}
+
+int bwd_sp(tp_layer* L, int phase, const tp_params* p, const tp_bwd_io* io, void* ws,
+           hipStream_t s) {
+  const int nc = L->nc;
+  int e;
+  switch (phase) {
+    case TP_BWD_SP_MLP:
+      if ((e = check_ptrs({io->dout, io->gathered_grad, io->gathered_act, io->partial,
+                           io->d_w_fc1, io->d_b_fc1, io->d_w_fc2, io->d_b_fc2})))
+        return e;
+      return bwd_mlp(L, p, io, io->partial, ws, s, io->gathered_grad, io->gathered_act, nc);
+    case TP_BWD_SP_LN2:
+      if ((e = check_ptrs({io->dc, io->dout, io->gathered_grad, io->d_ln2_gamma, io->d_ln2_beta,
+                           io->d_b_o})))
+        return e;
+      return ln_backward(L, io->dc, DT_F32, at<void>(ws, L->h_mid), at<float>(ws, L->mean2),
+                         at<float>(ws, L->rstd2), p->ln2_gamma, L->sdt, io->dout,
+                         at<float>(ws, L->dh_f), L->adt, chunk_rows(io->gathered_grad, L),
+                         io->d_ln2_gamma, io->d_ln2_beta, io->d_b_o, io->accumulate, ws, s, nc);
+    case TP_BWD_SP_ATTN:
+      if ((e = check_ptrs({io->gathered_grad, io->gathered_act, io->partial, io->d_w_qkv,
+                           io->d_b_qkv, io->d_w_o})))
+        return e;
+      return bwd_attn(L, p, io, nullptr, io->partial, ws, s, io->gathered_grad, io->gathered_act);
+    default: {  // TP_BWD_SP_LN1
+      if ((e = check_ptrs({io->x, io->da, io->dx, io->d_ln1_gamma, io->d_ln1_beta}))) return e;
+      float* dx32 = L->dx_f32 ? static_cast<float*>(io->dx) : nullptr;
+      void* dxst = L->dx_f32 ? nullptr : io->dx;
+      return ln_backward(L, io->da, L->sdt, io->x, at<float>(ws, L->mean1), at<float>(ws, L->rstd1),
+                         p->ln1_gamma, DT_F32, at<void>(ws, L->dh_f), dx32, L->sdt, dxst,
+                         io->d_ln1_gamma, io->d_ln1_beta, nullptr, io->accumulate, ws, s, nc);
+    }
+  }
 }
 
 void prof_fold(Prof& p) {
@@ -522,12 +625,14 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   int dx_dtype = TP_DTYPE_F32;
   int scores = TP_SCORES_AUTO;
   int recompute = TP_RECOMPUTE_NONE;
+  int seq_par = 0;
   if (opts) {
     eps = opts->ln_eps;
     gelu = opts->gelu;
     dx_dtype = opts->dx_dtype;
     scores = opts->scores;
     recompute = opts->recompute;
+    seq_par = opts->sequence_parallel;
     if (!(eps > 0.f)) return TP_ERR_ARG;
     if (gelu != TP_GELU_ERF && gelu != TP_GELU_TANH) return TP_ERR_UNSUPPORTED;
     if (dx_dtype != TP_DTYPE_F32 && dx_dtype != dtype) return TP_ERR_UNSUPPORTED;
@@ -535,6 +640,8 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
       return TP_ERR_UNSUPPORTED;
     if (scores == TP_SCORES_SPLIT && dtype != TP_DTYPE_BF16) return TP_ERR_UNSUPPORTED;
     if (recompute != TP_RECOMPUTE_NONE && recompute != TP_RECOMPUTE_FC1) return TP_ERR_UNSUPPORTED;
+    if (seq_par != 0 && seq_par != 1) return TP_ERR_UNSUPPORTED;
+    if (seq_par && n % t) return TP_ERR_SHAPE;
   }
   tp_layer* L = new (std::nothrow) tp_layer();
   if (!L) return TP_ERR_ARG;
@@ -543,6 +650,8 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   L->eps = eps; L->gelu_tanh = gelu == TP_GELU_TANH;
   L->dx_f32 = dx_dtype == TP_DTYPE_F32;
   L->recompute_fc1 = recompute == TP_RECOMPUTE_FC1;
+  L->sp = seq_par == 1;
+  L->nc = (int)(n / t);
   L->split_scores = dtype == TP_DTYPE_BF16 &&
                     (scores == TP_SCORES_SPLIT ||
                      (scores == TP_SCORES_AUTO && hidden >= kSplitScoresHidden));
@@ -559,7 +668,9 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
 
 int tp_layer_fwd(tp_layer* L, int phase, const tp_fwd_io* io, void* hip_stream) {
   if (!L || !io) return TP_ERR_ARG;
-  if (phase < TP_ALL || phase > TP_FWD_MLP) return TP_ERR_PHASE;
+  if (L->sp ? (phase < TP_FWD_SP_LN1 || phase > TP_FWD_SP_OUT)
+            : (phase < TP_ALL || phase > TP_FWD_MLP))
+    return TP_ERR_PHASE;
   int e = check_params(L, io->params);
   if (e) return e;
   if ((e = check_ws(L, io->workspace, io->workspace_bytes))) return e;
@@ -575,15 +686,19 @@ int tp_layer_fwd(tp_layer* L, int phase, const tp_fwd_io* io, void* hip_stream) 
     case TP_FWD_ATTN:
       if ((e = check_ptrs({io->x, io->out}))) return e;
       return fwd_attn(L, p, io->x, (float*)io->out, designated, ws, s);
-    default:
+    case TP_FWD_MLP:
       if ((e = check_ptrs({io->h_mid, io->out}))) return e;
       return fwd_mlp(L, p, io->h_mid, io->out, 1, designated, ws, s);
+    default:
+      return fwd_sp(L, phase, p, io, ws, s);
   }
 }
 
 int tp_layer_bwd(tp_layer* L, int phase, const tp_bwd_io* io, void* hip_stream) {
   if (!L || !io) return TP_ERR_ARG;
-  if (phase < TP_ALL || phase > TP_BWD_LN1) return TP_ERR_PHASE;
+  if (L->sp ? (phase < TP_BWD_SP_MLP || phase > TP_BWD_SP_LN1)
+            : (phase < TP_ALL || phase > TP_BWD_LN1))
+    return TP_ERR_PHASE;
   int e = check_params(L, io->params);
   if (e) return e;
   if ((e = check_ws(L, io->workspace, io->workspace_bytes))) return e;
@@ -609,9 +724,11 @@ int tp_layer_bwd(tp_layer* L, int phase, const tp_bwd_io* io, void* hip_stream) 
                            io->d_b_o, io->d_ln2_gamma, io->d_ln2_beta})))
         return e;
       return bwd_attn(L, p, io, io->dc, io->partial, ws, s);
-    default:
+    case TP_BWD_LN1:
       if ((e = check_ptrs({io->x, io->da, io->dx, io->d_ln1_gamma, io->d_ln1_beta}))) return e;
       return bwd_ln1(L, p, io, io->da, ws, s);
+    default:
+      return bwd_sp(L, phase, p, io, ws, s);
   }
 }
 

@@ -40,7 +40,7 @@ class Shard:
 
     def __init__(self, dims: LayerDims, rank: int, device="cuda:0", gelu: int = B.TP_GELU_ERF,
                  eps: float = 1e-5, dx_fp32: bool = True, scores: int = B.TP_SCORES_AUTO,
-                 recompute: int = B.TP_RECOMPUTE_NONE):
+                 recompute: int = B.TP_RECOMPUTE_NONE, sequence_parallel: bool = False):
         self.dims = dims
         self.rank = rank
         self.device = torch.device(device)
@@ -51,7 +51,8 @@ class Shard:
             B.TP_MASK_PADDING if dims.mask == "padding" else B.TP_MASK_CAUSAL,
             {"ln_eps": eps, "gelu": gelu,
              "dx_dtype": B.TP_DTYPE_F32 if dx_fp32 or dims.dtype == "f32" else B.TP_DTYPE_BF16,
-             "scores": scores, "recompute": recompute})
+             "scores": scores, "recompute": recompute,
+             "sequence_parallel": int(sequence_parallel)})
         self.dx_fp32 = dx_fp32
         _check("tp_layer_create", rc)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
@@ -99,23 +100,28 @@ class Shard:
     def stream(self) -> int:
         return torch.cuda.current_stream(self.device).cuda_stream
 
-    def fwd(self, p: "DeviceParams", out: torch.Tensor, x: Optional[torch.Tensor] = None,
-            h_mid: Optional[torch.Tensor] = None, phase: int = B.TP_ALL) -> int:
+    def fwd(self, p: "DeviceParams", out: Optional[torch.Tensor], x: Optional[torch.Tensor] = None,
+            h_mid: Optional[torch.Tensor] = None, phase: int = B.TP_ALL,
+            reduced: Optional[torch.Tensor] = None, gathered: Optional[torch.Tensor] = None) -> int:
         io = B.tp_fwd_io()
         io.params = p.ptr()
         io.x = x.data_ptr() if x is not None else None
         io.h_mid = h_mid.data_ptr() if h_mid is not None else None
-        io.out = out.data_ptr()
+        io.out = out.data_ptr() if out is not None else None
+        io.reduced = reduced.data_ptr() if reduced is not None else None
+        io.gathered = gathered.data_ptr() if gathered is not None else None
         io.workspace = self.ws.data_ptr()
         io.workspace_bytes = self.ws_bytes
         return B.tp_layer_fwd(self.handle, phase, io, self.stream())
 
     def bwd(self, p: "DeviceParams", grads: Dict[str, torch.Tensor], x=None, dout=None, dx=None,
-            dc=None, da=None, partial=None, accumulate=0, phase: int = B.TP_ALL) -> int:
+            dc=None, da=None, partial=None, accumulate=0, phase: int = B.TP_ALL,
+            gathered_act=None, gathered_grad=None) -> int:
         io = B.tp_bwd_io()
         io.params = p.ptr()
         for name, t in (("x", x), ("dout", dout), ("dx", dx), ("dc", dc), ("da", da),
-                        ("partial", partial)):
+                        ("partial", partial), ("gathered_act", gathered_act),
+                        ("gathered_grad", gathered_grad)):
             setattr(io, name, t.data_ptr() if t is not None else None)
         for k in PARAM_NAMES:
             g = grads.get(k) if grads is not None else None

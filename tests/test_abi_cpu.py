@@ -74,6 +74,8 @@ def create(**kw):
     (dict(dtype=B.TP_DTYPE_F32, opts={"dx_dtype": B.TP_DTYPE_BF16}), B.TP_ERR_UNSUPPORTED),
     (dict(opts={"scores": 3}), B.TP_ERR_UNSUPPORTED),
     (dict(opts={"recompute": 2}), B.TP_ERR_UNSUPPORTED),
+    (dict(opts={"sequence_parallel": 2}), B.TP_ERR_UNSUPPORTED),
+    (dict(seq=63, micro_batch=1, opts={"sequence_parallel": 1}), B.TP_ERR_SHAPE),  # n % t
     (dict(dtype=B.TP_DTYPE_F32, opts={"scores": B.TP_SCORES_SPLIT}), B.TP_ERR_UNSUPPORTED),
 ])
 def test_create_validation(lib, kw, code):
@@ -134,6 +136,27 @@ def test_recompute_fc1_workspace(lib):
     assert B.tp_layer_tap(h0, B.TAPS["u"])[0] == B.TP_OK
     B.tp_layer_destroy(h0)
     B.tp_layer_destroy(h1)
+
+
+def test_sequence_parallel_phases_are_separate(lib):
+    # a handle in the sequence-parallel layout takes only the TP_*_SP_* phases,
+    # and the ordinary handle none of them; the phase is checked before
+    # anything touches a device
+    rc, hs, ws = create(opts={"sequence_parallel": 1})
+    assert rc == B.TP_OK
+    rc, hn, _ = create()
+    assert rc == B.TP_OK
+    fio, bio = B.tp_fwd_io(), B.tp_bwd_io()
+    for ph in (B.TP_ALL, 1, 2):
+        assert B.tp_layer_fwd(hs, ph, fio) == B.TP_ERR_PHASE
+    for ph in (B.TP_FWD_SP_LN1, B.TP_FWD_SP_OUT, 8):
+        assert B.tp_layer_fwd(hn, ph, fio) == B.TP_ERR_PHASE
+    for ph in (B.TP_ALL, 1, 2, 3):
+        assert B.tp_layer_bwd(hs, ph, bio) == B.TP_ERR_PHASE
+    for ph in (B.TP_BWD_SP_MLP, B.TP_BWD_SP_LN1):
+        assert B.tp_layer_bwd(hn, ph, bio) == B.TP_ERR_PHASE
+    B.tp_layer_destroy(hs)
+    B.tp_layer_destroy(hn)
 
 
 def test_call_argument_errors_need_no_device(lib):
