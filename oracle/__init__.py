@@ -8,4 +8,5 @@ Modules:
   layer  -- the layer definition in NumPy fp64 (LOCAL, FULL, PARTIALS modes)
   brute  -- pure-Python loop forward of the same layer (independent pin)
   fd     -- central finite differences of loss = sum(out * dout)
+  decode -- one decode step against a per-rank KV cache shard
 """

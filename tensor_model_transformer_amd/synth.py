@@ -36,6 +36,7 @@ REPLICATED = 0xFFFF
 # Stable ids; never renumber (they are part of the seed).
 TENSOR_IDS = {
     "x": 1, "dout": 2, "valid_len": 3,
+    "x_new": 4, "k_cache": 5, "v_cache": 6, "positions": 7,
     "ln1_gamma": 10, "ln1_beta": 11, "ln2_gamma": 12, "ln2_beta": 13,
     "w_qkv": 20, "b_qkv": 21, "w_o": 22, "b_o": 23,
     "w_fc1": 24, "b_fc1": 25, "w_fc2": 26, "b_fc2": 27,
@@ -229,3 +230,56 @@ def layer_inputs(w: Workload):
     else:
         valid = np.full(d.batch, d.seq, dtype=np.int32)
     return x, dout, valid
+
+
+# ----------------------------------------------------------------------------
+# Decode-step inputs: one new token per sequence against a KV cache
+# ----------------------------------------------------------------------------
+def round_to_fp16(a: np.ndarray) -> np.ndarray:
+    """Nearest IEEE half value (ties to even), returned as float32."""
+    return a.astype(np.float16).astype(np.float32)
+
+
+def kv_std(w: Workload) -> float:
+    """Spread of the cached K and V values: a unit-variance LayerNorm output
+    times a weight column of ``hidden`` N(0, weight_std^2) entries."""
+    return float(w.weight_std * np.sqrt(w.dims.hidden))
+
+
+def rank_caches(w: Workload, rank: int, cache_len: int):
+    """K and V caches of rank ``rank``: [batch, H_l, cache_len, dh] each, float32 on
+    the grid of the layer's internal activation type (fp16 for bf16 storage).
+    The unsharded cache is the concatenation of the rank caches over heads."""
+    d = w.dims
+    shape = (d.batch, d.heads_local, cache_len, d.head_dim)
+    out = []
+    for name in ("k_cache", "v_cache"):
+        a = _rng(w.seed, name, rank).standard_normal(shape, dtype=np.float32)
+        a *= np.float32(kv_std(w))
+        out.append(round_to_fp16(a) if d.dtype == "bf16" else a)
+    return out[0], out[1]
+
+
+def full_caches(w: Workload, cache_len: int):
+    per = [rank_caches(w, r, cache_len) for r in range(w.dims.t)]
+    return (np.concatenate([k for k, _ in per], axis=1),
+            np.concatenate([v for _, v in per], axis=1))
+
+
+def decode_inputs(w: Workload, cache_len: int, positions: str = "ragged"):
+    """x_new [batch, h] (N(0,1) on the storage grid) and the position of each
+    sequence's new token (int32 [batch]): "full" puts every token at
+    cache_len - 1, "empty" at 0, "ragged" draws U{0..cache_len-1} with the
+    first sequence at 0 and the last at cache_len - 1."""
+    d = w.dims
+    x = _normal(w.seed, "x_new", REPLICATED, (d.batch, d.hidden), 1.0, 0.0, d.dtype)
+    if positions == "full":
+        pos = np.full(d.batch, cache_len - 1)
+    elif positions == "empty":
+        pos = np.zeros(d.batch)
+    else:
+        pos = _rng(w.seed, "positions", REPLICATED).integers(0, cache_len, size=d.batch)
+        pos[0] = 0
+        if d.batch > 1:
+            pos[-1] = cache_len - 1
+    return x, pos.astype(np.int32)
