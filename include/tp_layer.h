@@ -275,6 +275,71 @@ int tp_layer_destroy(tp_layer *L);
 int tp_exchange_sum(void *dst, int dst_dtype, const float *const *parts,
                     int nparts, size_t count, void *hip_stream);
 
+/* Decode step with a sharded KV cache ("Megatron-LM: GPU-Cluster Training
+ * Parallelism", section "Paper 1: QKV Column-Parallel Splitting in Detail",
+ * inference-time behaviour): generation keeps the training split. Each rank
+ * appends the K and V of its own heads for the new token to its own shard of
+ * the KV cache, which divides the cache memory by t, and the layer's two g
+ * sums now cover one row per sequence.
+ *
+ * One call runs the layer for one new token of each of the handle's
+ * micro_batch sequences (the decode batch B, 1 <= B <= 128), handles with
+ * TP_MASK_CAUSAL only (TP_ERR_UNSUPPORTED otherwise); the handle's seq is not
+ * used and the tensor-parallel phases apply whatever opts.sequence_parallel
+ * says. For sequence b with its new token at position pos = positions[b]:
+ *   a     = LN1(x[b])
+ *   qkv   = a @ W_qkv,r + b_qkv,r
+ *   K, V of local head j -> k_cache[b][j][pos], v_cache[b][j][pos]
+ *   o_j   = softmax(q_j K_j[0..pos]^T / sqrt(dh)) V_j[0..pos]
+ *           (the cache rows 0..pos, the new token included; rows > pos are
+ *           never read)
+ *   then h_mid, LN2, FC1 + GeLU, FC2 exactly as the forward, with n = B.
+ * Phases as tp_layer_fwd: TP_ALL (both g sums the identity; out in the
+ * storage dtype), TP_FWD_ATTN (out = fp32 [B, h] partial, + x + b_o on rank
+ * 0), TP_FWD_MLP (h_mid = the summed fp32 [B, h]; out = fp32 partial,
+ * + h_mid + b_fc2 on rank 0).
+ * KV cache: k_cache and v_cache are [B, H_l, cache_len, dh] in the internal
+ * activation type (fp16 for TP_DTYPE_BF16, fp32 for TP_DTYPE_F32), owned by
+ * the caller; rank r holds heads r*H_l .. (r+1)*H_l - 1. A handle with split
+ * scores (see TP_SCORES_*) also needs k_cache_lo, the same shape in fp16: the
+ * fp16 rounding residual of each cached K value, the scores then use
+ * K = k_cache + k_cache_lo. Positions are int32 device values; a position
+ * outside [0, cache_len) gives undefined outputs for that sequence but no
+ * access outside the cache (its K and V are not written).
+ * Cost: every weight and the cache rows 0..pos are read once per call. */
+typedef struct {
+  const tp_params *params;
+  const void *x;          /* [B, h] storage dtype: TP_ALL, TP_FWD_ATTN */
+  const float *h_mid;     /* TP_FWD_MLP: the summed fp32 [B, h] */
+  void *out;              /* TP_ALL: [B, h] storage dtype; split phases: fp32 [B, h] */
+  void *k_cache, *v_cache;  /* TP_ALL, TP_FWD_ATTN: [B, H_l, cache_len, dh] act */
+  void *k_cache_lo;       /* split scores only: [B, H_l, cache_len, dh] fp16 */
+  const int *positions;   /* TP_ALL, TP_FWD_ATTN: int32 [B] */
+  int cache_len;          /* rows per (sequence, head) of the caches, >= 1 */
+  void *workspace;        /* tp_layer_decode_workspace bytes, 16-byte aligned */
+  size_t workspace_bytes;
+} tp_decode_io;
+
+/* Workspace bytes of tp_layer_decode for this handle (a few MB; it does not
+ * depend on cache_len). The contents need no initialisation and may be
+ * reused freely between calls. */
+int tp_layer_decode_workspace(const tp_layer *L, size_t *bytes);
+
+/* Enqueue one decode phase (TP_ALL, TP_FWD_ATTN or TP_FWD_MLP). */
+int tp_layer_decode(tp_layer *L, int phase, const tp_decode_io *io, void *hip_stream);
+
+/* Prefill into a cache: copy the K and V of every token of the last forward
+ * on this handle (a TP_ALL, TP_FWD_ATTN or TP_FWD_SP_ATTN phase whose
+ * workspace is passed here untouched) into rows 0..seq-1 of the caches of the
+ * layout above (cache_len >= seq, else TP_ERR_SHAPE), and with split scores
+ * the K residuals into k_cache_lo (required then, ignored otherwise). With a
+ * right-padded prompt batch, the rows beyond a sequence's real length hold
+ * the padding's K and V; decode steps overwrite them in order and never read
+ * a row beyond their own position. */
+int tp_layer_kv_fill(const tp_layer *L, const void *workspace, size_t workspace_bytes,
+                     void *k_cache, void *v_cache, void *k_cache_lo, int cache_len,
+                     void *hip_stream);
+
 /* Test tap: byte offset and size inside the workspace of an intermediate
  * kept between forward and backward (TP_TAP_*). Layout is row-major;
  * "act" is fp16 for TP_DTYPE_BF16 and fp32 for TP_DTYPE_F32:

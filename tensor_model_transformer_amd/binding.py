@@ -44,7 +44,8 @@ GRAD_FIELDS = tuple("d_" + f for f in PARAM_FIELDS)
 
 # Every symbol the header declares (checked by the CPU test of the library).
 EXPORTS = ("tp_layer_create", "tp_layer_fwd", "tp_layer_bwd", "tp_layer_destroy",
-           "tp_exchange_sum", "tp_layer_tap", "tp_layer_profile", "tp_layer_profile_read")
+           "tp_exchange_sum", "tp_layer_tap", "tp_layer_profile", "tp_layer_profile_read",
+           "tp_layer_decode_workspace", "tp_layer_decode", "tp_layer_kv_fill")
 KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce")
 
 
@@ -69,6 +70,13 @@ class tp_bwd_io(Structure):
                 + [(f, c_void_p) for f in GRAD_FIELDS]
                 + [("accumulate", c_int), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
                    ("gathered_act", c_void_p), ("gathered_grad", c_void_p)])
+
+
+class tp_decode_io(Structure):
+    _fields_ = [("params", POINTER(tp_params)), ("x", c_void_p), ("h_mid", c_void_p),
+                ("out", c_void_p), ("k_cache", c_void_p), ("v_cache", c_void_p),
+                ("k_cache_lo", c_void_p), ("positions", c_void_p), ("cache_len", c_int),
+                ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
 
 
 _lib = None
@@ -103,6 +111,13 @@ def lib():
                                             POINTER(ctypes.c_double), POINTER(ctypes.c_double),
                                             POINTER(ctypes.c_double)]
         L.tp_layer_profile_read.restype = c_int
+        L.tp_layer_decode_workspace.argtypes = [c_void_p, POINTER(c_size_t)]
+        L.tp_layer_decode_workspace.restype = c_int
+        L.tp_layer_decode.argtypes = [c_void_p, c_int, POINTER(tp_decode_io), c_void_p]
+        L.tp_layer_decode.restype = c_int
+        L.tp_layer_kv_fill.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
+                                       c_int, c_void_p]
+        L.tp_layer_kv_fill.restype = c_int
         _lib = L
     return _lib
 
@@ -161,3 +176,20 @@ def tp_layer_profile_read(handle, kclass):
     rc = lib().tp_layer_profile_read(handle, k, ctypes.byref(n), ctypes.byref(ms),
                                      ctypes.byref(fl), ctypes.byref(by))
     return rc, n.value, ms.value, fl.value, by.value
+
+
+def tp_layer_decode_workspace(handle):
+    """Returns (status, bytes)."""
+    nb = c_size_t()
+    rc = lib().tp_layer_decode_workspace(handle, ctypes.byref(nb))
+    return rc, nb.value
+
+
+def tp_layer_decode(handle, phase, io: tp_decode_io, stream=0):
+    return lib().tp_layer_decode(handle, phase, ctypes.byref(io), stream)
+
+
+def tp_layer_kv_fill(handle, workspace, workspace_bytes, k_cache, v_cache, k_cache_lo,
+                     cache_len, stream=0):
+    return lib().tp_layer_kv_fill(handle, workspace, workspace_bytes, k_cache, v_cache,
+                                  k_cache_lo, cache_len, stream)

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtplayer.so")
-SOURCES = ["tp_layer.cpp", "norm.hip", "gemm.hip", "attn.hip"]
+SOURCES = ["tp_layer.cpp", "norm.hip", "gemm.hip", "attn.hip", "decode.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -18,9 +18,12 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 // y = gamma * (x - mean) * rstd + beta per row of h; saves mean and rstd.
 // x is `x_dtype`, gamma/beta are `p_dtype`, y is `y_dtype`. If x_copy != NULL
 // the fp32 value of x is also written there (keeps a caller's summed h_mid).
+// mean and rstd may be NULL. The first workgroup also sets zero[0..nzero) to 0
+// (the arrival counters of the decode kernels that follow in the stream).
 hipError_t ln_fwd(int x_dtype, int p_dtype, int y_dtype, const void* x, const void* gamma,
                   const void* beta, void* y, float* mean, float* rstd,
-                  float* x_copy, int rows, int h, float eps, hipStream_t s);
+                  float* x_copy, int rows, int h, float eps, hipStream_t s,
+                  int* zero = nullptr, int nzero = 0);
 
 // LayerNorm backward plus the residual-gradient add:
 //   dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) + dres,  g = dy * gamma
@@ -108,5 +111,59 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* qkv_lo, const void* 
                     const void* dO, const float* lse2, float* delta, void* dqkv,
                     const int* valid_len, int batch, int seq, int Hl, int D,
                     int mask, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Decode (decode.hip): one new token per sequence, M = decode batch <= 128.
+// ---------------------------------------------------------------------------
+enum { GEMV_EPI_OUT = 0, GEMV_EPI_GELU = 1, GEMV_EPI_QKV = 2 };
+
+// Y[M, N] = X[M, K] @ W[K, N] (row-major, row strides K and N) with the K
+// range split into nsplit pieces of kc rows (gemv_plan). math DT_F16: X fp16,
+// W bf16, fp16 MFMA; DT_F32: X and W fp32.
+struct GemvArgs {
+  int M, N, K;
+  const void* X;
+  const void* W;
+  int kc, nsplit;
+  float* part;   // [nsplit][M][N] fp32 when nsplit > 1
+  int* count;    // [ceil(N/64)] arrival counters: zero before the launch, zero after
+  int epi;
+  const void* bias; int bias_dt;     // [N] or null
+  // GEMV_EPI_OUT: out = v (+ bias) (+ resid); GEMV_EPI_GELU: out = GeLU(v + bias)
+  const void* resid; int resid_dt;   // [M, N] or null
+  void* out; int out_dt;             // [M, N]
+  int gelu_tanh;
+  // GEMV_EPI_QKV (head-interleaved columns, Hl heads of width D): q -> q
+  // (fp32 [M, Hl*D]); k, v -> caches [M, Hl, cache_len, D] at row pos[m]
+  // (rows outside [0, cache_len) are not written); klo (fp16, optional): the
+  // fp16 rounding residual of k.
+  float* q;
+  void* kcache; void* vcache; _Float16* klo; int cache_dt;
+  const int* pos; int cache_len;
+  int Hl, D;
+};
+void gemv_plan(int M, int N, int K, int* kc, int* nsplit);
+hipError_t gemv(const GemvArgs& g, int math, hipStream_t s);
+
+// Decode attention: waves per launch targeted, maximum cache slices per head.
+constexpr int kDecWaves = 4096;
+constexpr int kDecMaxSplit = 64;
+struct DecAttnArgs {
+  const float* q;                  // [batch, Hl*D] fp32, unscaled
+  const void* kc; const void* vc;  // [batch, Hl, cache_len, D] (fp16 or fp32)
+  const _Float16* klo;             // split scores: fp16 residuals of kc, else null
+  const int* pos;                  // [batch]: keys 0..pos attend (clamped to the cache)
+  int batch, Hl, cache_len, nsplit, chunk;
+  float scale_log2;                // log2(e) / sqrt(D)
+  float* part;                     // [batch*Hl][nsplit][D+2] when nsplit > 1
+  int* count;                      // [batch*Hl] arrival counters (zero before and after)
+  void* o; int o_dt;               // [batch, Hl*D]
+};
+// Slices per (sequence, head) for a cache of cache_len rows; *chunk = rows per slice.
+int dec_attn_split(int batch, int Hl, int cache_len, int* chunk);
+hipError_t dec_attn(int dtype, const DecAttnArgs& g, int D, int split, hipStream_t s);
+// Copies K, V (and K residuals) of a forward's qkv [batch*seq, 3*Hl*D] into caches.
+hipError_t kv_fill(int dtype, const void* qkv, const void* qkv_lo, void* kc, void* vc, void* klo,
+                   int batch, int seq, int Hl, int D, int cache_len, hipStream_t s);
 
 }  // namespace tpl

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <cmath>
 #include <initializer_list>
 #include <new>
 #include <vector>
@@ -72,6 +74,14 @@ struct tp_layer {
   int split_w2, split_w1, split_wo, split_wqkv;
   double attn_pairs;  // allowed query-key pairs (causal); 0 for padding (lengths on device)
   Prof prof;
+  // decode (one row per sequence): its own workspace plan
+  struct Dec {
+    Region a, q, apart, o, h_mid, c, z, gpart, cnt;
+    size_t bytes;
+    int kc[4], ns[4];     // GEMV K split: qkv, w_o, fc1, fc2
+    int tiles[4];         // 64-column strips of each GEMV (arrival counters)
+    int cnt_attn, cnt_mlp;  // counters cleared by LN1 / LN2
+  } dec;
 };
 
 namespace {
@@ -179,6 +189,42 @@ void plan(tp_layer* L) {
   }
   take(L->splitk, sk);
   L->ws_bytes = off;
+}
+
+// Decode workspace: the rows of one token per sequence (B = micro_batch), the
+// GEMV split-K partials, the attention slice partials and the arrival
+// counters: [qkv strips | attention (sequence, head) pairs | w_o strips]
+// cleared by LN1, then [fc1 strips | fc2 strips] cleared by LN2.
+void plan_decode(tp_layer* L) {
+  tp_layer::Dec& d = L->dec;
+  size_t off = 0;
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.bytes = bytes;
+    off += align_up(bytes);
+  };
+  const size_t B = (size_t)L->batch, h = (size_t)L->hidden, e = (size_t)L->esz;
+  const int MNK[4][2] = {{3 * L->hl, L->hidden}, {L->hidden, L->hl}, {L->fl, L->hidden},
+                         {L->hidden, L->fl}};
+  size_t gp = 0;
+  for (int i = 0; i < 4; ++i) {
+    gemv_plan(L->batch, MNK[i][0], MNK[i][1], &d.kc[i], &d.ns[i]);
+    d.tiles[i] = (MNK[i][0] + 63) / 64;
+    if (d.ns[i] > 1) gp = std::max(gp, (size_t)d.ns[i] * B * MNK[i][0] * 4);
+  }
+  const size_t pairs = B * L->Hl;
+  d.cnt_attn = d.tiles[0] + (int)pairs + d.tiles[1];
+  d.cnt_mlp = d.tiles[2] + d.tiles[3];
+  take(d.a, B * h * e);
+  take(d.q, B * L->hl * 4);
+  take(d.apart, ((size_t)kDecWaves + pairs) * (L->dh + 2) * 4);
+  take(d.o, B * L->hl * e);
+  take(d.h_mid, B * h * 4);
+  take(d.c, B * h * e);
+  take(d.z, B * L->fl * e);
+  take(d.gpart, gp);
+  take(d.cnt, (size_t)(d.cnt_attn + d.cnt_mlp) * 4);
+  d.bytes = off;
 }
 
 template <typename T>
@@ -601,6 +647,119 @@ void prof_fold(Prof& p) {
 
 }  // namespace
 
+// ---- decode ------------------------------------------------------------------
+double gemv_bytes(const tp_layer* L, const GemvArgs& g, double out_e) {
+  const double e = L->esz;
+  double b = (double)g.K * g.N * e + (double)g.M * g.K * e + (double)g.M * g.N * out_e;
+  if (g.bias) b += (double)g.N * e;
+  if (g.resid) b += (double)g.M * g.N * (g.resid_dt == DT_F32 ? 4.0 : e);
+  return b;
+}
+
+int run_gemv(tp_layer* L, const GemvArgs& g, double out_e, hipStream_t s) {
+  Scope ps(L, s, TP_K_GEMM, 2.0 * g.M * g.N * (double)g.K, gemv_bytes(L, g, out_e));
+  HIP_TRY(gemv(g, L->adt, s));
+  return TP_OK;
+}
+
+GemvArgs gemv_base(tp_layer* L, int which, void* ws, int* count) {
+  const tp_layer::Dec& d = L->dec;
+  GemvArgs g = {};
+  g.M = L->batch;
+  g.kc = d.kc[which];
+  g.nsplit = d.ns[which];
+  g.part = at<float>(ws, d.gpart);
+  g.count = count;
+  g.bias_dt = g.resid_dt = L->sdt;
+  g.gelu_tanh = L->gelu_tanh;
+  return g;
+}
+
+// x -> a -> qkv (q kept, K/V appended to the cache) -> o -> o @ W_o
+// [+ b_o + x] into `dst` (fp32 [B, h]).
+int dec_attn_phase(tp_layer* L, const tp_params* p, const tp_decode_io* io, float* dst,
+                   bool designated, void* ws, hipStream_t s) {
+  const tp_layer::Dec& d = L->dec;
+  const int B = L->batch, h = L->hidden, hl = L->hl, D = L->dh;
+  int* cnt = at<int>(ws, d.cnt);
+  int e;
+  {
+  Scope ps(L, s, TP_K_LN_FWD, 0, (double)B * h * 2 * L->esz);
+  HIP_TRY(ln_fwd(L->sdt, L->sdt, L->adt, io->x, p->ln1_gamma, p->ln1_beta, at<void>(ws, d.a),
+                 nullptr, nullptr, nullptr, B, h, L->eps, s, cnt, d.cnt_attn));
+  }
+  GemvArgs g = gemv_base(L, 0, ws, cnt);
+  g.N = 3 * hl; g.K = h;
+  g.X = at<void>(ws, d.a); g.W = p->w_qkv;
+  g.epi = GEMV_EPI_QKV;
+  g.bias = p->b_qkv;
+  g.q = at<float>(ws, d.q);
+  g.kcache = io->k_cache; g.vcache = io->v_cache;
+  g.klo = L->split_scores ? (_Float16*)io->k_cache_lo : nullptr;
+  g.cache_dt = L->adt;
+  g.pos = io->positions; g.cache_len = io->cache_len;
+  g.Hl = L->Hl; g.D = D;
+  if ((e = run_gemv(L, g, 0.0, s))) return e;
+  {
+  DecAttnArgs a = {};
+  a.q = at<float>(ws, d.q);
+  a.kc = io->k_cache; a.vc = io->v_cache;
+  a.klo = L->split_scores ? (const _Float16*)io->k_cache_lo : nullptr;
+  a.pos = io->positions;
+  a.batch = B; a.Hl = L->Hl; a.cache_len = io->cache_len;
+  a.nsplit = dec_attn_split(B, L->Hl, io->cache_len, &a.chunk);
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  a.part = at<float>(ws, d.apart);
+  a.count = cnt + d.tiles[0];
+  a.o = at<void>(ws, d.o); a.o_dt = L->adt;
+  const double keys = (double)B * L->Hl * io->cache_len;
+  Scope ps(L, s, TP_K_ATTN_FWD, 4.0 * D * keys,
+           keys * D * L->esz * (L->split_scores ? 3 : 2) + (double)B * hl * (4 + L->esz));
+  HIP_TRY(dec_attn(L->adt, a, D, L->split_scores, s));
+  }
+  g = gemv_base(L, 1, ws, cnt + d.tiles[0] + B * L->Hl);
+  g.N = h; g.K = hl;
+  g.X = at<void>(ws, d.o); g.W = p->w_o;
+  g.epi = GEMV_EPI_OUT;
+  if (designated) {
+    g.bias = p->b_o;
+    g.resid = io->x;
+  }
+  g.out = dst; g.out_dt = DT_F32;
+  return run_gemv(L, g, 4.0, s);
+}
+
+// h_mid (fp32 [B, h]) -> c -> z -> z @ W_fc2 [+ b_fc2 + h_mid] into `out`.
+int dec_mlp_phase(tp_layer* L, const tp_params* p, const float* h_mid, void* out, int out_dt,
+                  bool designated, void* ws, hipStream_t s) {
+  const tp_layer::Dec& d = L->dec;
+  const int B = L->batch, h = L->hidden, fl = L->fl;
+  int* cnt = at<int>(ws, d.cnt) + d.cnt_attn;
+  int e;
+  {
+  Scope ps(L, s, TP_K_LN_FWD, 0, (double)B * h * (4 + L->esz));
+  HIP_TRY(ln_fwd(DT_F32, L->sdt, L->adt, h_mid, p->ln2_gamma, p->ln2_beta, at<void>(ws, d.c),
+                 nullptr, nullptr, nullptr, B, h, L->eps, s, cnt, d.cnt_mlp));
+  }
+  GemvArgs g = gemv_base(L, 2, ws, cnt);
+  g.N = fl; g.K = h;
+  g.X = at<void>(ws, d.c); g.W = p->w_fc1;
+  g.epi = GEMV_EPI_GELU;
+  g.bias = p->b_fc1;
+  g.out = at<void>(ws, d.z); g.out_dt = L->adt;
+  if ((e = run_gemv(L, g, L->esz, s))) return e;
+  g = gemv_base(L, 3, ws, cnt + d.tiles[2]);
+  g.N = h; g.K = fl;
+  g.X = at<void>(ws, d.z); g.W = p->w_fc2;
+  g.epi = GEMV_EPI_OUT;
+  if (designated) {
+    g.bias = p->b_fc2;
+    g.resid = h_mid; g.resid_dt = DT_F32;
+  }
+  g.out = out; g.out_dt = out_dt;
+  return run_gemv(L, g, out_dt == DT_F32 ? 4.0 : L->esz, s);
+}
+
 extern "C" {
 
 int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, int t, int rank,
@@ -661,6 +820,7 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   L->adt = dtype == TP_DTYPE_BF16 ? DT_F16 : DT_F32;
   L->attn_pairs = mask == TP_MASK_CAUSAL ? (double)micro_batch * seq * (seq + 1) / 2.0 : 0.0;
   plan(L);
+  plan_decode(L);
   *out = L;
   *workspace_bytes = L->ws_bytes;
   return TP_OK;
@@ -730,6 +890,63 @@ int tp_layer_bwd(tp_layer* L, int phase, const tp_bwd_io* io, void* hip_stream) 
     default:
       return bwd_sp(L, phase, p, io, ws, s);
   }
+}
+
+int tp_layer_decode_workspace(const tp_layer* L, size_t* bytes) {
+  if (!L || !bytes) return TP_ERR_ARG;
+  *bytes = L->dec.bytes;
+  return TP_OK;
+}
+
+int tp_layer_decode(tp_layer* L, int phase, const tp_decode_io* io, void* hip_stream) {
+  if (!L || !io) return TP_ERR_ARG;
+  if (L->mask != TP_MASK_CAUSAL || L->batch > 128) return TP_ERR_UNSUPPORTED;
+  if (phase < TP_ALL || phase > TP_FWD_MLP) return TP_ERR_PHASE;
+  int e = check_params(L, io->params);
+  if (e) return e;
+  if (!io->workspace || io->workspace_bytes < L->dec.bytes) return TP_ERR_WORKSPACE;
+  if (!aligned(io->workspace)) return TP_ERR_ALIGN;
+  if (phase != TP_FWD_MLP) {
+    if ((e = check_ptrs({io->x, io->out, io->k_cache, io->v_cache, io->positions}))) return e;
+    if (L->split_scores && (e = check_ptrs({io->k_cache_lo}))) return e;
+    if (io->cache_len < 1) return TP_ERR_ARG;
+  } else if ((e = check_ptrs({io->h_mid, io->out}))) {
+    return e;
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  void* ws = io->workspace;
+  const tp_params* p = io->params;
+  const bool designated = L->rank == 0;
+  switch (phase) {
+    case TP_ALL: {
+      float* hm = at<float>(ws, L->dec.h_mid);
+      if ((e = dec_attn_phase(L, p, io, hm, true, ws, s))) return e;
+      return dec_mlp_phase(L, p, hm, io->out, L->sdt, true, ws, s);
+    }
+    case TP_FWD_ATTN:
+      return dec_attn_phase(L, p, io, (float*)io->out, designated, ws, s);
+    default:
+      return dec_mlp_phase(L, p, io->h_mid, io->out, DT_F32, designated, ws, s);
+  }
+}
+
+int tp_layer_kv_fill(const tp_layer* L, const void* workspace, size_t workspace_bytes,
+                     void* k_cache, void* v_cache, void* k_cache_lo, int cache_len,
+                     void* hip_stream) {
+  if (!L) return TP_ERR_ARG;
+  if (!workspace || workspace_bytes < L->ws_bytes) return TP_ERR_WORKSPACE;
+  if (!aligned(workspace)) return TP_ERR_ALIGN;
+  int e = check_ptrs({k_cache, v_cache});
+  if (e) return e;
+  if (L->split_scores && (e = check_ptrs({k_cache_lo}))) return e;
+  if (cache_len < L->seq) return TP_ERR_SHAPE;
+  void* ws = const_cast<void*>(workspace);
+  if (kv_fill(L->adt, at<void>(ws, L->qkv),
+              L->split_scores ? at<void>(ws, L->qkv_lo) : nullptr, k_cache, v_cache,
+              L->split_scores ? k_cache_lo : nullptr, L->batch, L->seq, L->Hl, L->dh,
+              cache_len, (hipStream_t)hip_stream) != hipSuccess)
+    return TP_ERR_HIP;
+  return TP_OK;
 }
 
 int tp_layer_destroy(tp_layer* L) {

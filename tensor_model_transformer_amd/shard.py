@@ -56,6 +56,8 @@ class Shard:
         self.dx_fp32 = dx_fp32
         _check("tp_layer_create", rc)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        self.dws = None
+        self.dws_bytes = 0
 
     def close(self):
         if self.handle:
@@ -96,6 +98,26 @@ class Shard:
         _check("tp_layer_tap", rc)
         return self.ws[off:off + nbytes]
 
+    def act_dtype(self):
+        """Internal activation type: fp16 for the bf16 layer (also the KV cache)."""
+        return torch.float16 if self.dims.dtype == "bf16" else torch.float32
+
+    def upload_cache(self, a: np.ndarray) -> torch.Tensor:
+        """A [B, H_l, L, dh] cache array (already on the act grid) on the device."""
+        return to_device(a, self.act_dtype(), self.device)
+
+    def empty_cache(self, cache_len: int) -> torch.Tensor:
+        d = self.dims
+        return torch.zeros(d.batch, d.heads_local, cache_len, d.head_dim, dtype=self.act_dtype(),
+                           device=self.device)
+
+    def decode_workspace(self) -> torch.Tensor:
+        if self.dws is None:
+            rc, self.dws_bytes = B.tp_layer_decode_workspace(self.handle)
+            _check("tp_layer_decode_workspace", rc)
+            self.dws = torch.empty(max(self.dws_bytes, 256), dtype=torch.uint8, device=self.device)
+        return self.dws
+
     # -- calls -----------------------------------------------------------
     def stream(self) -> int:
         return torch.cuda.current_stream(self.device).cuda_stream
@@ -130,6 +152,28 @@ class Shard:
         io.workspace = self.ws.data_ptr()
         io.workspace_bytes = self.ws_bytes
         return B.tp_layer_bwd(self.handle, phase, io, self.stream())
+
+
+    def decode(self, p: "DeviceParams", out: Optional[torch.Tensor], x=None, h_mid=None,
+               k_cache=None, v_cache=None, k_cache_lo=None, positions=None,
+               phase: int = B.TP_ALL) -> int:
+        ws = self.decode_workspace()
+        io = B.tp_decode_io()
+        io.params = p.ptr()
+        for name, t in (("x", x), ("h_mid", h_mid), ("out", out), ("k_cache", k_cache),
+                        ("v_cache", v_cache), ("k_cache_lo", k_cache_lo),
+                        ("positions", positions)):
+            setattr(io, name, t.data_ptr() if t is not None else None)
+        io.cache_len = int(k_cache.shape[2]) if k_cache is not None else 0
+        io.workspace = ws.data_ptr()
+        io.workspace_bytes = self.dws_bytes
+        return B.tp_layer_decode(self.handle, phase, io, self.stream())
+
+    def kv_fill(self, k_cache, v_cache, k_cache_lo=None) -> int:
+        return B.tp_layer_kv_fill(self.handle, self.ws.data_ptr(), self.ws_bytes,
+                                  k_cache.data_ptr(), v_cache.data_ptr(),
+                                  k_cache_lo.data_ptr() if k_cache_lo is not None else None,
+                                  int(k_cache.shape[2]), self.stream())
 
 
 class DeviceParams:

@@ -203,3 +203,83 @@ def test_padding_mask_requires_valid_len(lib):
     io.workspace_bytes = ws
     assert B.tp_layer_fwd(h, B.TP_ALL, io, 0) == B.TP_ERR_ARG
     B.tp_layer_destroy(h)
+
+
+def _decode_io(ws_bytes, fake=1 << 20):
+    p = B.tp_params()
+    for f in B.PARAM_FIELDS:
+        setattr(p, f, fake)
+    io = B.tp_decode_io()
+    io.params = ctypes.pointer(p)
+    io.workspace = fake
+    io.workspace_bytes = ws_bytes
+    for f in ("x", "out", "k_cache", "v_cache", "positions"):
+        setattr(io, f, fake)
+    io.cache_len = 16
+    return io, p
+
+
+def test_decode_workspace_is_small_and_independent_of_seq(lib):
+    sizes = []
+    for seq in (64, 4096):
+        rc, h, ws = create(seq=seq, micro_batch=8)
+        assert rc == B.TP_OK
+        rc, dws = B.tp_layer_decode_workspace(h)
+        assert rc == B.TP_OK and 0 < dws < ws
+        sizes.append(dws)
+        B.tp_layer_destroy(h)
+    assert sizes[0] == sizes[1]
+    assert B.tp_layer_decode_workspace(None)[0] == B.TP_ERR_ARG
+
+
+def test_decode_argument_errors_need_no_device(lib):
+    rc, h, _ = create(micro_batch=4)
+    assert rc == B.TP_OK
+    _, dws = B.tp_layer_decode_workspace(h)
+    io, p = _decode_io(dws)
+    assert B.tp_layer_decode(None, B.TP_ALL, io, 0) == B.TP_ERR_ARG
+    assert B.tp_layer_decode(h, 3, io, 0) == B.TP_ERR_PHASE
+    io.workspace_bytes = dws - 1
+    assert B.tp_layer_decode(h, B.TP_ALL, io, 0) == B.TP_ERR_WORKSPACE
+    io.workspace_bytes = dws
+    io.workspace = (1 << 20) + 8
+    assert B.tp_layer_decode(h, B.TP_ALL, io, 0) == B.TP_ERR_ALIGN
+    io.workspace = 1 << 20
+    io.positions = None
+    assert B.tp_layer_decode(h, B.TP_FWD_ATTN, io, 0) == B.TP_ERR_ARG
+    io.positions = 1 << 20
+    io.cache_len = 0
+    assert B.tp_layer_decode(h, B.TP_ALL, io, 0) == B.TP_ERR_ARG
+    # the MLP phase needs neither the caches nor the token rows, only h_mid and out
+    io2, _ = _decode_io(dws)
+    io2.x = io2.k_cache = io2.v_cache = io2.positions = None
+    io2.h_mid = None
+    assert B.tp_layer_decode(h, B.TP_FWD_MLP, io2, 0) == B.TP_ERR_ARG
+    # kv_fill: training workspace, cache at least seq rows
+    rc, h2, ws2 = create(seq=64)
+    assert B.tp_layer_kv_fill(h2, 1 << 20, ws2 - 1, 1 << 20, 1 << 20, None, 64, 0) == \
+        B.TP_ERR_WORKSPACE
+    assert B.tp_layer_kv_fill(h2, 1 << 20, ws2, 1 << 20, 1 << 20, None, 63, 0) == B.TP_ERR_SHAPE
+    assert B.tp_layer_kv_fill(h2, 1 << 20, ws2, None, 1 << 20, None, 64, 0) == B.TP_ERR_ARG
+    B.tp_layer_destroy(h2)
+    B.tp_layer_destroy(h)
+
+
+def test_decode_needs_causal_mask_batch_limit_and_split_residuals(lib):
+    rc, h, _ = create(mask=B.TP_MASK_PADDING)
+    _, dws = B.tp_layer_decode_workspace(h)
+    io, p = _decode_io(dws)
+    p.valid_len = 1 << 20
+    assert B.tp_layer_decode(h, B.TP_ALL, io, 0) == B.TP_ERR_UNSUPPORTED
+    B.tp_layer_destroy(h)
+    rc, h, _ = create(micro_batch=129)
+    _, dws = B.tp_layer_decode_workspace(h)
+    io, _ = _decode_io(dws)
+    assert B.tp_layer_decode(h, B.TP_ALL, io, 0) == B.TP_ERR_UNSUPPORTED
+    B.tp_layer_destroy(h)
+    opts = {"scores": B.TP_SCORES_SPLIT}
+    rc, h, _ = create(opts=opts)
+    _, dws = B.tp_layer_decode_workspace(h)
+    io, _ = _decode_io(dws)
+    assert B.tp_layer_decode(h, B.TP_ALL, io, 0) == B.TP_ERR_ARG  # k_cache_lo missing
+    B.tp_layer_destroy(h)
