@@ -8,6 +8,12 @@ algorithmic TFLOP/s (GEMMs 2MNK, attention 4*dh*H_l per allowed query-key
 pair, backward = 2x forward; no recomputation, masked work, LayerNorm or
 elementwise work counted) and its fraction of the bf16 dense MFMA peak.
 
+With `--mode decode` a step is instead one decode step of the same shard
+(tp_layer_decode, TP_ALL): one new token for each of the micro-batch's
+sequences against a KV cache shard of `--cache-len` rows; the metric is
+generated tokens per second and the roofline is HBM bandwidth (weights and
+cache rows read once per step).
+
 Prints ONE JSON line. `--gpus N` with N > 1 exits: this build runs one GPU.
 """
 from __future__ import annotations
@@ -126,10 +132,163 @@ def copy_probe(nbytes, reps):
                       "dtype_code": B.TP_DTYPE_F32}))
 
 
+DECODE_METRIC = ("decode tokens/s per GPU, one TP-rank layer shard, one new token per sequence "
+                 "against its KV cache shard")
+
+
+def decode_bytes(d, positions, split_scores):
+    """Algorithmic HBM bytes of one decode step of one rank: every weight and
+    bias read once, cache rows 0..pos read once per sequence (K, V, and the K
+    residuals with split scores), the new K and V rows written, the token rows
+    read and the output written once. The [B, h] intermediates between the
+    kernels are not counted."""
+    e = 2 if d.dtype == "bf16" else 4
+    h, hl, fl, B = d.hidden, d.hidden_local, d.ffn_local, d.batch
+    weights = (h * 3 * hl + hl * h + h * fl + fl * h) * e + (6 * h + 3 * hl + fl) * e
+    keys = sum(int(p) + 1 for p in positions)
+    per_key = hl * e * (3 if split_scores else 2)
+    return weights + keys * per_key + 2 * B * hl * e + 2 * B * h * e
+
+
+def cpu_decode_baseline(w, cache_len, min_seconds):
+    """The fp64 decode oracle timed on the host: the same decode step (all
+    sequences, full cache), repeated until `min_seconds` have run."""
+    from oracle import decode as OD
+    from tensor_model_transformer_amd.synth import decode_inputs, rank_caches, rank_params
+    d = w.dims
+    params = rank_params(w)
+    x, pos = decode_inputs(w, cache_len, "full")
+    kc, vc = rank_caches(w, w.rank, cache_len)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        OD.decode_step(params, x, kc, vc, pos, d.heads_local)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * d.batch / dt, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"the whole decode step ({d.batch} sequences at position {cache_len - 1}) "
+                      f"of the {w.name} shard, fp64 NumPy oracle, run {reps}x"}
+
+
+def bench_decode(args):
+    import torch
+    from tensor_model_transformer_amd import binding as B
+    from tensor_model_transformer_amd.shard import Shard, _check
+    from tensor_model_transformer_amd.synth import WORKLOADS, decode_inputs, rank_caches, rank_params
+
+    w = WORKLOADS[args.workload]
+    d = w.dims
+    if d.mask != "causal":
+        print(f"bench.py: {w.name} is a bidirectional (padding-mask) layer; decode needs a causal "
+              "one", file=sys.stderr)
+        sys.exit(2)
+    L = args.cache_len or d.seq
+    sh = Shard(d, w.rank)
+    p = sh.upload_params(rank_params(w))
+    x, pos = decode_inputs(w, L, "full")
+    kc, vc = rank_caches(w, w.rank, L)
+    xd = torch.from_numpy(x).to(sh.device).to(sh.dtype)
+    kd, vd = sh.upload_cache(kc), sh.upload_cache(vc)
+    del kc, vc
+    split = sh.split_scores
+    klo = torch.zeros_like(kd) if split else None
+    posd = torch.from_numpy(pos).to(sh.device)
+    out = torch.empty(d.batch, d.hidden, dtype=sh.dtype, device=sh.device)
+    sh.decode_workspace()
+    stream = torch.cuda.Stream(device=sh.device)
+
+    def step():
+        _check("tp_layer_decode", sh.decode(p, out, x=xd, k_cache=kd, v_cache=vd,
+                                            k_cache_lo=klo, positions=posd))
+
+    def timed(fn, n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(n):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        t0 = time.perf_counter()
+        ms_per_step = timed(step, args.steps)
+        wall = time.perf_counter() - t0
+        # the same step captured once in a HIP graph and replayed (reported
+        # beside the direct calls, which are faster on this stack)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        graph_ms = timed(graph.replay, args.steps)
+    value = d.batch / (ms_per_step * 1e-3)
+    nbytes = decode_bytes(d, pos, split)
+    print(f"[bench] decode {w.name} B={d.batch} L={L}: {ms_per_step * 1e3:.1f} us/step, "
+          f"{graph_ms * 1e3:.1f} us/step graph replay, {value:.0f} tokens/s, "
+          f"{nbytes / ms_per_step / 1e6:.0f} GB/s (wall {wall:.2f} s)", file=sys.stderr, flush=True)
+
+    # per-kernel-class event timing over eager steps
+    _check("tp_layer_profile", B.tp_layer_profile(sh.handle, 1))
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for k in B.KCLASSES:
+        rc, n, kms, kfl, kby = B.tp_layer_profile_read(sh.handle, k)
+        _check("tp_layer_profile_read", rc)
+        if n:
+            breakdown[k] = {"launches_per_step": n / args.steps, "ms_per_step": kms / args.steps,
+                            "gbyte_per_step": kby / args.steps / 1e9}
+    B.tp_layer_profile(sh.handle, 0)
+    dom = max(breakdown, key=lambda k: breakdown[k]["ms_per_step"])
+    bd = breakdown[dom]
+    achieved = bd["gbyte_per_step"] / bd["ms_per_step"] * 1e3
+    roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "algorithmic_bytes_per_launch": bd["gbyte_per_step"] * 1e9 / bd["launches_per_step"],
+            "launches_per_step": bd["launches_per_step"],
+            "avg_launch_ms": bd["ms_per_step"] / bd["launches_per_step"],
+            "step_bytes": nbytes, "step_gbs": nbytes / ms_per_step / 1e6,
+            "step_frac": nbytes / ms_per_step / 1e6 / HBM_PEAK_GBS}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_decode_baseline(w, L, args.cpu_min_seconds)
+        print(f"[bench] cpu oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads",
+              file=sys.stderr, flush=True)
+    line = {
+        "metric": DECODE_METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": d.dtype, "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, "
+                                  "N(0, (0.02 sqrt h)^2) cache)",
+        "config": {"workload": f"decode_{w.name}", "decode_batch": d.batch, "cache_len": L,
+                   "positions": "all at cache_len - 1", "hidden": d.hidden, "heads": d.heads,
+                   "ffn": d.ffn, "t": d.t, "rank": w.rank, "split_scores": split,
+                   "launch": "direct C-ABI calls", "graph_replay_ms_per_step": graph_ms,
+                   "decode_workspace_bytes": sh.dws_bytes},
+        "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown,
+    }
+    print(json.dumps(line))
+    del graph
+    sh.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 30; 1000 for --mode decode)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt_1p2b_t1")
     ap.add_argument("--cpu-seqs", type=int, default=0,
@@ -141,9 +300,15 @@ def main():
                          "sequence-parallel phases (its kernels only, exchanges excluded)")
     ap.add_argument("--recompute", action="store_true",
                     help="recompute the FC1 pre-activation in backward (TP_RECOMPUTE_FC1)")
+    ap.add_argument("--mode", choices=("train", "decode"), default="train",
+                    help="train: forward + backward (the headline); decode: one decode step")
+    ap.add_argument("--cache-len", type=int, default=0,
+                    help="decode: KV cache rows per sequence (default: the workload's seq)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 1000 if args.mode == "decode" else 30
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU tensor parallelism is described in DESIGN.md, not launched.",
@@ -160,6 +325,9 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe(args.copy_probe, 10)
+        return
+    if args.mode == "decode":
+        bench_decode(args)
         return
     w = WORKLOADS[args.workload]
     d = w.dims

@@ -18,12 +18,10 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 // y = gamma * (x - mean) * rstd + beta per row of h; saves mean and rstd.
 // x is `x_dtype`, gamma/beta are `p_dtype`, y is `y_dtype`. If x_copy != NULL
 // the fp32 value of x is also written there (keeps a caller's summed h_mid).
-// mean and rstd may be NULL. The first workgroup also sets zero[0..nzero) to 0
-// (the arrival counters of the decode kernels that follow in the stream).
+// mean and rstd may be NULL.
 hipError_t ln_fwd(int x_dtype, int p_dtype, int y_dtype, const void* x, const void* gamma,
                   const void* beta, void* y, float* mean, float* rstd,
-                  float* x_copy, int rows, int h, float eps, hipStream_t s,
-                  int* zero = nullptr, int nzero = 0);
+                  float* x_copy, int rows, int h, float eps, hipStream_t s);
 
 // LayerNorm backward plus the residual-gradient add:
 //   dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) + dres,  g = dy * gamma
@@ -115,53 +113,58 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* qkv_lo, const void* 
 // ---------------------------------------------------------------------------
 // Decode (decode.hip): one new token per sequence, M = decode batch <= 128.
 // ---------------------------------------------------------------------------
-enum { GEMV_EPI_OUT = 0, GEMV_EPI_GELU = 1, GEMV_EPI_QKV = 2 };
+enum { GEMV_EPI_OUT = 0, GEMV_EPI_GELU = 1 };
 
-// Y[M, N] = X[M, K] @ W[K, N] (row-major, row strides K and N) with the K
-// range split into nsplit pieces of kc rows (gemv_plan). math DT_F16: X fp16,
-// W bf16, fp16 MFMA; DT_F32: X and W fp32.
+// Y[M, N] = X[M, K] @ W[K, N] (row-major, row strides K and N): workgroups
+// own `strip`-column strips and kc rows of K staged `chunk` rows at a time,
+// the K range split into nsplit pieces (gemv_plan). math DT_F16: X fp16,
+// W bf16, fp16 MFMA; DT_F32: X and W fp32 (strip 64). With raw = 1 the
+// launch only writes the split partials (also for nsplit = 1) for a consumer
+// that sums them itself; otherwise the partials are summed in split order and
+// the epilogue writes out.
 struct GemvArgs {
   int M, N, K;
   const void* X;
   const void* W;
-  int kc, nsplit;
-  float* part;   // [nsplit][M][N] fp32 when nsplit > 1
-  int* count;    // [ceil(N/64)] arrival counters: zero before the launch, zero after
+  int strip, chunk, kc, nsplit;
+  int raw;
+  float* part;   // [nsplit][M][N] fp32 when nsplit > 1 or raw
   int epi;
   const void* bias; int bias_dt;     // [N] or null
   // GEMV_EPI_OUT: out = v (+ bias) (+ resid); GEMV_EPI_GELU: out = GeLU(v + bias)
   const void* resid; int resid_dt;   // [M, N] or null
   void* out; int out_dt;             // [M, N]
   int gelu_tanh;
-  // GEMV_EPI_QKV (head-interleaved columns, Hl heads of width D): q -> q
-  // (fp32 [M, Hl*D]); k, v -> caches [M, Hl, cache_len, D] at row pos[m]
-  // (rows outside [0, cache_len) are not written); klo (fp16, optional): the
-  // fp16 rounding residual of k.
-  float* q;
-  void* kcache; void* vcache; _Float16* klo; int cache_dt;
-  const int* pos; int cache_len;
-  int Hl, D;
 };
-void gemv_plan(int M, int N, int K, int* kc, int* nsplit);
+void gemv_plan(int math, int M, int N, int K, int* strip, int* chunk, int* kc, int* nsplit);
 hipError_t gemv(const GemvArgs& g, int math, hipStream_t s);
 
 // Decode attention: waves per launch targeted, maximum cache slices per head.
 constexpr int kDecWaves = 4096;
 constexpr int kDecMaxSplit = 64;
 struct DecAttnArgs {
-  const float* q;                  // [batch, Hl*D] fp32, unscaled
-  const void* kc; const void* vc;  // [batch, Hl, cache_len, D] (fp16 or fp32)
-  const _Float16* klo;             // split scores: fp16 residuals of kc, else null
+  // the QKV GEMV's raw split partials [qkv_ns][batch][3*Hl*D] (head-interleaved
+  // columns) and its bias: the new token's q, k, v are their sum
+  const float* qkv_part; int qkv_ns;
+  const void* b_qkv; int bias_dt;
+  void* kc; void* vc;              // [batch, Hl, cache_len, D] (fp16 or fp32); row pos written
+  _Float16* klo;                   // split scores: fp16 residuals of kc, else null
   const int* pos;                  // [batch]: keys 0..pos attend (clamped to the cache)
   int batch, Hl, cache_len, nsplit, chunk;
   float scale_log2;                // log2(e) / sqrt(D)
   float* part;                     // [batch*Hl][nsplit][D+2] when nsplit > 1
-  int* count;                      // [batch*Hl] arrival counters (zero before and after)
   void* o; int o_dt;               // [batch, Hl*D]
 };
 // Slices per (sequence, head) for a cache of cache_len rows; *chunk = rows per slice.
 int dec_attn_split(int batch, int Hl, int cache_len, int* chunk);
 hipError_t dec_attn(int dtype, const DecAttnArgs& g, int D, int split, hipStream_t s);
+// h_mid[rows, h] = sum_s part[s] + bias + x (fp32), y = LN(h_mid) (gamma, beta):
+// the output projection's split partials [ns][rows][h] finished together with
+// the second LayerNorm. dtype DT_F16: bias/x/gamma/beta bf16, y fp16; DT_F32:
+// all fp32.
+hipError_t dec_resid_ln(int dtype, const float* part, int ns, const void* bias, const void* x,
+                        float* h_mid, const void* gamma, const void* beta, void* y, int rows,
+                        int h, float eps, hipStream_t s);
 // Copies K, V (and K residuals) of a forward's qkv [batch*seq, 3*Hl*D] into caches.
 hipError_t kv_fill(int dtype, const void* qkv, const void* qkv_lo, void* kc, void* vc, void* klo,
                    int batch, int seq, int Hl, int D, int cache_len, hipStream_t s);

@@ -22,12 +22,10 @@ template <typename Tin, typename T, typename To, int NT, int NV>
 __global__ __launch_bounds__(NT) void ln_fwd_kernel(
     const Tin* __restrict__ x, const T* __restrict__ gamma, const T* __restrict__ beta,
     To* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out,
-    float* __restrict__ x_copy, int h, float eps, int* __restrict__ zero, int nzero) {
+    float* __restrict__ x_copy, int h, float eps) {
   __shared__ float red[16];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  if (row == 0)
-    for (int i = tid; i < nzero; i += NT) zero[i] = 0;
   const int nvec = h >> 3;
   const Tin* xr = x + (size_t)row * h;
   float v[NV][8];
@@ -94,15 +92,14 @@ static bool row_config(int h, int* nt, int* nv) {
 template <typename Tin, typename T, typename To>
 static hipError_t ln_fwd_t(const void* x, const void* gamma, const void* beta, void* y,
                            float* mean, float* rstd, float* x_copy, int rows, int h,
-                           float eps, hipStream_t s, int* zero, int nzero) {
+                           float eps, hipStream_t s) {
   int nt, nv;
   if (!row_config(h, &nt, &nv)) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
 #define TPL_LNF(NT_, NV_)                                                                   \
   if (nt == NT_ && nv == NV_) {                                                             \
     ln_fwd_kernel<Tin, T, To, NT_, NV_><<<rows, NT_, 0, s>>>(                               \
-        (const Tin*)x, (const T*)gamma, (const T*)beta, (To*)y, mean, rstd, x_copy, h, eps,   \
-        zero, nzero);                                                                       \
+        (const Tin*)x, (const T*)gamma, (const T*)beta, (To*)y, mean, rstd, x_copy, h, eps); \
     return hipGetLastError();                                                               \
   }
   TPL_LNF(256, 1) TPL_LNF(256, 2) TPL_LNF(512, 2) TPL_LNF(1024, 2) TPL_LNF(1024, 4)
@@ -112,15 +109,15 @@ static hipError_t ln_fwd_t(const void* x, const void* gamma, const void* beta, v
 
 hipError_t ln_fwd(int x_dtype, int p_dtype, int y_dtype, const void* x, const void* gamma,
                   const void* beta, void* y, float* mean, float* rstd, float* x_copy,
-                  int rows, int h, float eps, hipStream_t s, int* zero, int nzero) {
+                  int rows, int h, float eps, hipStream_t s) {
   if (p_dtype == DT_BF16 && y_dtype == DT_F16) {
     if (x_dtype == DT_BF16)
-      return ln_fwd_t<bf16, bf16, f16>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s, zero, nzero);
+      return ln_fwd_t<bf16, bf16, f16>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s);
     if (x_dtype == DT_F32)
-      return ln_fwd_t<float, bf16, f16>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s, zero, nzero);
+      return ln_fwd_t<float, bf16, f16>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s);
   }
   if (p_dtype == DT_F32 && y_dtype == DT_F32 && x_dtype == DT_F32)
-    return ln_fwd_t<float, float, float>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s, zero, nzero);
+    return ln_fwd_t<float, float, float>(x, gamma, beta, y, mean, rstd, x_copy, rows, h, eps, s);
   return hipErrorInvalidValue;
 }
 

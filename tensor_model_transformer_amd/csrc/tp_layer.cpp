@@ -76,11 +76,9 @@ struct tp_layer {
   Prof prof;
   // decode (one row per sequence): its own workspace plan
   struct Dec {
-    Region a, q, apart, o, h_mid, c, z, gpart, cnt;
+    Region a, apart, o, h_mid, c, z, gpart;
     size_t bytes;
-    int kc[4], ns[4];     // GEMV K split: qkv, w_o, fc1, fc2
-    int tiles[4];         // 64-column strips of each GEMV (arrival counters)
-    int cnt_attn, cnt_mlp;  // counters cleared by LN1 / LN2
+    int strip[4], chunk[4], kc[4], ns[4];  // GEMV tiling and K split: qkv, w_o, fc1, fc2
   } dec;
 };
 
@@ -192,9 +190,8 @@ void plan(tp_layer* L) {
 }
 
 // Decode workspace: the rows of one token per sequence (B = micro_batch), the
-// GEMV split-K partials, the attention slice partials and the arrival
-// counters: [qkv strips | attention (sequence, head) pairs | w_o strips]
-// cleared by LN1, then [fc1 strips | fc2 strips] cleared by LN2.
+// GEMV split-K partials (one buffer, the GEMVs run one after another) and the
+// attention slice partials.
 void plan_decode(tp_layer* L) {
   tp_layer::Dec& d = L->dec;
   size_t off = 0;
@@ -208,22 +205,18 @@ void plan_decode(tp_layer* L) {
                          {L->hidden, L->fl}};
   size_t gp = 0;
   for (int i = 0; i < 4; ++i) {
-    gemv_plan(L->batch, MNK[i][0], MNK[i][1], &d.kc[i], &d.ns[i]);
-    d.tiles[i] = (MNK[i][0] + 63) / 64;
-    if (d.ns[i] > 1) gp = std::max(gp, (size_t)d.ns[i] * B * MNK[i][0] * 4);
+    gemv_plan(L->adt, L->batch, MNK[i][0], MNK[i][1], &d.strip[i], &d.chunk[i], &d.kc[i],
+              &d.ns[i]);
+    gp = std::max(gp, (size_t)d.ns[i] * B * MNK[i][0] * 4);
   }
   const size_t pairs = B * L->Hl;
-  d.cnt_attn = d.tiles[0] + (int)pairs + d.tiles[1];
-  d.cnt_mlp = d.tiles[2] + d.tiles[3];
   take(d.a, B * h * e);
-  take(d.q, B * L->hl * 4);
   take(d.apart, ((size_t)kDecWaves + pairs) * (L->dh + 2) * 4);
   take(d.o, B * L->hl * e);
   take(d.h_mid, B * h * 4);
   take(d.c, B * h * e);
   take(d.z, B * L->fl * e);
   take(d.gpart, gp);
-  take(d.cnt, (size_t)(d.cnt_attn + d.cnt_mlp) * 4);
   d.bytes = off;
 }
 
@@ -662,64 +655,72 @@ int run_gemv(tp_layer* L, const GemvArgs& g, double out_e, hipStream_t s) {
   return TP_OK;
 }
 
-GemvArgs gemv_base(tp_layer* L, int which, void* ws, int* count) {
+GemvArgs gemv_base(tp_layer* L, int which, void* ws) {
   const tp_layer::Dec& d = L->dec;
   GemvArgs g = {};
   g.M = L->batch;
+  g.strip = d.strip[which];
+  g.chunk = d.chunk[which];
   g.kc = d.kc[which];
   g.nsplit = d.ns[which];
   g.part = at<float>(ws, d.gpart);
-  g.count = count;
   g.bias_dt = g.resid_dt = L->sdt;
   g.gelu_tanh = L->gelu_tanh;
   return g;
 }
 
-// x -> a -> qkv (q kept, K/V appended to the cache) -> o -> o @ W_o
-// [+ b_o + x] into `dst` (fp32 [B, h]).
+// x -> a -> qkv partials -> attention (sums them, appends K/V to the cache)
+// -> o -> o @ W_o. fused_ln (TP_ALL): the W_o partials are finished together
+// with LN2 (h_mid and c in the workspace); else the result [+ b_o + x] goes
+// to `dst` (fp32 [B, h]).
 int dec_attn_phase(tp_layer* L, const tp_params* p, const tp_decode_io* io, float* dst,
-                   bool designated, void* ws, hipStream_t s) {
+                   bool designated, bool fused_ln, bool* c_done, void* ws, hipStream_t s) {
   const tp_layer::Dec& d = L->dec;
   const int B = L->batch, h = L->hidden, hl = L->hl, D = L->dh;
-  int* cnt = at<int>(ws, d.cnt);
   int e;
+  // one workgroup per row sums the W_o partials in the fused kernel: only
+  // worth it while a row's partials are small
+  fused_ln = fused_ln && (size_t)d.ns[1] * h * 4 <= 131072;
+  *c_done = fused_ln;
   {
   Scope ps(L, s, TP_K_LN_FWD, 0, (double)B * h * 2 * L->esz);
   HIP_TRY(ln_fwd(L->sdt, L->sdt, L->adt, io->x, p->ln1_gamma, p->ln1_beta, at<void>(ws, d.a),
-                 nullptr, nullptr, nullptr, B, h, L->eps, s, cnt, d.cnt_attn));
+                 nullptr, nullptr, nullptr, B, h, L->eps, s));
   }
-  GemvArgs g = gemv_base(L, 0, ws, cnt);
+  GemvArgs g = gemv_base(L, 0, ws);
   g.N = 3 * hl; g.K = h;
   g.X = at<void>(ws, d.a); g.W = p->w_qkv;
-  g.epi = GEMV_EPI_QKV;
-  g.bias = p->b_qkv;
-  g.q = at<float>(ws, d.q);
-  g.kcache = io->k_cache; g.vcache = io->v_cache;
-  g.klo = L->split_scores ? (_Float16*)io->k_cache_lo : nullptr;
-  g.cache_dt = L->adt;
-  g.pos = io->positions; g.cache_len = io->cache_len;
-  g.Hl = L->Hl; g.D = D;
-  if ((e = run_gemv(L, g, 0.0, s))) return e;
+  g.raw = 1;  // the attention kernel sums the partials
+  if ((e = run_gemv(L, g, 4.0, s))) return e;
   {
   DecAttnArgs a = {};
-  a.q = at<float>(ws, d.q);
+  a.qkv_part = at<float>(ws, d.gpart); a.qkv_ns = d.ns[0];
+  a.b_qkv = p->b_qkv; a.bias_dt = L->sdt;
   a.kc = io->k_cache; a.vc = io->v_cache;
-  a.klo = L->split_scores ? (const _Float16*)io->k_cache_lo : nullptr;
+  a.klo = L->split_scores ? (_Float16*)io->k_cache_lo : nullptr;
   a.pos = io->positions;
   a.batch = B; a.Hl = L->Hl; a.cache_len = io->cache_len;
   a.nsplit = dec_attn_split(B, L->Hl, io->cache_len, &a.chunk);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   a.part = at<float>(ws, d.apart);
-  a.count = cnt + d.tiles[0];
   a.o = at<void>(ws, d.o); a.o_dt = L->adt;
   const double keys = (double)B * L->Hl * io->cache_len;
   Scope ps(L, s, TP_K_ATTN_FWD, 4.0 * D * keys,
-           keys * D * L->esz * (L->split_scores ? 3 : 2) + (double)B * hl * (4 + L->esz));
+           keys * D * L->esz * (L->split_scores ? 3 : 2) + (double)B * hl * L->esz);
   HIP_TRY(dec_attn(L->adt, a, D, L->split_scores, s));
   }
-  g = gemv_base(L, 1, ws, cnt + d.tiles[0] + B * L->Hl);
+  g = gemv_base(L, 1, ws);
   g.N = h; g.K = hl;
   g.X = at<void>(ws, d.o); g.W = p->w_o;
+  if (fused_ln) {
+    g.raw = 1;
+    if ((e = run_gemv(L, g, 4.0, s))) return e;
+    Scope ps(L, s, TP_K_LN_FWD, 0, (double)B * h * (4 + L->esz + 4 + L->esz) + 2.0 * h * L->esz);
+    HIP_TRY(dec_resid_ln(L->adt, at<float>(ws, d.gpart), g.nsplit, p->b_o, io->x,
+                         at<float>(ws, d.h_mid), p->ln2_gamma, p->ln2_beta, at<void>(ws, d.c), B,
+                         h, L->eps, s));
+    return TP_OK;
+  }
   g.epi = GEMV_EPI_OUT;
   if (designated) {
     g.bias = p->b_o;
@@ -730,25 +731,25 @@ int dec_attn_phase(tp_layer* L, const tp_params* p, const tp_decode_io* io, floa
 }
 
 // h_mid (fp32 [B, h]) -> c -> z -> z @ W_fc2 [+ b_fc2 + h_mid] into `out`.
+// With have_c, c = LN2(h_mid) is already in the workspace.
 int dec_mlp_phase(tp_layer* L, const tp_params* p, const float* h_mid, void* out, int out_dt,
-                  bool designated, void* ws, hipStream_t s) {
+                  bool designated, bool have_c, void* ws, hipStream_t s) {
   const tp_layer::Dec& d = L->dec;
   const int B = L->batch, h = L->hidden, fl = L->fl;
-  int* cnt = at<int>(ws, d.cnt) + d.cnt_attn;
   int e;
-  {
+  if (!have_c) {
   Scope ps(L, s, TP_K_LN_FWD, 0, (double)B * h * (4 + L->esz));
   HIP_TRY(ln_fwd(DT_F32, L->sdt, L->adt, h_mid, p->ln2_gamma, p->ln2_beta, at<void>(ws, d.c),
-                 nullptr, nullptr, nullptr, B, h, L->eps, s, cnt, d.cnt_mlp));
+                 nullptr, nullptr, nullptr, B, h, L->eps, s));
   }
-  GemvArgs g = gemv_base(L, 2, ws, cnt);
+  GemvArgs g = gemv_base(L, 2, ws);
   g.N = fl; g.K = h;
   g.X = at<void>(ws, d.c); g.W = p->w_fc1;
   g.epi = GEMV_EPI_GELU;
   g.bias = p->b_fc1;
   g.out = at<void>(ws, d.z); g.out_dt = L->adt;
   if ((e = run_gemv(L, g, L->esz, s))) return e;
-  g = gemv_base(L, 3, ws, cnt + d.tiles[2]);
+  g = gemv_base(L, 3, ws);
   g.N = h; g.K = fl;
   g.X = at<void>(ws, d.z); g.W = p->w_fc2;
   g.epi = GEMV_EPI_OUT;
@@ -920,13 +921,16 @@ int tp_layer_decode(tp_layer* L, int phase, const tp_decode_io* io, void* hip_st
   switch (phase) {
     case TP_ALL: {
       float* hm = at<float>(ws, L->dec.h_mid);
-      if ((e = dec_attn_phase(L, p, io, hm, true, ws, s))) return e;
-      return dec_mlp_phase(L, p, hm, io->out, L->sdt, true, ws, s);
+      bool have_c;
+      if ((e = dec_attn_phase(L, p, io, hm, true, true, &have_c, ws, s))) return e;
+      return dec_mlp_phase(L, p, hm, io->out, L->sdt, true, have_c, ws, s);
     }
-    case TP_FWD_ATTN:
-      return dec_attn_phase(L, p, io, (float*)io->out, designated, ws, s);
+    case TP_FWD_ATTN: {
+      bool have_c;
+      return dec_attn_phase(L, p, io, (float*)io->out, designated, false, &have_c, ws, s);
+    }
     default:
-      return dec_mlp_phase(L, p, io->h_mid, io->out, DT_F32, designated, ws, s);
+      return dec_mlp_phase(L, p, io->h_mid, io->out, DT_F32, designated, false, ws, s);
   }
 }
 

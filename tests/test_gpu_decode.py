@@ -30,11 +30,10 @@ def _wl(name, batch, hidden, heads, ffn, t=1, dtype="bf16", seed=60, rank=0, seq
                                     mask="causal"), rank=rank, seed=seed, affine="perturbed")
 
 
-def run_decode(w, cache_len, positions="ragged", scores=0, rank=None, phase_split=False):
+def run_decode(w, cache_len, positions="ragged", scores=0, rank=None):
     """One TP_ALL decode step of one rank on the GPU. Returns numpy results
     and the inputs it used."""
     import torch
-    from tensor_model_transformer_amd import binding as B
     from tensor_model_transformer_amd.shard import Shard, _check
 
     d = w.dims
@@ -45,7 +44,7 @@ def run_decode(w, cache_len, positions="ragged", scores=0, rank=None, phase_spli
     p = sh.upload_params(rank_params(w, r))
     xd = torch.from_numpy(x).to(sh.device).to(sh.dtype)
     kd, vd = sh.upload_cache(kc), sh.upload_cache(vc)
-    klo = torch.zeros_like(kd) if (scores == B.TP_SCORES_SPLIT) else None
+    klo = torch.zeros_like(kd) if sh.split_scores else None
     posd = torch.from_numpy(pos).to(sh.device)
     out = torch.empty(d.batch, d.hidden, dtype=sh.dtype, device=sh.device)
     print(f"[decode] {w.name} B={d.batch} h={d.hidden} dh={d.head_dim} L={cache_len} "
