@@ -50,9 +50,12 @@
  *    Every gradient of a parameter is written in fp32. With TP_DTYPE_BF16
  *    the activations and gradients kept inside the layer (LayerNorm outputs,
  *    qkv, attention output, FC1 pre/post activation and their gradients) are
- *    IEEE fp16, fed to fp16 MFMA (same rate as bf16 on gfx950); bf16 weights
- *    and dout are converted to fp16 as they are loaded, which is exact in
- *    fp16's normal range. The residual stream h_mid and its gradient are fp32.
+ *    IEEE fp16, fed to fp16 MFMA (same rate as bf16 on gfx950). The forward
+ *    phases copy the bf16 weights they use into fp16 copies in the workspace
+ *    (the backward reads those copies, so the weights must not change in
+ *    between), and the MLP backward copies dout to fp16; the conversion is
+ *    exact in fp16's normal range. The residual stream h_mid and its
+ *    gradient are fp32.
  *  - Exchange partials (the tensors the f/g all-reduce would sum) are fp32
  *    [n, h] buffers owned by the caller.
  *  - The caller owns all memory, including the workspace. The library never
@@ -378,7 +381,8 @@ enum {
   TP_K_LN_FWD = 3,    /* LayerNorm forward */
   TP_K_LN_BWD = 4,    /* LayerNorm backward + residual-gradient add */
   TP_K_REDUCE = 5,    /* column sums and partial reductions (bias / gamma / beta grads) */
-  TP_K_COUNT = 6
+  TP_K_CONVERT = 6,   /* bf16 -> fp16 copies of the weights and the upstream gradient */
+  TP_K_COUNT = 7
 };
 int tp_layer_profile(tp_layer *L, int enable);
 

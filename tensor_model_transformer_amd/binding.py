@@ -46,7 +46,7 @@ GRAD_FIELDS = tuple("d_" + f for f in PARAM_FIELDS)
 EXPORTS = ("tp_layer_create", "tp_layer_fwd", "tp_layer_bwd", "tp_layer_destroy",
            "tp_exchange_sum", "tp_layer_tap", "tp_layer_profile", "tp_layer_profile_read",
            "tp_layer_decode_workspace", "tp_layer_decode", "tp_layer_kv_fill")
-KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce")
+KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce", "convert")
 
 
 class tp_layer_opts(Structure):

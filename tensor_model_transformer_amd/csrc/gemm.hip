@@ -9,9 +9,9 @@
 //
 // 16-bit path: MFMA 32x32x16 on fp16 operands (v_mfma_f32_32x32x16_f16,
 // fp32 accumulate; the same rate as bf16 on gfx950) on LDS double-buffered
-// tiles. Internal activations are fp16; bf16 tensors at the layer boundary
-// (weights, the upstream gradient) are converted to fp16 as they are staged,
-// which is exact for every bf16 value in fp16's normal range. LDS always
+// tiles. Both operands are fp16 in memory: internal activations are fp16, and
+// the caller hands in fp16 copies of the bf16 tensors at the layer boundary
+// (weights, the upstream gradient), made once per step. LDS always
 // holds both operands K-contiguous ([rows][BK+8], 16-byte padding against
 // bank conflicts) so every MFMA operand
 // is one 16-byte LDS read. Operands that are contiguous along M or N in HBM
@@ -132,11 +132,14 @@ struct TileLoader {
   static constexpr int kChunks = ROWS * BK / 8;
   static constexpr int kPer = KMAJ ? (kChunks + NT - 1) / NT : 8 * ((ROWS * BK / 64 + NT - 1) / NT);
   uint4 st[kPer];
-  bool cvt;  // the source is bf16: convert to fp16 when staging into LDS
 
   // src(row, k) = KMAJ ? p[row*ld + k] : p[k*ld + row]; 16-bit elements.
   // The loaded registers are consumed only by store(), after the MFMAs of
   // the current tile, so the global-load latency overlaps the compute.
+  // EDGE = false: the tile lies wholly inside the matrix (every M, N and K
+  // of the layer's GEMMs is a multiple of the tile), so the loads carry no
+  // guards and their addresses are loop-invariant apart from k0.
+  template <bool EDGE>
   __device__ __forceinline__ void load(const uint16_t* __restrict__ p, long ld, int row0, int nrows,
                                        int k0, int K, int tid) {
     if constexpr (KMAJ) {
@@ -145,10 +148,19 @@ struct TileLoader {
         const int c = tid + i * NT;
         const int row = c / (BK / 8), kc = c % (BK / 8);
         const int gr = row0 + row, gk = k0 + 8 * kc;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (c < kChunks && gr < nrows && gk < K)
-          v = *reinterpret_cast<const uint4*>(p + (size_t)gr * ld + gk);
-        st[i] = v;
+        if constexpr (!EDGE) {
+          // 32-bit element offsets (checked on the host): scalar base + one
+          // offset register per load
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (kChunks % NT == 0 || c < kChunks)
+            v = *reinterpret_cast<const uint4*>(p + (uint32_t)(gr * (int)ld + gk));
+          st[i] = v;
+        } else {
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (c < kChunks && gr < nrows && gk < K)
+            v = *reinterpret_cast<const uint4*>(p + (size_t)gr * ld + gk);
+          st[i] = v;
+        }
       }
     } else {
       constexpr int nblk = ROWS * BK / 64;
@@ -160,10 +172,17 @@ struct TileLoader {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int gk = k0 + 8 * kb + r;
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (b < nblk && gr < nrows && gk < K)
-            v = *reinterpret_cast<const uint4*>(p + (size_t)gk * ld + gr);
-          st[8 * i + r] = v;
+          if constexpr (!EDGE) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (nblk % NT == 0 || b < nblk)
+              v = *reinterpret_cast<const uint4*>(p + (uint32_t)(gk * (int)ld + gr));
+            st[8 * i + r] = v;
+          } else {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (b < nblk && gr < nrows && gk < K)
+              v = *reinterpret_cast<const uint4*>(p + (size_t)gk * ld + gr);
+            st[8 * i + r] = v;
+          }
         }
       }
     }
@@ -178,7 +197,7 @@ struct TileLoader {
         const int c = tid + i * NT;
         const int row = c / (BK / 8), kc = c % (BK / 8);
         if (c < kChunks)
-          *reinterpret_cast<uint4*>(lds + row * LDK + 8 * kc) = cvt ? bf16x8_to_f16x8(st[i]) : st[i];
+          *reinterpret_cast<uint4*>(lds + row * LDK + 8 * kc) = st[i];
       }
     } else {
       constexpr int nblk = ROWS * BK / 64;
@@ -188,10 +207,6 @@ struct TileLoader {
         const int kb = b % (BK / 8), rb = b / (BK / 8);
         if (b < nblk) {
           uint4 w[8];
-          if (cvt) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) st[8 * i + r] = bf16x8_to_f16x8(st[8 * i + r]);
-          }
           transpose8x8(&st[8 * i], w);
 #pragma unroll
           for (int j = 0; j < 8; ++j)
@@ -202,7 +217,7 @@ struct TileLoader {
   }
 };
 
-template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM>
+template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM, bool EDGE>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int ktiles_per_split) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -229,8 +244,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
   const uint16_t* B = (const uint16_t*)g.B;
   TileLoader<BM, BK, NT, AK> la;
   TileLoader<BN, BK, NT, BKM> lb;
-  la.cvt = g.a_dtype == DT_BF16;
-  lb.cvt = g.b_dtype == DT_BF16;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -241,8 +254,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   if (kt0 < kt1) {
-    la.load(A, g.lda, m0, g.M, kt0 * BK, g.K, tid);
-    lb.load(B, g.ldb, n0, g.N, kt0 * BK, g.K, tid);
+    la.template load<EDGE>(A, g.lda, m0, g.M, kt0 * BK, g.K, tid);
+    lb.template load<EDGE>(B, g.ldb, n0, g.N, kt0 * BK, g.K, tid);
     la.store(As, tid);
     lb.store(Bs, tid);
     __syncthreads();
@@ -252,8 +265,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
     const int cur = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) {
-      la.load(A, g.lda, m0, g.M, (kt + 1) * BK, g.K, tid);
-      lb.load(B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, tid);
+      la.template load<EDGE>(A, g.lda, m0, g.M, (kt + 1) * BK, g.K, tid);
+      lb.template load<EDGE>(B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, tid);
     }
     const uint16_t* as = As + cur * BM * LDK + (wm * WTM + lrow) * LDK + lk;
     const uint16_t* bs = Bs + cur * BN * LDK + (wn * WTN + lrow) * LDK + lk;
@@ -456,17 +469,23 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
   constexpr int BK = 64;
   constexpr int NT = WM * WN * 64;
   const size_t lds = (size_t)2 * (BM + BN) * (BK + 8) * sizeof(uint16_t);
-  auto kern = gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM>;
-  static bool attr_set = false;  // per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int ktiles = (int)ceil_div(g.K, BK);
   const int per = (int)ceil_div(ktiles, split);
   const int real_split = (int)ceil_div(ktiles, per);
+  // every tile inside the matrix: no guards on the operand loads, and the
+  // element offsets of both operands fit 31 bits
+  const bool interior = g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0 &&
+                        (size_t)(g.a_kmajor ? g.M : g.K) * g.lda < (1u << 31) &&
+                        (size_t)(g.b_kmajor ? g.N : g.K) * g.ldb < (1u << 31);
+  auto kern = interior ? gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM, false>
+                       : gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM, true>;
+  static bool attr_set[2] = {false, false};  // per instantiation
+  if (!attr_set[interior]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set[interior] = true;
+  }
   dim3 grid((unsigned)(ceil_div(g.M, BM) * ceil_div(g.N, BN)), (unsigned)real_split);
   GemmArgs a = g;
   a.split = real_split;
@@ -509,7 +528,7 @@ hipError_t gemm(const GemmArgs& g, hipStream_t s) {
   if (split > 1 && (!g.ws || g.epi != EPI_STORE || g.bias || g.resid || g.c_dtype != DT_F32))
     return hipErrorInvalidValue;
   if (g.math == DT_F16) {
-    if (g.a_dtype == DT_F32 || g.b_dtype == DT_F32) return hipErrorInvalidValue;
+    if (g.a_dtype != DT_F16 || g.b_dtype != DT_F16) return hipErrorInvalidValue;
     // 16-byte operand chunks: the contiguous dimension must be a multiple of 8
     if (g.a_kmajor ? (g.K % 8) : (g.M % 8)) return hipErrorInvalidValue;
     if (g.b_kmajor ? (g.K % 8) : (g.N % 8)) return hipErrorInvalidValue;

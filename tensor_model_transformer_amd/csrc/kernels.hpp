@@ -56,6 +56,10 @@ hipError_t reduce_partials(const float* part, int nblk, int nout, int width,
                            hipStream_t s);
 size_t reduce_scratch_floats(int nblk, int nout, int width);
 
+// dst[k][i] = fp16(src[k][i]) for bf16 src, i < count[k], k < nseg (1..4).
+hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
+                  hipStream_t s);
+
 // dst[i] = sum_p parts[p][i]  (fp32 sum in order), written as dst_dtype.
 hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts,
                         int nparts, size_t count, hipStream_t s);
@@ -66,8 +70,8 @@ hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts,
 enum { EPI_STORE = 0, EPI_BIAS_GELU = 1, EPI_DGELU = 2, EPI_SPLIT16 = 3 };
 
 struct GemmArgs {
-  // Arithmetic: DT_F32 (fp32 FMA) or DT_F16 (fp16 MFMA, fp32 accumulate;
-  // bf16 operands are converted to fp16 while staged into LDS).
+  // Arithmetic: DT_F32 (fp32 FMA, fp32 operands) or DT_F16 (fp16 MFMA,
+  // fp32 accumulate, fp16 operands).
   int math;
   int M, N, K;
   // A(m,k) = A[m*lda + k] if a_kmajor else A[k*lda + m]

@@ -5,6 +5,8 @@
 // LayerNorm placement follows "Megatron-LM: GPU-Cluster Training Parallelism",
 // section "Paper 1: BERT LayerNorm Rearrangement" (pre-LN: each sublayer reads
 // LN of the residual stream, whose un-normalised value is carried forward).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -390,6 +392,58 @@ hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts, int
     else
       exchange_sum_tail_kernel<float><<<1, 64, 0, s>>>((float*)dst, pp, nparts, nvec * 8, count);
   }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// bf16 -> fp16 copies of up to 4 tensors in one launch (the weights and the
+// upstream gradient the fp16 MFMA GEMMs read). Round to nearest even; every
+// bf16 value inside fp16's normal range converts exactly. 8 elements per
+// thread per step, grid-stride; tails (count % 8) element by element.
+// ----------------------------------------------------------------------------
+struct CvtSegs {
+  const bf16* src[4];
+  f16* dst[4];
+  size_t n[4];
+  size_t start[5];  // prefix sums of the vector counts
+  int nseg;
+};
+
+__global__ __launch_bounds__(256) void to_f16_kernel(CvtSegs c) {
+  const size_t total = c.start[c.nseg];
+  for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < total;
+       v += (size_t)gridDim.x * 256) {
+    int sg = 0;
+    while (sg + 1 < c.nseg && v >= c.start[sg + 1]) ++sg;
+    const size_t i = 8 * (v - c.start[sg]);
+    const bf16* src = c.src[sg] + i;
+    f16* dst = c.dst[sg] + i;
+    if (i + 8 <= c.n[sg]) {
+      float f[8];
+      Vec8<bf16>::load(src, f);
+      Vec8<f16>::store(dst, f);
+    } else {
+      for (size_t e = i; e < c.n[sg]; ++e) c.dst[sg][e] = (f16)bf2f(c.src[sg][e]);
+    }
+  }
+}
+
+hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
+                  hipStream_t s) {
+  if (nseg < 1 || nseg > 4) return hipErrorInvalidValue;
+  CvtSegs c = {};
+  c.nseg = nseg;
+  c.start[0] = 0;
+  for (int i = 0; i < nseg; ++i) {
+    c.src[i] = (const bf16*)src[i];
+    c.dst[i] = (f16*)dst[i];
+    c.n[i] = count[i];
+    c.start[i + 1] = c.start[i] + (count[i] + 7) / 8;
+  }
+  const size_t total = c.start[nseg];
+  if (!total) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 8192);
+  to_f16_kernel<<<grid, 256, 0, s>>>(c);
   return hipGetLastError();
 }
 

@@ -70,6 +70,9 @@ struct tp_layer {
   // workspace regions
   Region mean1, rstd1, a, qkv, qkv_lo, o, lse2, h_mid, mean2, rstd2, c, u, z;
   Region du, dc, dh_f, dh_s, dO, delta, dqkv, da, part, splitk;
+  // fp16 copies of the bf16 weights (made by the forward, read again by the
+  // backward) and of the upstream gradient: the MFMA GEMMs read fp16 only
+  Region w16_qkv, w16_o, w16_fc1, w16_fc2, dout16;
   size_t ws_bytes;
   int split_w2, split_w1, split_wo, split_wqkv;
   double attn_pairs;  // allowed query-key pairs (causal); 0 for padding (lengths on device)
@@ -186,6 +189,12 @@ void plan(tp_layer* L) {
     }
   }
   take(L->splitk, sk);
+  const bool cvt = L->sdt == DT_BF16;
+  take(L->w16_qkv, cvt ? h * 3 * L->hl * 2 : 0);
+  take(L->w16_o, cvt ? (size_t)L->hl * h * 2 : 0);
+  take(L->w16_fc1, cvt ? h * L->fl * 2 : 0);
+  take(L->w16_fc2, cvt ? (size_t)L->fl * h * 2 : 0);
+  take(L->dout16, cvt ? n * h * 2 : 0);
   L->ws_bytes = off;
 }
 
@@ -227,6 +236,11 @@ T* at(void* ws, const Region& r) {
 
 // The fp16 residuals of qkv, or null when scores use qkv alone.
 void* qkv_lo(tp_layer* L, void* ws) { return L->split_scores ? at<void>(ws, L->qkv_lo) : nullptr; }
+
+// A weight as the GEMMs read it: the fp16 copy for a bf16 layer, else itself.
+const void* wmat(tp_layer* L, void* ws, const Region& copy, const void* w) {
+  return L->sdt == DT_BF16 ? at<void>(ws, copy) : w;
+}
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -309,6 +323,30 @@ int run_gemm(tp_layer* L, const GemmArgs& g, hipStream_t s) {
   return TP_OK;
 }
 
+// bf16 -> fp16 copies (nothing to do for an fp32 layer).
+int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
+                  std::initializer_list<const Region*> dst, std::initializer_list<size_t> count,
+                  void* ws, hipStream_t s) {
+  if (L->sdt != DT_BF16) return TP_OK;
+  const void* sp[4];
+  void* dp[4];
+  size_t np[4];
+  int k = 0;
+  double bytes = 0;
+  auto d = dst.begin();
+  auto c = count.begin();
+  for (const void* x : src) {
+    sp[k] = x;
+    dp[k] = at<void>(ws, **d++);
+    np[k] = *c++;
+    bytes += 4.0 * np[k];
+    ++k;
+  }
+  Scope ps(L, s, TP_K_CONVERT, 0, bytes);
+  HIP_TRY(to_f16(sp, dp, np, k, s));
+  return TP_OK;
+}
+
 // ---- forward pieces --------------------------------------------------------
 // x -> a -> qkv -> o -> (o @ W_o) [+ b_o + x] into `dst` (fp32 [n, h]).
 // With a_in (the sequence-parallel layout) LN1 has run per chunk already and
@@ -318,6 +356,9 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   const int n = L->n, h = L->hidden, hl = L->hl;
   int e;
   const double nh = (double)n * h;
+  if ((e = to_f16_copies(L, {p->w_qkv, p->w_o}, {&L->w16_qkv, &L->w16_o},
+                         {(size_t)h * 3 * hl, (size_t)hl * h}, ws, s)))
+    return e;
   if (!a_in) {
   Scope ps(L, s, TP_K_LN_FWD, 0, nh * 2 * L->esz + 8.0 * n);
   HIP_TRY(ln_fwd(L->sdt, L->sdt, L->adt, x, p->ln1_gamma, p->ln1_beta, at<void>(ws, L->a),
@@ -326,7 +367,7 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   GemmArgs g = gemm_base(L);
   g.M = n; g.N = 3 * hl; g.K = h;
   g.A = a_in ? a_in : at<void>(ws, L->a); g.lda = h; g.a_kmajor = 1;
-  g.B = p->w_qkv; g.ldb = 3 * hl; g.b_kmajor = 0; g.b_dtype = L->sdt;
+  g.B = wmat(L, ws, L->w16_qkv, p->w_qkv); g.ldb = 3 * hl; g.b_kmajor = 0;
   g.bias = p->b_qkv;
   g.C = at<void>(ws, L->qkv); g.ldc = 3 * hl;
   if (L->split_scores) {
@@ -344,7 +385,7 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = hl;
   g.A = at<void>(ws, L->o); g.lda = hl; g.a_kmajor = 1;
-  g.B = p->w_o; g.ldb = h; g.b_kmajor = 0; g.b_dtype = L->sdt;
+  g.B = wmat(L, ws, L->w16_o, p->w_o); g.ldb = h; g.b_kmajor = 0;
   if (designated) {
     g.bias = p->b_o;
     g.resid = x; g.ldr = h; g.resid_dtype = L->sdt;
@@ -362,6 +403,9 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
   float* h_mid = at<float>(ws, L->h_mid);
+  if ((e = to_f16_copies(L, {p->w_fc1, p->w_fc2}, {&L->w16_fc1, &L->w16_fc2},
+                         {(size_t)h * fl, (size_t)fl * h}, ws, s)))
+    return e;
   if (!c_in) {
   Scope ps(L, s, TP_K_LN_FWD, 0,
            (double)n * h * (4 + L->esz + (h_mid_in == h_mid ? 0 : 4)) + 8.0 * n);
@@ -372,7 +416,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   GemmArgs g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
   g.A = c_in ? c_in : at<void>(ws, L->c); g.lda = h; g.a_kmajor = 1;
-  g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 0; g.b_dtype = L->sdt;
+  g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 0;
   g.bias = p->b_fc1;
   g.epi = EPI_BIAS_GELU;
   g.C = L->recompute_fc1 ? nullptr : at<void>(ws, L->u); g.ldc = fl;
@@ -381,7 +425,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = fl;
   g.A = at<void>(ws, L->z); g.lda = fl; g.a_kmajor = 1;
-  g.B = p->w_fc2; g.ldb = h; g.b_kmajor = 0; g.b_dtype = L->sdt;
+  g.B = wmat(L, ws, L->w16_fc2, p->w_fc2); g.ldb = h; g.b_kmajor = 0;
   if (designated) {
     g.bias = p->b_fc2;
     g.resid = h_mid; g.ldr = h; g.resid_dtype = DT_F32;
@@ -436,7 +480,10 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
             int db2_rows = -1) {
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
+  // the upstream gradient as the GEMMs read it (fp16 copy for a bf16 layer)
   const void* dout = dout_full ? dout_full : io->dout;
+  if ((e = to_f16_copies(L, {dout}, {&L->dout16}, {(size_t)n * h}, ws, s))) return e;
+  if (L->sdt == DT_BF16) dout = at<void>(ws, L->dout16);
   const void* c_act = c_in ? c_in : at<void>(ws, L->c);
   float* skw = at<float>(ws, L->splitk);
   GemmArgs g;
@@ -445,7 +492,7 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
     g = gemm_base(L);
     g.M = n; g.N = fl; g.K = h;
     g.A = c_act; g.lda = h; g.a_kmajor = 1;
-    g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 0; g.b_dtype = L->sdt;
+    g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 0;
     g.bias = p->b_fc1;
     g.C = at<void>(ws, L->du); g.ldc = fl;
     if ((e = run_gemm(L, g, s))) return e;
@@ -455,8 +502,8 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   // same thread of the epilogue)
   g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
-  g.A = dout; g.lda = h; g.a_kmajor = 1; g.a_dtype = L->sdt;
-  g.B = p->w_fc2; g.ldb = h; g.b_kmajor = 1; g.b_dtype = L->sdt;
+  g.A = dout; g.lda = h; g.a_kmajor = 1;
+  g.B = wmat(L, ws, L->w16_fc2, p->w_fc2); g.ldb = h; g.b_kmajor = 1;
   g.epi = EPI_DGELU;
   g.aux = at<void>(ws, L->recompute_fc1 ? L->du : L->u); g.ldaux = fl;
   g.C = at<void>(ws, L->du); g.ldc = fl;
@@ -464,7 +511,6 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s, db2_rows)))
     return e;
   g = wgrad_args(L, fl, h, at<void>(ws, L->z), dout, io->d_w_fc2, io->accumulate);
-  g.b_dtype = L->sdt;
   g.split = L->split_w2; g.ws = skw;
   if ((e = run_gemm(L, g, s))) return e;
   g = wgrad_args(L, h, fl, c_act, at<void>(ws, L->du), io->d_w_fc1, io->accumulate);
@@ -475,7 +521,7 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = fl;
   g.A = at<void>(ws, L->du); g.lda = fl; g.a_kmajor = 1;
-  g.B = p->w_fc1; g.ldb = fl; g.b_kmajor = 1; g.b_dtype = L->sdt;
+  g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 1;
   g.C = dc_out; g.ldc = h; g.c_dtype = DT_F32;
   return run_gemm(L, g, s);
 }
@@ -502,7 +548,7 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
   GemmArgs g = gemm_base(L);
   g.M = n; g.N = hl; g.K = h;
   g.A = dh_s; g.lda = h; g.a_kmajor = 1;
-  g.B = p->w_o; g.ldb = h; g.b_kmajor = 1; g.b_dtype = L->sdt;
+  g.B = wmat(L, ws, L->w16_o, p->w_o); g.ldb = h; g.b_kmajor = 1;
   g.C = at<void>(ws, L->dO); g.ldc = hl;
   if ((e = run_gemm(L, g, s))) return e;
   g = wgrad_args(L, hl, h, at<void>(ws, L->o), dh_s, io->d_w_o, io->accumulate);
@@ -525,7 +571,7 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = 3 * hl;
   g.A = at<void>(ws, L->dqkv); g.lda = 3 * hl; g.a_kmajor = 1;
-  g.B = p->w_qkv; g.ldb = 3 * hl; g.b_kmajor = 1; g.b_dtype = L->sdt;
+  g.B = wmat(L, ws, L->w16_qkv, p->w_qkv); g.ldb = 3 * hl; g.b_kmajor = 1;
   g.C = da_out; g.ldc = h; g.c_dtype = DT_F32;
   return run_gemm(L, g, s);
 }
