@@ -66,28 +66,6 @@ __device__ __forceinline__ f16x8 pack8v(const f32x16& a, int off) {
   return pack8(v);
 }
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-#define LDS_V4S(p) ((__attribute__((address_space(3))) v4s*)(p))
-
-// Four 16-bit values of one column of a row-major LDS tile T (pitch P
-// elements), read transposed with ds_read_b64_tr_b16: within each 16-lane
-// group, lane j receives T[k0 + i][mb + j] for i = 0..3 when input lane L
-// points at T[k0 + L/4][mb + 4*(L%4)].
-__device__ __forceinline__ uint2 tr4(const f16* T, int P, int k0, int mb, int L) {
-  const f16* p = T + (k0 + (L >> 2)) * P + mb + 4 * (L & 3);
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_V4S(p)));
-}
-
-// MFMA operand whose rows are columns m0 .. m0+31 of the row-major tile T
-// (this lane's column m0 + lane%32) and whose 8 reduction slots are the tile
-// rows kA + 0..3 then kB + 0..3, with (kA, kB) given for lane half h.
-__device__ __forceinline__ f16x8 tr_frag(const f16* T, int P, int m0, int kA, int kB, int lane) {
-  const int g = lane >> 4, L = lane & 15;
-  const int mb = m0 + 16 * (g & 1);
-  const uint2 a = tr4(T, P, kA, mb, L), b = tr4(T, P, kB, mb, L);
-  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
-}
-
 // Register staging for a [R][D] row-major slice of global memory (row stride
 // ld), rows >= nrows read as zero; stored into an LDS tile of pitch P. The
 // address is clamped to the last row (nrows >= 1) and the value selected.

@@ -51,17 +51,6 @@ __device__ __forceinline__ void st_dt(void* p, int dt, size_t i, float v) {
   else ((f16*)p)[i] = (f16)v;
 }
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-#define DEC_LDS_V4S(p) ((__attribute__((address_space(3))) v4s*)(p))
-
-// Four fp16 values of column mb + j of a row-major LDS tile T (pitch P),
-// rows k0..k0+3, for lane j of each 16-lane group (ds_read_b64_tr_b16: lane L
-// of the group addresses row k0 + L/4, columns mb + 4*(L%4) .. +3).
-__device__ __forceinline__ uint2 tr4(const f16* T, int P, int k0, int mb, int L) {
-  const f16* p = T + (k0 + (L >> 2)) * P + mb + 4 * (L & 3);
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(DEC_LDS_V4S(p)));
-}
-
 // One output element of a decode GEMV: v is the full K sum.
 __device__ __forceinline__ void gemv_epilogue(const GemvArgs& g, int m, int n, float v) {
   if (g.bias) v += ld_dt(g.bias, g.bias_dt, n);

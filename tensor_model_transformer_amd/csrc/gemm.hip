@@ -11,13 +11,13 @@
 // fp32 accumulate; the same rate as bf16 on gfx950) on LDS double-buffered
 // tiles. Both operands are fp16 in memory: internal activations are fp16, and
 // the caller hands in fp16 copies of the bf16 tensors at the layer boundary
-// (weights, the upstream gradient), made once per step. LDS always
-// holds both operands K-contiguous ([rows][BK+8], 16-byte padding against
-// bank conflicts) so every MFMA operand
-// is one 16-byte LDS read. Operands that are contiguous along M or N in HBM
-// (weights [in,out] in forward; both operands of a weight gradient) are
-// transposed in registers, 8x8 blocks of 16-bit values at a time, between the global load
-// and the LDS store. The MFMA is issued with B as the first operand, so the
+// (weights, the upstream gradient), made once per step. An operand
+// tile keeps its HBM orientation in LDS: K-contiguous operands as
+// [rows][BK+8] (each MFMA fragment one 16-byte LDS read), operands that are
+// contiguous along M or N (weights [in,out] in forward; both operands of a
+// weight gradient) as [BK][rows+16], whose fragments come from
+// ds_read_b64_tr_b16, gfx950's transposing LDS read, so nothing is transposed
+// in registers. The MFMA is issued with B as the first operand, so the
 // accumulator holds C transposed: each lane owns one output row and 4
 // consecutive columns per 32x32 tile, which the epilogue writes as one vector.
 //
@@ -107,30 +107,23 @@ __device__ __forceinline__ void partial4(const GemmArgs& g, int split_idx, int m
 // ----------------------------------------------------------------------------
 // fp16 MFMA GEMM
 // ----------------------------------------------------------------------------
-// In-register transpose of an 8x8 block of 16-bit values: r[i] holds 8 elements of
-// source row i; w[j] receives element j of every source row.
-__device__ __forceinline__ void transpose8x8(const uint4 r[8], uint4 w[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t* lo = reinterpret_cast<const uint32_t*>(&r[2 * p]);
-      const uint32_t* hi = reinterpret_cast<const uint32_t*>(&r[2 * p + 1]);
-      // low half <- element j of row 2p, high half <- element j of row 2p+1
-      o[p] = __builtin_amdgcn_perm(hi[j >> 1], lo[j >> 1],
-                                   (j & 1) ? 0x07060302u : 0x05040100u);
-    }
-    w[j] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
+// LDS pitch (16-bit elements) of an operand tile: K-contiguous tiles are
+// [ROWS][BK + 8] (16-byte MFMA fragment reads); row-contiguous tiles are
+// [BK][ROWS + 16], read with ds_read_b64_tr_b16 (each 16-lane group reads 4
+// rows x 32 bytes; the +16 pad puts the 4 rows on disjoint banks).
+template <int ROWS, int BK, bool KMAJ>
+struct TilePitch {
+  static constexpr int P = KMAJ ? BK + 8 : ROWS + 16;
+  static constexpr int kElems = KMAJ ? ROWS * (BK + 8) : BK * (ROWS + 16);
+};
 
 template <int ROWS, int BK, int NT, bool KMAJ>
 struct TileLoader {
-  // K-contiguous source: 16-byte chunks of 8 k-values; ROWS*BK/8 chunks.
-  // Row-contiguous source: 8(k) x 8(row) blocks; ROWS*BK/64 blocks.
+  // 16-byte chunks of 8 elements along the contiguous dimension:
+  // K-contiguous source: chunk (row, 8 k); row-contiguous source: (k, 8 rows).
   static constexpr int kChunks = ROWS * BK / 8;
-  static constexpr int kPer = KMAJ ? (kChunks + NT - 1) / NT : 8 * ((ROWS * BK / 64 + NT - 1) / NT);
+  static constexpr int kPer = (kChunks + NT - 1) / NT;
+  static constexpr int kPerRow = KMAJ ? BK / 8 : ROWS / 8;  // chunks per contiguous line
   uint4 st[kPer];
 
   // src(row, k) = KMAJ ? p[row*ld + k] : p[k*ld + row]; 16-bit elements.
@@ -138,96 +131,66 @@ struct TileLoader {
   // the current tile, so the global-load latency overlaps the compute.
   // EDGE = false: the tile lies wholly inside the matrix (every M, N and K
   // of the layer's GEMMs is a multiple of the tile), so the loads carry no
-  // guards and their addresses are loop-invariant apart from k0.
+  // guards, and the element offsets fit 32 bits (checked on the host).
   template <bool EDGE>
   __device__ __forceinline__ void load(const uint16_t* __restrict__ p, long ld, int row0, int nrows,
                                        int k0, int K, int tid) {
-    if constexpr (KMAJ) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / (BK / 8), kc = c % (BK / 8);
-        const int gr = row0 + row, gk = k0 + 8 * kc;
-        if constexpr (!EDGE) {
-          // 32-bit element offsets (checked on the host): scalar base + one
-          // offset register per load
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (kChunks % NT == 0 || c < kChunks)
-            v = *reinterpret_cast<const uint4*>(p + (uint32_t)(gr * (int)ld + gk));
-          st[i] = v;
-        } else {
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (c < kChunks && gr < nrows && gk < K)
-            v = *reinterpret_cast<const uint4*>(p + (size_t)gr * ld + gk);
-          st[i] = v;
-        }
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      const int line = c / kPerRow, w = c % kPerRow;
+      // KMAJ: line = row, w = k chunk; else line = k, w = row chunk
+      const int gr = KMAJ ? row0 + line : row0 + 8 * w;
+      const int gk = KMAJ ? k0 + 8 * w : k0 + line;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if constexpr (!EDGE) {
+        if (kChunks % NT == 0 || c < kChunks)
+          v = *reinterpret_cast<const uint4*>(
+              p + (uint32_t)(KMAJ ? gr * (int)ld + gk : gk * (int)ld + gr));
+      } else {
+        if ((kChunks % NT == 0 || c < kChunks) && gr < nrows && gk < K)
+          v = *reinterpret_cast<const uint4*>(
+              p + (KMAJ ? (size_t)gr * ld + gk : (size_t)gk * ld + gr));
       }
-    } else {
-      constexpr int nblk = ROWS * BK / 64;
-#pragma unroll
-      for (int i = 0; i < kPer / 8; ++i) {
-        const int b = tid + i * NT;
-        const int kb = b % (BK / 8), rb = b / (BK / 8);
-        const int gr = row0 + 8 * rb;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int gk = k0 + 8 * kb + r;
-          if constexpr (!EDGE) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (nblk % NT == 0 || b < nblk)
-              v = *reinterpret_cast<const uint4*>(p + (uint32_t)(gk * (int)ld + gr));
-            st[8 * i + r] = v;
-          } else {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (b < nblk && gr < nrows && gk < K)
-              v = *reinterpret_cast<const uint4*>(p + (size_t)gk * ld + gr);
-            st[8 * i + r] = v;
-          }
-        }
-      }
+      st[i] = v;
     }
   }
 
-  // LDS tile: [ROWS][BK + 8] fp16, K-contiguous.
   __device__ __forceinline__ void store(uint16_t* lds, int tid) {
-    constexpr int LDK = BK + 8;
-    if constexpr (KMAJ) {
+    constexpr int P = TilePitch<ROWS, BK, KMAJ>::P;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / (BK / 8), kc = c % (BK / 8);
-        if (c < kChunks)
-          *reinterpret_cast<uint4*>(lds + row * LDK + 8 * kc) = st[i];
-      }
-    } else {
-      constexpr int nblk = ROWS * BK / 64;
-#pragma unroll
-      for (int i = 0; i < kPer / 8; ++i) {
-        const int b = tid + i * NT;
-        const int kb = b % (BK / 8), rb = b / (BK / 8);
-        if (b < nblk) {
-          uint4 w[8];
-          transpose8x8(&st[8 * i], w);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<uint4*>(lds + (8 * rb + j) * LDK + 8 * kb) = w[j];
-        }
-      }
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      if (kChunks % NT == 0 || c < kChunks)
+        *reinterpret_cast<uint4*>(lds + (c / kPerRow) * P + 8 * (c % kPerRow)) = st[i];
     }
   }
 };
+
+// MFMA operand fragment of rows r0 .. r0+31 of an operand tile for K step
+// ks (16 k), this lane's row r0 + lane%32 and k = 16 ks + 8 (lane/32) + 0..7.
+template <int ROWS, int BK, bool KMAJ>
+__device__ __forceinline__ f16x8 frag(const uint16_t* tile, int r0, int ks, int lane) {
+  constexpr int P = TilePitch<ROWS, BK, KMAJ>::P;
+  const int kA = 16 * ks + 8 * (lane >> 5);
+  if constexpr (KMAJ) {
+    return *reinterpret_cast<const f16x8*>(tile + (r0 + (lane & 31)) * P + kA);
+  } else {
+    return tr_frag(reinterpret_cast<const f16*>(tile), P, r0, kA, kA + 4, lane);
+  }
+}
 
 template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM, bool EDGE>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int ktiles_per_split) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int LDK = BK + 8;
+  constexpr int AE = TilePitch<BM, BK, AK>::kElems, BE = TilePitch<BN, BK, BKM>::kElems;
   static_assert(TM >= 1 && TN >= 1 && BK % 16 == 0, "tile shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* As = reinterpret_cast<uint16_t*>(smem);       // [2][BM*LDK] fp16
-  uint16_t* Bs = As + 2 * BM * LDK;                       // [2][BN*LDK] fp16
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);       // [2][AE] fp16
+  uint16_t* Bs = As + 2 * AE;                             // [2][BE] fp16
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -260,7 +223,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
     lb.store(Bs, tid);
     __syncthreads();
   }
-  const int lrow = lane & 31, lk = 8 * (lane >> 5);
+  const int lrow = lane & 31;
   for (int kt = kt0; kt < kt1; ++kt) {
     const int cur = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
@@ -268,17 +231,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
       la.template load<EDGE>(A, g.lda, m0, g.M, (kt + 1) * BK, g.K, tid);
       lb.template load<EDGE>(B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, tid);
     }
-    const uint16_t* as = As + cur * BM * LDK + (wm * WTM + lrow) * LDK + lk;
-    const uint16_t* bs = Bs + cur * BN * LDK + (wn * WTN + lrow) * LDK + lk;
+    const uint16_t* as = As + cur * AE;
+    const uint16_t* bs = Bs + cur * BE;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       f16x8 af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const f16x8*>(as + i * 32 * LDK + ks * 16);
+      for (int i = 0; i < TM; ++i) af[i] = frag<BM, BK, AK>(as, wm * WTM + 32 * i, ks, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const f16x8*>(bs + j * 32 * LDK + ks * 16);
+      for (int j = 0; j < TN; ++j) bfr[j] = frag<BN, BK, BKM>(bs, wn * WTN + 32 * j, ks, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -286,8 +247,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
     if (more) {
-      la.store(As + (cur ^ 1) * BM * LDK, tid);
-      lb.store(Bs + (cur ^ 1) * BN * LDK, tid);
+      la.store(As + (cur ^ 1) * AE, tid);
+      lb.store(Bs + (cur ^ 1) * BE, tid);
     }
     __syncthreads();
   }
@@ -300,7 +261,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
   // written by adjacent lanes (coalesced) and acc is only ever indexed by
   // constants.
   constexpr int CP = WTN + 4;  // fp32 pitch of a slice row
-  static_assert(2 * (BM + BN) * LDK * 2 >= WM * WN * 32 * CP * 4, "epilogue slices fit in LDS");
+  static_assert(2 * (AE + BE) * 2 >= WM * WN * 32 * CP * 4, "epilogue slices fit in LDS");
   float* cs = reinterpret_cast<float*>(smem) + wid * 32 * CP;
   const int half = lane >> 5;
   __syncthreads();  // every wave is done with the operand tiles
@@ -468,7 +429,9 @@ template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
 static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
   constexpr int BK = 64;
   constexpr int NT = WM * WN * 64;
-  const size_t lds = (size_t)2 * (BM + BN) * (BK + 8) * sizeof(uint16_t);
+  const size_t lds = (size_t)2 *
+                     (TilePitch<BM, BK, AK>::kElems + TilePitch<BN, BK, BKM>::kElems) *
+                     sizeof(uint16_t);
   const int ktiles = (int)ceil_div(g.K, BK);
   const int per = (int)ceil_div(ktiles, split);
   const int real_split = (int)ceil_div(ktiles, per);
