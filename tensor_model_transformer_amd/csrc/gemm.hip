@@ -463,8 +463,8 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
 template <bool AK, bool BKM>
 static hipError_t dispatch_f16(const GemmArgs& g, int split, hipStream_t s) {
   const TileCfg t = choose_tile(g.M, g.N, split);
-  if (t.bm == 256 && t.bn == 256) return launch_f16<256, 256, 2, 4, AK, BKM>(g, split, s);
-  if (t.bm == 256) return launch_f16<256, 192, 4, 2, AK, BKM>(g, split, s);
+  if (t.bm == 256 && t.bn == 256) return launch_f16<256, 256, 4, 4, AK, BKM>(g, split, s);
+  if (t.bm == 256) return launch_f16<256, 192, 4, 3, AK, BKM>(g, split, s);
   return launch_f16<128, 128, 2, 2, AK, BKM>(g, split, s);
 }
 
