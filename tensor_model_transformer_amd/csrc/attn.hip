@@ -306,26 +306,43 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
 // delta = rowsum(dO * O) per (token, head), fp32
 // ============================================================================
 template <typename T>
-__global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o,
-                                                         const T* __restrict__ dO,
-                                                         float* __restrict__ delta, int seq,
-                                                         int Hl, int D, long ntasks) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= ntasks) return;
-  const long tok = idx / Hl;
-  const int head = (int)(idx % Hl);
-  const T* a = o + tok * Hl * D + (long)head * D;
-  const T* g = dO + tok * Hl * D + (long)head * D;
-  float acc = 0.f;
-  for (int d = 0; d < D; d += 8) {
+// Delta = rowsum(dO * O) per (token, head). One wave per token row: lanes
+// read the row's 16-byte chunks of O and dO (coalesced) and sum each chunk's
+// products; the chunk sums go through LDS and one lane per head adds its
+// head's chunks in order.
+__global__ __launch_bounds__(64) void attn_delta_kernel(const T* __restrict__ o,
+                                                        const T* __restrict__ dO,
+                                                        float* __restrict__ delta, int seq,
+                                                        int Hl, int D) {
+  constexpr int V = 16 / sizeof(T);  // elements per chunk
+  extern __shared__ float csum[];    // [Hl * D / V]
+  const int lane = threadIdx.x;
+  const long tok = blockIdx.x;
+  const int C = Hl * D / V;
+  const T* a = o + tok * Hl * D;
+  const T* g = dO + tok * Hl * D;
+  for (int c = lane; c < C; c += 64) {
     float x[8], y[8];
-    Vec8<T>::load(a + d, x);
-    Vec8<T>::load(g + d, y);
+    if constexpr (V == 8) {
+      Vec8<T>::load(a + 8 * c, x);
+      Vec8<T>::load(g + 8 * c, y);
+    } else {
+      Vec4<T>::load(a + 4 * c, x);
+      Vec4<T>::load(g + 4 * c, y);
+    }
+    float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
+    for (int e = 0; e < V; ++e) acc += x[e] * y[e];
+    csum[c] = acc;
   }
+  __syncthreads();
   const long b = tok / seq, q = tok % seq;
-  delta[(b * Hl + head) * seq + q] = acc;
+  const int per = D / V;
+  for (int hd = lane; hd < Hl; hd += 64) {
+    float acc = 0.f;
+    for (int i = 0; i < per; ++i) acc += csum[hd * per + i];
+    delta[(b * Hl + hd) * seq + q] = acc;
+  }
 }
 
 // ============================================================================
@@ -864,13 +881,12 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* qkv_lo, const void* 
                     int seq, int Hl, int D, int mask, hipStream_t s) {
   if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
   if (qkv_lo && dtype != DT_F16) return hipErrorInvalidValue;
-  const long ntasks = (long)batch * seq * Hl;
   if (dtype == DT_F16)
-    attn_delta_kernel<f16><<<(unsigned)((ntasks + 255) / 256), 256, 0, s>>>(
-        (const f16*)o, (const f16*)dO, delta, seq, Hl, D, ntasks);
+    attn_delta_kernel<f16><<<(unsigned)(batch * seq), 64, (size_t)Hl * D / 8 * 4, s>>>(
+        (const f16*)o, (const f16*)dO, delta, seq, Hl, D);
   else
-    attn_delta_kernel<float><<<(unsigned)((ntasks + 255) / 256), 256, 0, s>>>(
-        (const float*)o, (const float*)dO, delta, seq, Hl, D, ntasks);
+    attn_delta_kernel<float><<<(unsigned)(batch * seq), 64, (size_t)Hl * D / 4 * 4, s>>>(
+        (const float*)o, (const float*)dO, delta, seq, Hl, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int causal = mask == 0;

@@ -356,10 +356,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   const int m = (int)(idx / g.N), n = (int)(idx % g.N);
   float acc[4], v[4];
   Vec4<float>::load(g.ws + idx, acc);
-  for (int s = 1; s < g.split; ++s) {
-    Vec4<float>::load(g.ws + (size_t)s * g.M * g.N + idx, v);
+  const size_t stride = (size_t)g.M * g.N;
+  for (int s0 = 1; s0 < g.split; s0 += 4) {
+    // 4 splits in flight, summed in split order
+    float x[4][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    for (int u = 0; u < 4; ++u)
+      Vec4<float>::load(g.ws + (size_t)min(s0 + u, g.split - 1) * stride + idx, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + u < g.split)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += x[u][e];
   }
   float* c = (float*)g.C + (size_t)m * g.ldc + n;
   if (g.accumulate) {

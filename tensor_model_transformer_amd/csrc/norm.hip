@@ -145,6 +145,70 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) dg[i][e] = db[i][e] = ds[i][e] = 0.f;
 
+  // Rows of up to 512 threads: row r + 1's inputs are fetched while row r is
+  // reduced and written. Wider rows (1024 threads) have no registers for the
+  // second copy and load each row in turn.
+  if constexpr (NT <= 512) {
+  float nd[NV][8], nx[NV][8], nr[NV][8];
+#define TPL_LNB_FETCH(ROW)                                                     \
+  _Pragma("unroll") for (int i = 0; i < NV; ++i) {                             \
+    const int j = tid + i * NT;                                                \
+    if (j < nvec) {                                                            \
+      Vec8<float>::load(dy + (size_t)(ROW) * h + 8 * j, nd[i]);               \
+      Vec8<Tx>::load(x + (size_t)(ROW) * h + 8 * j, nx[i]);                   \
+      Vec8<Tr>::load(dres + (size_t)(ROW) * h + 8 * j, nr[i]);                \
+    }                                                                          \
+  }
+  if (r0 < r1) TPL_LNB_FETCH(r0)
+  for (int row = r0; row < r1; ++row) {
+    const float mu = mean[row], rs = rstd[row];
+    float d[NV][8], xv[NV][8], rv[NV][8];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        d[i][e] = nd[i][e];
+        xv[i][e] = nx[i][e];
+        rv[i][e] = nr[i][e];
+      }
+    if (row + 1 < r1) TPL_LNB_FETCH(row + 1)
+    float gy[NV][8], xh[NV][8];
+    float sums[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = tid + i * NT;
+      if (j < nvec) {
+        float g[8];
+        Vec8<T>::load(gamma + 8 * j, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xh[i][e] = (xv[i][e] - mu) * rs;
+          gy[i][e] = d[i][e] * g[e];
+          sums[0] += gy[i][e];
+          sums[1] += gy[i][e] * xh[i][e];
+          dg[i][e] += d[i][e] * xh[i][e];
+          db[i][e] += d[i][e];
+        }
+      }
+    }
+    block_sum<2>(sums, red);
+    const float mg = sums[0] / (float)h, mgx = sums[1] / (float)h;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = tid + i * NT;
+      if (j < nvec) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[e] = rs * (gy[i][e] - mg - xh[i][e] * mgx) + rv[i][e];
+          ds[i][e] += o[e];
+        }
+        if (dx_f32) Vec8<float>::store(dx_f32 + (size_t)row * h + 8 * j, o);
+        if (dx_st) Vec8<Ts>::store(dx_st + (size_t)row * h + 8 * j, o);
+      }
+    }
+  }
+  } else {
   for (int row = r0; row < r1; ++row) {
     const float mu = mean[row], rs = rstd[row];
     float gy[NV][8], xh[NV][8];
@@ -186,6 +250,8 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
       }
     }
   }
+  }
+#undef TPL_LNB_FETCH
   float* pb = part + (size_t)blockIdx.x * 3 * h;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -257,7 +323,18 @@ __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ y, in
   const int r0 = blockIdx.y * rows_per_blk;
   const int r1 = min(rows, r0 + rows_per_blk);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = r0; r < r1; ++r) {
+  int r = r0;
+  // 8 rows in flight at a time, summed in row order
+  for (; r + 8 <= r1; r += 8) {
+    float v[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) Vec8<T>::load(y + (size_t)(r + u) * ld + 8 * j, v[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
+  }
+  for (; r < r1; ++r) {
     float v[8];
     Vec8<T>::load(y + (size_t)r * ld + 8 * j, v);
 #pragma unroll
@@ -301,8 +378,13 @@ __global__ __launch_bounds__(256) void reduce_stage1_kernel(const float* __restr
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
   const int b0 = blockIdx.y * kGroup, b1 = min(nblk, b0 + kGroup);
+  float x[kGroup];
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u) x[u] = part[(size_t)min(b0 + u, b1 - 1) * total + idx];
   float acc = 0.f;
-  for (int b = b0; b < b1; ++b) acc += part[(size_t)b * total + idx];
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u)
+    if (b0 + u < b1) acc += x[u];
   grp[(size_t)blockIdx.y * total + idx] = acc;
 }
 
@@ -314,7 +396,14 @@ __global__ __launch_bounds__(256) void reduce_stage2_kernel(const float* __restr
   const int total = nout * width;
   if (idx >= total) return;
   float acc = 0.f;
-  for (int g = 0; g < ngrp; ++g) acc += grp[(size_t)g * total + idx];
+  for (int g0 = 0; g0 < ngrp; g0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = grp[(size_t)min(g0 + u, ngrp - 1) * total + idx];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (g0 + u < ngrp) acc += x[u];
+  }
   const int k = idx / width, j = idx - k * width;
   float* o = k == 0 ? out0 : (k == 1 ? out1 : out2);
   if (!o) return;
