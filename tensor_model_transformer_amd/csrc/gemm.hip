@@ -413,15 +413,37 @@ static TileCfg choose_tile(int M, int N, int split) {
   return best;
 }
 
+// Split-K factor of a weight-gradient GEMM (few output tiles, long K). When
+// some tile shape and split fill one round of the CUs to at least 70 %, the
+// fullest such single round wins (fewest splits on ties): measured on the
+// layer's weight gradients, one full round beats several rounds plus the
+// partial-sum traffic of a larger split. Otherwise the split that best fills
+// whole rounds of 256x256 tiles.
 int gemm_choose_split(const GemmArgs& g) {
   if (g.math != DT_F16) return 1;
   if (g.epi != EPI_STORE || g.bias || g.resid || g.c_dtype != DT_F32) return 1;
-  const long tiles = ceil_div(g.M, kBig.bm) * ceil_div(g.N, kBig.bn);
   const long ktiles = ceil_div(g.K, 64);
+  double best_fill = 0.0;
+  int one_round = 0;
+  for (const TileCfg& t : {kBig, kWide}) {
+    const long tiles = ceil_div(g.M, t.bm) * ceil_div(g.N, t.bn);
+    for (int s = 1; s <= 16; ++s) {
+      if (s > 1 && ktiles / s < 8) break;  // keep >= 8 K-tiles per split
+      const long w = tiles * s;
+      if (w > kCUs) break;
+      const double fill = (double)w / kCUs;
+      if (fill > best_fill + 1e-9) {
+        best_fill = fill;
+        one_round = s;
+      }
+    }
+  }
+  if (best_fill >= 0.7) return one_round;
+  const long tiles = ceil_div(g.M, kBig.bm) * ceil_div(g.N, kBig.bn);
   int best = 1;
   double best_util = 0.0;
   for (int s = 1; s <= 16; ++s) {
-    if (ktiles / s < 8) break;  // keep >= 8 K-tiles per split
+    if (ktiles / s < 8) break;
     const long w = tiles * s;
     const double util = (double)w / (double)(kCUs * ceil_div(w, kCUs));
     if (util > best_util + 0.05) {
