@@ -11,15 +11,22 @@
 // fp32 accumulate; the same rate as bf16 on gfx950) on LDS double-buffered
 // tiles. Both operands are fp16 in memory: internal activations are fp16, and
 // the caller hands in fp16 copies of the bf16 tensors at the layer boundary
-// (weights, the upstream gradient), made once per step. An operand
-// tile keeps its HBM orientation in LDS: K-contiguous operands as
-// [rows][BK+8] (each MFMA fragment one 16-byte LDS read), operands that are
-// contiguous along M or N (weights [in,out] in forward; both operands of a
-// weight gradient) as [BK][rows+16], whose fragments come from
-// ds_read_b64_tr_b16, gfx950's transposing LDS read, so nothing is transposed
-// in registers. The MFMA is issued with B as the first operand, so the
-// accumulator holds C transposed: each lane owns one output row and 4
+// (weights, the upstream gradient), made once per step. An operand tile keeps
+// its HBM orientation in LDS: K-contiguous operands as rows of BK, operands
+// that are contiguous along M or N (weights [in,out] in forward; both operands
+// of a weight gradient) as k-lines of the tile's rows, whose MFMA fragments
+// come from ds_read_b64_tr_b16, gfx950's transposing LDS read, so nothing is
+// transposed in registers. The MFMA is issued with B as the first operand, so
+// the accumulator holds C transposed: each lane owns one output row and 4
 // consecutive columns per 32x32 tile, which the epilogue writes as one vector.
+//
+// Tiles wholly inside the matrix (every tile of the layer's GEMMs) are loaded
+// from HBM straight into LDS (buffer_load_dword*4 ... lds): no staging
+// registers and no LDS store instructions. Those loads write 64 consecutive
+// 16-byte chunks per instruction, so the tiles are unpadded and their 16-byte
+// chunks XOR-swizzled to keep the fragment reads free of bank conflicts.
+// Edge tiles (ragged shapes) take a register-staged kernel with padded tiles
+// and bounds checks.
 //
 // fp32 path: a plain tiled FMA kernel (exact fp32 arithmetic).
 #include "common.hpp"
@@ -109,12 +116,14 @@ __device__ __forceinline__ void partial4(const GemmArgs& g, int split_idx, int m
 // ----------------------------------------------------------------------------
 // LDS pitch (16-bit elements) of an operand tile: K-contiguous tiles are
 // [ROWS][BK + 8] (16-byte MFMA fragment reads); row-contiguous tiles are
-// [BK][ROWS + 16], read with ds_read_b64_tr_b16 (each 16-lane group reads 4
-// rows x 32 bytes; the +16 pad puts the 4 rows on disjoint banks).
+// [BK][ROWS + 32], read with ds_read_b64_tr_b16. Each half wave of such a
+// read covers 4 tile rows x 64 bytes; the +32 pad (64 bytes) makes the row
+// pitch 16 or 48 dwords modulo the 64 LDS banks, so the 4 rows fall on
+// disjoint banks.
 template <int ROWS, int BK, bool KMAJ>
 struct TilePitch {
-  static constexpr int P = KMAJ ? BK + 8 : ROWS + 16;
-  static constexpr int kElems = KMAJ ? ROWS * (BK + 8) : BK * (ROWS + 16);
+  static constexpr int P = KMAJ ? BK + 8 : ROWS + 32;
+  static constexpr int kElems = KMAJ ? ROWS * (BK + 8) : BK * (ROWS + 32);
 };
 
 template <int ROWS, int BK, int NT, bool KMAJ>
@@ -126,13 +135,10 @@ struct TileLoader {
   static constexpr int kPerRow = KMAJ ? BK / 8 : ROWS / 8;  // chunks per contiguous line
   uint4 st[kPer];
 
-  // src(row, k) = KMAJ ? p[row*ld + k] : p[k*ld + row]; 16-bit elements.
-  // The loaded registers are consumed only by store(), after the MFMAs of
-  // the current tile, so the global-load latency overlaps the compute.
-  // EDGE = false: the tile lies wholly inside the matrix (every M, N and K
-  // of the layer's GEMMs is a multiple of the tile), so the loads carry no
-  // guards, and the element offsets fit 32 bits (checked on the host).
-  template <bool EDGE>
+  // src(row, k) = KMAJ ? p[row*ld + k] : p[k*ld + row]; 16-bit elements;
+  // chunks outside the matrix read as zero. The loaded registers are consumed
+  // only by store(), after the MFMAs of the current tile, so the global-load
+  // latency overlaps the compute.
   __device__ __forceinline__ void load(const uint16_t* __restrict__ p, long ld, int row0, int nrows,
                                        int k0, int K, int tid) {
 #pragma unroll
@@ -143,15 +149,9 @@ struct TileLoader {
       const int gr = KMAJ ? row0 + line : row0 + 8 * w;
       const int gk = KMAJ ? k0 + 8 * w : k0 + line;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if constexpr (!EDGE) {
-        if (kChunks % NT == 0 || c < kChunks)
-          v = *reinterpret_cast<const uint4*>(
-              p + (uint32_t)(KMAJ ? gr * (int)ld + gk : gk * (int)ld + gr));
-      } else {
-        if ((kChunks % NT == 0 || c < kChunks) && gr < nrows && gk < K)
-          v = *reinterpret_cast<const uint4*>(
-              p + (KMAJ ? (size_t)gr * ld + gk : (size_t)gk * ld + gr));
-      }
+      if ((kChunks % NT == 0 || c < kChunks) && gr < nrows && gk < K)
+        v = *reinterpret_cast<const uint4*>(
+            p + (KMAJ ? (size_t)gr * ld + gk : (size_t)gk * ld + gr));
       st[i] = v;
     }
   }
@@ -180,7 +180,8 @@ __device__ __forceinline__ f16x8 frag(const uint16_t* tile, int r0, int ks, int 
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM, bool EDGE>
+// Edge tiles: register-staged loads with bounds checks into padded tiles.
+template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int ktiles_per_split) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -217,8 +218,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   if (kt0 < kt1) {
-    la.template load<EDGE>(A, g.lda, m0, g.M, kt0 * BK, g.K, tid);
-    lb.template load<EDGE>(B, g.ldb, n0, g.N, kt0 * BK, g.K, tid);
+    la.load(A, g.lda, m0, g.M, kt0 * BK, g.K, tid);
+    lb.load(B, g.ldb, n0, g.N, kt0 * BK, g.K, tid);
     la.store(As, tid);
     lb.store(Bs, tid);
     __syncthreads();
@@ -228,8 +229,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
     const int cur = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) {
-      la.template load<EDGE>(A, g.lda, m0, g.M, (kt + 1) * BK, g.K, tid);
-      lb.template load<EDGE>(B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, tid);
+      la.load(A, g.lda, m0, g.M, (kt + 1) * BK, g.K, tid);
+      lb.load(B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, tid);
     }
     const uint16_t* as = As + cur * AE;
     const uint16_t* bs = Bs + cur * BE;
@@ -275,6 +276,191 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
             make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
                         acc[i][j][4 * jj + 3]);
     constexpr int LPR = WTN / 4;  // lanes per slice row
+#pragma unroll 1
+    for (int r = lane / LPR; r < 32; r += 64 / LPR) {
+      const int c = 4 * (lane % LPR);
+      const float4 q = *reinterpret_cast<const float4*>(cs + r * CP + c);
+      float v[4] = {q.x, q.y, q.z, q.w};
+      const int m = m0 + wm * WTM + i * 32 + r, n = n0 + wn * WTN + c;
+      if (gridDim.y > 1) partial4(g, split_idx, m, n, v);
+      else epilogue4(g, m, n, v);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Interior tiles: HBM -> LDS direct loads, two stages of BK = 64
+// ----------------------------------------------------------------------------
+// s_waitcnt vmcnt(N), other counters not waited.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier after this wave's LDS operations completed (lgkmcnt(0));
+// global loads may stay in flight, unlike __syncthreads(). The empty asm
+// statements keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One operand tile of ROWS (M or N) x BK in LDS, filled by direct loads.
+//  K-contiguous source: ROWS lines of BK elements; 16-byte chunk position p
+//    of line r holds source chunk p ^ ((r >> 1) & 7). A fragment read covers
+//    16 consecutive lines at one chunk; line pairs share the 64 banks and the
+//    XOR spreads the 8 pairs over distinct 4-bank groups.
+//  Row-contiguous source: BK k-lines of ROWS elements; chunk position p of
+//    k-line k holds source row chunk p ^ f(k). A half-wave transposing read
+//    covers 4 k-lines x 4 chunks: with a line length that is a multiple of
+//    256 bytes f(k) = 4 (k & 3); with 384-byte lines (ROWS = 192), which
+//    already alternate between bank halves, f(k) = 4 ((k >> 1) & 1).
+// Each wave issues kPerWave loads of 64 chunks per stage; when the count does
+// not divide evenly, the last loads repeat chunks another wave also loads
+// (same data to the same place), so every wave waits for the same count.
+template <int ROWS, int BK, int NW, bool KMAJ>
+struct DtlOperand {
+  static constexpr int kChunks = ROWS * BK / 8;
+  static constexpr int kInstr = kChunks / 64;
+  static constexpr int kPerWave = (kInstr + NW - 1) / NW;
+  static constexpr int kPerLine = KMAJ ? BK / 8 : ROWS / 8;
+  static_assert(kChunks % 64 == 0 && kInstr >= NW, "direct-load chunking");
+  static_assert(BK == 64, "swizzle written for 8 chunks per K-contiguous line");
+
+  __device__ __forceinline__ static int swz(int line) {
+    if constexpr (KMAJ) return (line >> 1) & 7;
+    else return (ROWS * 2) % 256 == 0 ? 4 * (line & 3) : 4 * ((line >> 1) & 1);
+  }
+
+  // rs covers the whole operand; element (row, k) sits at row * ld + k
+  // (K-contiguous) or k * ld + row; byte offsets fit 31 bits (host check).
+  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t rs, int ld, int row0, int k0,
+                                              uint16_t* stage, int wid, int lane) {
+#pragma unroll
+    for (int t = 0; t < kPerWave; ++t) {
+      int q = wid + NW * t;
+      if (q >= kInstr) q -= kInstr;
+      const int p = 64 * q + lane;
+      const int line = p / kPerLine, pos = p % kPerLine;
+      const int c = pos ^ swz(line);
+      const int off = KMAJ ? ((row0 + line) * ld + k0 + 8 * c) * 2
+                           : ((k0 + line) * ld + row0 + 8 * c) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(stage + 64 * q * 8), 16, off, 0, 0, 0);
+    }
+  }
+
+  // MFMA operand of rows r0 .. r0+31 for K step ks (as frag() above).
+  __device__ __forceinline__ static f16x8 frag(const uint16_t* st, int r0, int ks, int lane) {
+    if constexpr (KMAJ) {
+      const int r = r0 + (lane & 31);
+      const int kc = 2 * ks + (lane >> 5);
+      return *reinterpret_cast<const f16x8*>(st + r * BK + (kc ^ swz(r)) * 8);
+    } else {
+      const int gq = lane >> 4, L = lane & 15;
+      const int row = r0 + 16 * (gq & 1) + 4 * (L & 3);
+      const int kb = ks * 16 + 8 * (gq >> 1) + (L >> 2);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          TPL_LDS_V4S(st + kb * ROWS + ((row >> 3) ^ swz(kb)) * 8 + (row & 7)));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          TPL_LDS_V4S(st + (kb + 4) * ROWS + ((row >> 3) ^ swz(kb + 4)) * 8 + (row & 7)));
+      const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+      return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+    }
+  }
+};
+
+// Same tiling and epilogue as gemm_f16_kernel. Iteration j: wait for this
+// wave's loads of stage j, barrier (stage j complete in LDS; every wave done
+// with stage j-1), issue the loads of stage j+1 into stage j-1's buffer, then
+// the MFMAs of stage j.
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, int ktiles_per_split) {
+  constexpr int BK = 64, NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  using OA = DtlOperand<BM, BK, NW, AK>;
+  using OB = DtlOperand<BN, BK, NW, BKM>;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);  // [2][BM * BK]
+  uint16_t* Bs = As + 2 * BM * BK;                   // [2][BN * BK]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid / WN, wn = wid % WN;
+  int tm, tn;
+  tile_coords(g.M, g.N, BM, BN, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int split_idx = blockIdx.y;
+  const int ktiles = g.K / BK;
+  const int kt0 = split_idx * ktiles_per_split;
+  const int kt1 = min(ktiles, kt0 + ktiles_per_split);
+  const int nk = kt1 - kt0;
+
+  const int a_bytes = (int)((AK ? (long)g.M : (long)g.K) * g.lda * 2);
+  const int b_bytes = (int)((BKM ? (long)g.N : (long)g.K) * g.ldb * 2);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), (short)0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.B), (short)0, b_bytes, 0x00020000);
+  const int lda = (int)g.lda, ldb = (int)g.ldb;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  if (nk > 0) {
+    OA::load(ra, lda, m0, kt0 * BK, As, wid, lane);
+    OB::load(rb, ldb, n0, kt0 * BK, Bs, wid, lane);
+  }
+  for (int j = 0; j < nk; ++j) {
+    wait_vm<0>();
+    lds_barrier();
+    if (j + 1 < nk) {
+      const int nb = (j + 1) & 1;
+      OA::load(ra, lda, m0, (kt0 + j + 1) * BK, As + nb * BM * BK, wid, lane);
+      OB::load(rb, ldb, n0, (kt0 + j + 1) * BK, Bs + nb * BN * BK, wid, lane);
+    }
+    const uint16_t* as = As + (j & 1) * BM * BK;
+    const uint16_t* bs = Bs + (j & 1) * BN * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      f16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = OA::frag(as, wm * WTM + 32 * i, ks, lane);
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj) bfr[jj] = OB::frag(bs, wn * WTN + 32 * jj, ks, lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[jj], af[i], acc[i][jj], 0, 0, 0);
+    }
+  }
+
+  // Epilogue through LDS slices (see gemm_f16_kernel).
+  constexpr int CP = WTN + 4;
+  float* cs = reinterpret_cast<float*>(smem) + wid * 32 * CP;
+  const int lrow = lane & 31, half = lane >> 5;
+  __syncthreads();  // every wave is done with the operand tiles
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(cs + lrow * CP + j * 32 + 8 * jj + 4 * half) =
+            make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
+                        acc[i][j][4 * jj + 3]);
+    constexpr int LPR = WTN / 4;
 #pragma unroll 1
     for (int r = lane / LPR; r < 32; r += 64 / LPR) {
       const int c = 4 * (lane % LPR);
@@ -459,19 +645,23 @@ template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
 static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
   constexpr int BK = 64;
   constexpr int NT = WM * WN * 64;
-  const size_t lds = (size_t)2 *
-                     (TilePitch<BM, BK, AK>::kElems + TilePitch<BN, BK, BKM>::kElems) *
-                     sizeof(uint16_t);
   const int ktiles = (int)ceil_div(g.K, BK);
   const int per = (int)ceil_div(ktiles, split);
   const int real_split = (int)ceil_div(ktiles, per);
-  // every tile inside the matrix: no guards on the operand loads, and the
-  // element offsets of both operands fit 31 bits
+  // every tile inside the matrix, and byte offsets of both operands within
+  // 31 bits: the direct-load kernel
   const bool interior = g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0 &&
-                        (size_t)(g.a_kmajor ? g.M : g.K) * g.lda < (1u << 31) &&
-                        (size_t)(g.b_kmajor ? g.N : g.K) * g.ldb < (1u << 31);
-  auto kern = interior ? gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM, false>
-                       : gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM, true>;
+                        (size_t)(g.a_kmajor ? g.M : g.K) * g.lda * 2 < (1u << 31) &&
+                        (size_t)(g.b_kmajor ? g.N : g.K) * g.ldb * 2 < (1u << 31);
+  const size_t slices = (size_t)WM * WN * 32 * (BN / WN + 4) * sizeof(float);
+  const size_t lds_pad = (size_t)2 *
+                         (TilePitch<BM, BK, AK>::kElems + TilePitch<BN, BK, BKM>::kElems) *
+                         sizeof(uint16_t);
+  const size_t lds_ops = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);
+  const size_t lds_dtl = lds_ops > slices ? lds_ops : slices;
+  const size_t lds = interior ? lds_dtl : lds_pad;
+  auto kern = interior ? gemm_f16_dtl_kernel<BM, BN, WM, WN, AK, BKM>
+                       : gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM>;
   static bool attr_set[2] = {false, false};  // per instantiation
   if (!attr_set[interior]) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
