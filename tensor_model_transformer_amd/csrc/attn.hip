@@ -164,6 +164,14 @@ __device__ __forceinline__ void block_pipeline(int nblk, Stage& sa, Stage& sb, F
   }
 }
 
+// Waves per SIMD requested from the compiler: two where the registers fit
+// without spilling (forward and dQ up to head dim 96, dK/dV up to 64, without
+// the split-score residuals), else no constraint.
+template <int D, bool SPLIT>
+constexpr int kAttnWaves = (D <= 96 && !SPLIT) ? 2 : 1;
+template <int D, bool SPLIT>
+constexpr int kDkdvWaves = (D <= 64 && !SPLIT) ? 2 : 1;
+
 // ============================================================================
 // fp16 forward
 // ============================================================================
@@ -171,7 +179,7 @@ __device__ __forceinline__ void block_pipeline(int nblk, Stage& sa, Stage& sb, F
 // sweeps 64-key blocks; K and V tiles are double-buffered in LDS through
 // registers (the next block's loads are in flight during the current MFMAs).
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<D, SPLIT>))) void attn_fwd_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, f16* __restrict__ o,
     float* __restrict__ lse2, const int* __restrict__ valid_len, int seq, int Hl, int causal,
     float sl2) {
@@ -243,36 +251,56 @@ __global__ __launch_bounds__(256) void attn_fwd_f16_kernel(
           }
         }
       }
-      // S[st][4*jj+ii]: key kb0 + 32*st + 8*jj + 4*hh + ii, query q
+      // S[st][4*jj+ii]: key kb0 + 32*st + 8*jj + 4*hh + ii, query q. Raw
+      // scores: the scale sl2 > 0 is applied inside the exponent's FMA. Only
+      // blocks that cross this wave's causal diagonal or the padding limit
+      // need the mask (a wave-uniform test).
+      const bool need_mask = causal ? kb0 + KB - 1 > qw0 : kb0 + KB > L;
       float mx = -INFINITY;
+      if (need_mask) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const float s = key < lim ? S[st][e] * sl2 : -INFINITY;
-          S[st][e] = s;
-          mx = fmaxf(mx, s);
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int key = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
+            S[st][e] = key < lim ? S[st][e] : -INFINITY;
+            mx = fmaxf(mx, S[st][e]);
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[st][e]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);
+      // Lazy rescaling: the reference point m_run (log2 domain) moves only
+      // when this block's maximum exceeds it by more than kSlack, so p stays
+      // below 2^kSlack (exact in fp32, and well inside fp16 for the P operand)
+      // and most blocks skip the rescale of O. The result is independent of
+      // the reference point up to rounding; lse2 = m_run + log2(l_run).
+      constexpr float kSlack = 8.f;
+      const float m_blk = mx * sl2;
+      if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kSlack)) {
+        const float m_new = m_blk > m_run + kSlack ? m_blk : m_run;
+        const float alpha = exp2_fast(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) O[t][e] *= alpha;
+      }
       float ls = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2_fast(S[st][e] - m_new);
+          const float p = exp2_fast(__builtin_fmaf(S[st][e], sl2, -m_run));
           S[st][e] = p;
           ls += p;
         }
       ls += __shfl_xor(ls, 32, 64);
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) O[t][e] *= alpha;
+      l_run += ls;
       // O^T[d][q] += sum_key V[key][d] P[q][key]; 16 keys per MFMA, slot order
       // {4h..4h+3, 8+4h..8+4h+3} within the 16 (the accumulator's row order)
 #pragma unroll
@@ -352,7 +380,7 @@ __global__ __launch_bounds__(64) void attn_delta_kernel(const T* __restrict__ o,
 // are double-buffered in LDS through registers. Q^T and dO^T operands are
 // read from the row-major tiles with transposing LDS reads.
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D, SPLIT>))) void attn_bwd_dkdv_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
     const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale) {
@@ -467,14 +495,27 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
         dlv[4 * jj] = b.x; dlv[4 * jj + 1] = b.y; dlv[4 * jj + 2] = b.z; dlv[4 * jj + 3] = b.w;
       }
       float Pv[16], dS[16];
+      // every (query, key) of this half allowed: no mask (a wave-uniform
+      // test; the unmasked copy is left out where its registers would spill)
+      constexpr bool kFast = !(D >= 160 && SPLIT);
+      const bool need_mask = !kFast | (qh0 + 31 >= seq) | (kw0 + 31 >= L) | (causal & (kw0 + 31 > qh0));
+      if (need_mask) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qq = qh0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-        // bitwise & / |: no short-circuit, hence no branch per element
-        const bool ok = (qq < seq) & (key < L) & (!causal | (key <= qq));
-        const float p = exp2_fast(ok ? S[e] * sl2 - lsv[e] : -INFINITY);  // 0 when masked
-        Pv[e] = p;
-        dS[e] = p * (dP[e] - dlv[e]);
+        for (int e = 0; e < 16; ++e) {
+          const int qq = qh0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          // bitwise & / |: no short-circuit, hence no branch per element
+          const bool ok = (qq < seq) & (key < L) & (!causal | (key <= qq));
+          const float p = exp2_fast(ok ? __builtin_fmaf(S[e], sl2, -lsv[e]) : -INFINITY);
+          Pv[e] = p;
+          dS[e] = p * (dP[e] - dlv[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2_fast(__builtin_fmaf(S[e], sl2, -lsv[e]));
+          Pv[e] = p;
+          dS[e] = p * (dP[e] - dlv[e]);
+        }
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -514,7 +555,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f16_kernel(
 // fp16 backward: dQ (a workgroup owns 128 queries, 32 per wave)
 // ============================================================================
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<D, SPLIT>))) void attn_bwd_dq_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
     const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale) {
@@ -594,11 +635,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f16_kernel(
           }
           dP = mfma32(ld8(Vs + off), gf[ks], dP);
         }
+        // every (query, key) of this 32-key half allowed: no mask (a
+        // wave-uniform test); otherwise masked elements get p = 0
+        const int k0 = kb0 + 32 * st;
+        const bool need_mask = (qw0 + 31 >= seq) | (causal ? k0 + 31 > qw0 : k0 + 32 > L);
+        if (need_mask) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int k = kb0 + 32 * st + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const float p = exp2_fast((qok & (k < lim)) ? S[e] * sl2 - lq : -INFINITY);
-          dS[st][e] = p * (dP[e] - dq_);
+          for (int e = 0; e < 16; ++e) {
+            const int k = k0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const float p = exp2_fast((qok & (k < lim)) ? __builtin_fmaf(S[e], sl2, -lq) : -INFINITY);
+            dS[st][e] = p * (dP[e] - dq_);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = exp2_fast(__builtin_fmaf(S[e], sl2, -lq));
+            dS[st][e] = p * (dP[e] - dq_);
+          }
         }
       }
 #pragma unroll
