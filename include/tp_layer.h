@@ -64,6 +64,14 @@
  *    NULL = the null stream) and the call returns after enqueue. A handle must
  *    not be used on two streams at once. Asynchronous device faults surface at
  *    the caller's synchronisation.
+ *  - The backward runs its weight and bias gradients on a second stream of
+ *    the handle's own (created, with default priority, on the current device
+ *    by the first tp_layer_bwd call) concurrently with the data-gradient
+ *    chain: it waits for `hip_stream` through an event before each such
+ *    group, and every backward phase makes `hip_stream` wait for it before
+ *    returning, so all of a phase's outputs are ordered on `hip_stream` as if
+ *    it had run alone (this also holds under stream capture). The handle must
+ *    be used on that device afterwards.
  *  - Return value: TP_OK (0) or a negative TP_ERR_* code. No exceptions cross
  *    the ABI, nothing is printed, nothing aborts. After an error the handle
  *    stays valid and nothing has been enqueued (except TP_ERR_HIP, which

@@ -70,6 +70,8 @@ struct tp_layer {
   // workspace regions
   Region mean1, rstd1, a, qkv, qkv_lo, o, lse2, h_mid, mean2, rstd2, c, u, z;
   Region du, dc, dh_f, dh_s, dO, delta, dqkv, da, part, splitk;
+  // column-sum partials of the bias gradients that run on the side stream
+  Region part2;
   // fp16 copies of the bf16 weights (made by the forward, read again by the
   // backward) and of the upstream gradient: the MFMA GEMMs read fp16 only
   Region w16_qkv, w16_o, w16_fc1, w16_fc2, dout16;
@@ -77,6 +79,14 @@ struct tp_layer {
   int split_w2, split_w1, split_wo, split_wqkv;
   double attn_pairs;  // allowed query-key pairs (causal); 0 for padding (lengths on device)
   Prof prof;
+  // Side stream of the backward: the weight gradients (and bias column sums)
+  // run on it concurrently with the data-gradient chain on the caller's
+  // stream; every phase joins it back before returning. Created on the
+  // current device by the first backward call; null if that failed (then
+  // everything runs on the caller's stream).
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  bool side_tried = false;
   // decode (one row per sequence): its own workspace plan
   struct Dec {
     Region a, apart, o, h_mid, c, z, gpart;
@@ -171,6 +181,10 @@ void plan(tp_layer* L) {
     if (p > part) part = p;
   }
   take(L->part, part * 4);
+  size_t part2 = 0;
+  for (int i = 0; i < 3; ++i)
+    part2 = std::max(part2, reduce_scratch_floats(colsum_blocks(L->n, cols[i], &rpb), 1, cols[i]));
+  take(L->part2, part2 * 4);
   // split-K partials of the weight gradients
   size_t sk = 0;
   struct W {
@@ -323,6 +337,44 @@ int run_gemm(tp_layer* L, const GemmArgs& g, hipStream_t s) {
   return TP_OK;
 }
 
+// The side stream (created on first use), or the caller's stream if none.
+hipStream_t side_stream(tp_layer* L, hipStream_t s) {
+  if (!L->side_tried) {
+    L->side_tried = true;
+    hipStream_t st = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess &&
+        hipEventCreateWithFlags(&a, hipEventDisableTiming) == hipSuccess &&
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) == hipSuccess) {
+      L->side = st;
+      L->fork_ev = a;
+      L->join_ev = b;
+    } else {
+      if (b) (void)hipEventDestroy(b);
+      if (a) (void)hipEventDestroy(a);
+      if (st) (void)hipStreamDestroy(st);
+      (void)hipGetLastError();
+    }
+  }
+  return L->side ? L->side : s;
+}
+
+// side waits for everything enqueued on s so far.
+int fork_to(tp_layer* L, hipStream_t s, hipStream_t side) {
+  if (side == s) return TP_OK;
+  HIP_TRY(hipEventRecord(L->fork_ev, s));
+  HIP_TRY(hipStreamWaitEvent(side, L->fork_ev, 0));
+  return TP_OK;
+}
+
+// s waits for everything enqueued on side so far.
+int join_from(tp_layer* L, hipStream_t s, hipStream_t side) {
+  if (side == s) return TP_OK;
+  HIP_TRY(hipEventRecord(L->join_ev, side));
+  HIP_TRY(hipStreamWaitEvent(s, L->join_ev, 0));
+  return TP_OK;
+}
+
 // bf16 -> fp16 copies (nothing to do for an fp32 layer).
 int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
                   std::initializer_list<const Region*> dst, std::initializer_list<size_t> count,
@@ -437,11 +489,12 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
 
 // ---- backward pieces -------------------------------------------------------
 // Bias gradient: out (+)= column sums of y [n, cols] (two-stage, deterministic).
+// Bias gradient (column sums of y) on the side stream, with its own partials.
 int bias_grad(tp_layer* L, const void* y, int y_dtype, int cols, float* out, int accumulate,
               void* ws, hipStream_t s, int rows = -1) {
   if (rows < 0) rows = L->n;
   Scope ps(L, s, TP_K_REDUCE, 0, (double)rows * cols * L->esz + 4.0 * cols);
-  float* part = at<float>(ws, L->part);
+  float* part = at<float>(ws, L->part2);
   int rpb;
   const int nb = colsum_blocks(rows, cols, &rpb);
   HIP_TRY(colsum_partial(y_dtype, y, rows, cols, cols, part, rpb, s));
@@ -500,6 +553,14 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   // du = (dout @ W_fc2,r^T) * GeLU'(u); with recompute u is in the du buffer
   // and is overwritten in place (each element is read, then written, by the
   // same thread of the epilogue)
+  // side stream: db2 and dW2 (need only dout and z) while du is computed
+  hipStream_t sd = side_stream(L, s);
+  if ((e = fork_to(L, s, sd))) return e;
+  if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, sd, db2_rows)))
+    return e;
+  g = wgrad_args(L, fl, h, at<void>(ws, L->z), dout, io->d_w_fc2, io->accumulate);
+  g.split = L->split_w2; g.ws = skw;
+  if ((e = run_gemm(L, g, sd))) return e;
   g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
   g.A = dout; g.lda = h; g.a_kmajor = 1;
@@ -508,22 +569,20 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   g.aux = at<void>(ws, L->recompute_fc1 ? L->du : L->u); g.ldaux = fl;
   g.C = at<void>(ws, L->du); g.ldc = fl;
   if ((e = run_gemm(L, g, s))) return e;
-  if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s, db2_rows)))
-    return e;
-  g = wgrad_args(L, fl, h, at<void>(ws, L->z), dout, io->d_w_fc2, io->accumulate);
-  g.split = L->split_w2; g.ws = skw;
-  if ((e = run_gemm(L, g, s))) return e;
+  // side stream: dW1 and db1 (need du) while dc is computed
+  if ((e = fork_to(L, s, sd))) return e;
   g = wgrad_args(L, h, fl, c_act, at<void>(ws, L->du), io->d_w_fc1, io->accumulate);
   g.split = L->split_w1; g.ws = skw;
-  if ((e = run_gemm(L, g, s))) return e;
-  if ((e = bias_grad(L, at<void>(ws, L->du), L->adt, fl, io->d_b_fc1, io->accumulate, ws, s)))
+  if ((e = run_gemm(L, g, sd))) return e;
+  if ((e = bias_grad(L, at<void>(ws, L->du), L->adt, fl, io->d_b_fc1, io->accumulate, ws, sd)))
     return e;
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = fl;
   g.A = at<void>(ws, L->du); g.lda = fl; g.a_kmajor = 1;
   g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 1;
   g.C = dc_out; g.ldc = h; g.c_dtype = DT_F32;
-  return run_gemm(L, g, s);
+  if ((e = run_gemm(L, g, s))) return e;
+  return join_from(L, s, sd);
 }
 
 // dc (summed) -> dh, LN2 grads, db_o -> dW_o, do -> attention -> dqkv ->
@@ -545,14 +604,17 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
     return e;
   const void* dh_s = dh_in ? dh_in : at<void>(ws, L->dh_s);
   const void* a_act = a_in ? a_in : at<void>(ws, L->a);
-  GemmArgs g = gemm_base(L);
+  // side stream: dW_o (needs dh) during the attention backward
+  hipStream_t sd = side_stream(L, s);
+  if ((e = fork_to(L, s, sd))) return e;
+  GemmArgs g = wgrad_args(L, hl, h, at<void>(ws, L->o), dh_s, io->d_w_o, io->accumulate);
+  g.split = L->split_wo; g.ws = skw;
+  if ((e = run_gemm(L, g, sd))) return e;
+  g = gemm_base(L);
   g.M = n; g.N = hl; g.K = h;
   g.A = dh_s; g.lda = h; g.a_kmajor = 1;
   g.B = wmat(L, ws, L->w16_o, p->w_o); g.ldb = h; g.b_kmajor = 1;
   g.C = at<void>(ws, L->dO); g.ldc = hl;
-  if ((e = run_gemm(L, g, s))) return e;
-  g = wgrad_args(L, hl, h, at<void>(ws, L->o), dh_s, io->d_w_o, io->accumulate);
-  g.split = L->split_wo; g.ws = skw;
   if ((e = run_gemm(L, g, s))) return e;
   {
     Scope ps(L, s, TP_K_ATTN_BWD, 8.0 * L->dh * L->Hl * L->attn_pairs,
@@ -562,18 +624,21 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
                      at<float>(ws, L->lse2), at<float>(ws, L->delta), at<void>(ws, L->dqkv),
                      p->valid_len, L->batch, L->seq, L->Hl, L->dh, L->mask, s));
   }
+  // side stream: dW_qkv and db_qkv (need dqkv) while da is computed
+  if ((e = fork_to(L, s, sd))) return e;
   g = wgrad_args(L, h, 3 * hl, a_act, at<void>(ws, L->dqkv), io->d_w_qkv, io->accumulate);
   g.split = L->split_wqkv; g.ws = skw;
-  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = run_gemm(L, g, sd))) return e;
   if ((e = bias_grad(L, at<void>(ws, L->dqkv), L->adt, 3 * hl, io->d_b_qkv, io->accumulate, ws,
-                     s)))
+                     sd)))
     return e;
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = 3 * hl;
   g.A = at<void>(ws, L->dqkv); g.lda = 3 * hl; g.a_kmajor = 1;
   g.B = wmat(L, ws, L->w16_qkv, p->w_qkv); g.ldb = 3 * hl; g.b_kmajor = 1;
   g.C = da_out; g.ldc = h; g.c_dtype = DT_F32;
-  return run_gemm(L, g, s);
+  if ((e = run_gemm(L, g, s))) return e;
+  return join_from(L, s, sd);
 }
 
 // da (summed) -> dx (+ dh), LN1 grads.
@@ -1003,6 +1068,12 @@ int tp_layer_destroy(tp_layer* L) {
   if (L) {
     prof_fold(L->prof);
     for (hipEvent_t e : L->prof.pool) (void)hipEventDestroy(e);
+    if (L->side) {
+      (void)hipStreamSynchronize(L->side);
+      (void)hipEventDestroy(L->fork_ev);
+      (void)hipEventDestroy(L->join_ev);
+      (void)hipStreamDestroy(L->side);
+    }
   }
   delete L;
   return TP_OK;
