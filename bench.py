@@ -396,7 +396,9 @@ def main():
     print(f"[bench] {w.name}: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s "
           f"(wall {wall:.2f} s for {args.steps} steps)", file=sys.stderr, flush=True)
 
-    # Per-kernel-class event timing over the same number of steps.
+    # Per-kernel-class event timing over the same number of steps. While
+    # profiling, the library runs the backward on one stream (no overlap of
+    # the weight gradients), so each launch group is timed alone.
     _check("tp_layer_profile", B.tp_layer_profile(sh.handle, 1))
     for _ in range(args.steps):
         step()
@@ -427,6 +429,7 @@ def main():
                 "algorithmic_bytes_per_launch": bd["gbyte_per_step"] * 1e9 / bd["launches_per_step"]}
     roof["launches_per_step"] = bd["launches_per_step"]
     roof["avg_launch_ms"] = bd["ms_per_step"] / bd["launches_per_step"]
+    roof["timing"] = "HIP events on the launch stream, profiled pass with a serial backward"
 
     cpu = None
     if not args.no_cpu_baseline:

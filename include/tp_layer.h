@@ -381,7 +381,9 @@ int tp_layer_tap(const tp_layer *L, int tap, size_t *offset, size_t *bytes);
  * query-key pair for the attention forward, twice that backward) and bytes
  * (each input read once, each output written once). Enabling, disabling or
  * re-enabling clears what was recorded. The events are created on first use
- * and reused; no device memory is allocated. */
+ * and reused; no device memory is allocated. While profiling is on, the
+ * backward enqueues everything on the call's stream (no second stream), so
+ * each bracket times its launch group alone. */
 enum {
   TP_K_GEMM = 0,      /* MFMA / FMA GEMMs incl. their split-K reduction */
   TP_K_ATTN_FWD = 1,  /* attention forward */

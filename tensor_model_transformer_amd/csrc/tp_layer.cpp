@@ -337,8 +337,10 @@ int run_gemm(tp_layer* L, const GemmArgs& g, hipStream_t s) {
   return TP_OK;
 }
 
-// The side stream (created on first use), or the caller's stream if none.
+// The side stream (created on first use), or the caller's stream if none or
+// while profiling (each event pair then brackets its launch group alone).
 hipStream_t side_stream(tp_layer* L, hipStream_t s) {
+  if (L->prof.on) return s;
   if (!L->side_tried) {
     L->side_tried = true;
     hipStream_t st = nullptr;
