@@ -109,10 +109,12 @@ enum { TP_GELU_ERF = 0, TP_GELU_TANH = 1 };
 enum { TP_SCORES_AUTO = 0, TP_SCORES_FP16 = 1, TP_SCORES_SPLIT = 2 };
 /* Activation recomputation (selective recomputation, "Megatron-LM:
  * GPU-Cluster Training Parallelism", section "Microbatch and Activation
- * Memory Tradeoff"). TP_RECOMPUTE_NONE keeps the FC1 pre-activation u
- * [n, f_l] from forward to backward. TP_RECOMPUTE_FC1 does not keep it: the
- * backward recomputes u = c @ W_fc1,r + b_fc1,r (one more FC1 GEMM) and the
- * workspace shrinks by n*f_l elements. The attention probabilities are never
+ * Memory Tradeoff"). TP_RECOMPUTE_NONE keeps GeLU'(u) [n, f_l], the
+ * derivative of the FC1 activation at its pre-activation
+ * u = c @ W_fc1,r + b_fc1,r (computed in the FC1 epilogue together with
+ * GeLU(u)), from forward to backward. TP_RECOMPUTE_FC1 does not keep it: the
+ * backward recomputes it (one more FC1 GEMM) and the workspace shrinks by
+ * n*f_l elements. The attention probabilities are never
  * kept in either mode (the backward recomputes them from the saved
  * log-sum-exp). */
 enum { TP_RECOMPUTE_NONE = 0, TP_RECOMPUTE_FC1 = 1 };
@@ -361,15 +363,17 @@ int tp_layer_kv_fill(const tp_layer *L, const void *workspace, size_t workspace_
  *                   log2(sum_k exp(S_ik)) with S the scaled scores
  *   TP_TAP_H_MID    h_mid  [n, h]      fp32
  *   TP_TAP_LN2_OUT  c      [n, h]      act
- *   TP_TAP_FC1_PRE  u      [n, f_l]    act (FC1 output before GeLU;
- *                                      TP_ERR_UNSUPPORTED with TP_RECOMPUTE_FC1)
+ *   TP_TAP_FC1_DGELU GeLU'(u) [n, f_l] act (derivative of the FC1 activation
+ *                                      at the pre-activation u, kept for the
+ *                                      backward; TP_ERR_UNSUPPORTED with
+ *                                      TP_RECOMPUTE_FC1)
  *   TP_TAP_FC1_OUT  z      [n, f_l]    act
  *   TP_TAP_DQKV     dqkv   [n, 3*h_l]  act (after a backward)
  *   TP_TAP_DH       dh     [n, h]      fp32 (residual-stream grad, after TP_BWD_ATTN)
  * Returns TP_ERR_ARG for an unknown id. */
 enum {
   TP_TAP_LN1_OUT = 0, TP_TAP_QKV = 1, TP_TAP_ATTN_OUT = 2, TP_TAP_LSE = 3,
-  TP_TAP_H_MID = 4, TP_TAP_LN2_OUT = 5, TP_TAP_FC1_PRE = 6, TP_TAP_FC1_OUT = 7,
+  TP_TAP_H_MID = 4, TP_TAP_LN2_OUT = 5, TP_TAP_FC1_DGELU = 6, TP_TAP_FC1_OUT = 7,
   TP_TAP_DQKV = 8, TP_TAP_DH = 9
 };
 int tp_layer_tap(const tp_layer *L, int tap, size_t *offset, size_t *bytes);

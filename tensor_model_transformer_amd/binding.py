@@ -35,7 +35,7 @@ TP_MASK_CAUSAL, TP_MASK_PADDING = 0, 1
 TP_GELU_ERF, TP_GELU_TANH = 0, 1
 TP_ALL, TP_FWD_ATTN, TP_FWD_MLP = 0, 1, 2
 TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1 = 1, 2, 3
-TAPS = {"a": 0, "qkv": 1, "o": 2, "lse2": 3, "h_mid": 4, "c": 5, "u": 6, "z": 7,
+TAPS = {"a": 0, "qkv": 1, "o": 2, "lse2": 3, "h_mid": 4, "c": 5, "dgelu": 6, "z": 7,
         "dqkv": 8, "dh": 9}
 
 PARAM_FIELDS = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_o", "b_o",

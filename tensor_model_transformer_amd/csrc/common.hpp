@@ -227,16 +227,26 @@ __device__ __forceinline__ float gelu_f(float u, int tanh_form) {
   const float er = copysignf(erf_as7126(ax, ex2), u);
   return 0.5f * u * (1.f + er);
 }
-__device__ __forceinline__ float gelu_grad_f(float u, int tanh_form) {
+// GeLU(u) and GeLU'(u) together (the erf and the exponential shared).
+__device__ __forceinline__ void gelu_and_grad(float u, int tanh_form, float* z, float* gp) {
   if (tanh_form) {
     const float c = 0.7978845608028654f;
-    float th = tanhf(c * (u + 0.044715f * u * u * u));
-    return 0.5f * (1.f + th) + 0.5f * u * (1.f - th * th) * c * (1.f + 0.134145f * u * u);
+    const float th = tanhf(c * (u + 0.044715f * u * u * u));
+    *z = 0.5f * u * (1.f + th);
+    *gp = 0.5f * (1.f + th) + 0.5f * u * (1.f - th * th) * c * (1.f + 0.134145f * u * u);
+    return;
   }
   const float ax = fabsf(u) * 0.7071067811865476f;
   const float ex2 = exp2f(-1.4426950408889634f * ax * ax);
-  const float er = copysignf(erf_as7126(ax, ex2), u);
-  return 0.5f * (1.f + er) + u * 0.3989422804014327f * ex2;
+  const float cdf = 0.5f * (1.f + copysignf(erf_as7126(ax, ex2), u));  // Phi(u)
+  *z = u * cdf;
+  *gp = cdf + u * 0.3989422804014327f * ex2;
+}
+// GeLU'(u) alone: the same arithmetic as gelu_and_grad (bit for bit).
+__device__ __forceinline__ float gelu_grad_f(float u, int tanh_form) {
+  float z, gp;
+  gelu_and_grad(u, tanh_form, &z, &gp);
+  return gp;
 }
 
 }  // namespace tpl

@@ -52,15 +52,19 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float
     for (int e = 0; e < 4; ++e) v[e] += r[e];
   }
   if (g.epi == EPI_BIAS_GELU) {
+    // z = GeLU(v) to C2; C (if given) keeps GeLU'(v) for the backward
     float z[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = gelu_f(v[e], g.gelu_tanh);
+    for (int e = 0; e < 4; ++e) gelu_and_grad(v[e], g.gelu_tanh, &z[e], &v[e]);
     store4_dt(g.C2, g.c2_dtype, (size_t)m * g.ldc2 + n, z);
-  } else if (g.epi == EPI_DGELU) {
-    float u[4];
-    load4_dt(g.aux, g.aux_dtype, (size_t)m * g.ldaux + n, u);
+  } else if (g.epi == EPI_GELU_GRAD) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e], g.gelu_tanh);
+    for (int e = 0; e < 4; ++e) v[e] = gelu_grad_f(v[e], g.gelu_tanh);
+  } else if (g.epi == EPI_DGELU) {
+    float gp[4];
+    load4_dt(g.aux, g.aux_dtype, (size_t)m * g.ldaux + n, gp);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= gp[e];
   } else if (g.epi == EPI_SPLIT16) {
     // hi = fp16(v) goes to C below (exactly representable, so stored as is);
     // lo = v - hi is exact in fp32 and rounded once more to fp16 in C2.

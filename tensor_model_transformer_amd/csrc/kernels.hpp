@@ -67,7 +67,7 @@ hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts,
 // ---------------------------------------------------------------------------
 // GEMM (gemm.hip): C[M,N] = A[M,K] @ B[K,N] with a fused epilogue.
 // ---------------------------------------------------------------------------
-enum { EPI_STORE = 0, EPI_BIAS_GELU = 1, EPI_DGELU = 2, EPI_SPLIT16 = 3 };
+enum { EPI_STORE = 0, EPI_BIAS_GELU = 1, EPI_DGELU = 2, EPI_SPLIT16 = 3, EPI_GELU_GRAD = 4 };
 
 struct GemmArgs {
   // Arithmetic: DT_F32 (fp32 FMA, fp32 operands) or DT_F16 (fp16 MFMA,
@@ -79,7 +79,8 @@ struct GemmArgs {
   // B(k,n) = B[n*ldb + k] if b_kmajor else B[k*ldb + n]
   const void* B; long ldb; int b_kmajor; int b_dtype;
   // epilogue, per element: v = acc (+ bias[n]) (+ resid[m,n]);
-  //   EPI_BIAS_GELU: C = v, C2 = GeLU(v);  EPI_DGELU: C = v * GeLU'(aux[m,n]);
+  //   EPI_BIAS_GELU: C = GeLU'(v) (kept for the backward), C2 = GeLU(v);
+  //   EPI_GELU_GRAD: C = GeLU'(v);  EPI_DGELU: C = v * aux[m,n] (aux = GeLU'(u));
   //   EPI_SPLIT16: C = fp16(v), C2 = fp16(v - fp16(v)) (both fp16; v = C + C2
   //   to about 2^-22 relative);
   //   accumulate: C (fp32) += v.

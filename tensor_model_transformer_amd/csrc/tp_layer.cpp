@@ -60,7 +60,7 @@ struct tp_layer {
   int gelu_tanh;
   bool dx_f32;  // dx written in fp32 (else in the storage dtype)
   bool split_scores;  // qkv also kept as fp16 residuals; scores from three products
-  bool recompute_fc1;  // FC1 pre-activation recomputed in backward, not kept
+  bool recompute_fc1;  // GeLU'(u) of FC1 recomputed in backward, not kept
   bool sp;             // sequence-parallel layout (phases TP_*_SP_*)
   int nc;              // rows of this rank's token chunk in that layout (n / t)
   // derived
@@ -148,11 +148,12 @@ void plan(tp_layer* L) {
   take(L->mean2, n * 4);
   take(L->rstd2, n * 4);
   take(L->c, n * h * e);
-  // u (FC1 pre-activation) is kept from forward unless it is recomputed in
-  // backward. du has its own buffer, so a backward leaves the forward's saved
-  // tensors intact (it can be run again, e.g. to accumulate); with recompute,
-  // du and the recomputed u share one buffer placed over the attention-
-  // backward buffers, which are not yet live while du is.
+  // The "u" region keeps GeLU'(u), the derivative of the FC1 activation at
+  // its pre-activation u (all the backward needs of u), from forward unless it
+  // is recomputed in backward. du has its own buffer, so a backward leaves the
+  // forward's saved tensors intact (it can be run again, e.g. to accumulate);
+  // with recompute, du and the recomputed GeLU'(u) share one buffer placed
+  // over the attention-backward buffers, which are not yet live while du is.
   take(L->u, L->recompute_fc1 ? 0 : n * L->fl * e);
   take(L->z, n * L->fl * e);
   if (!L->recompute_fc1) take(L->du, n * L->fl * e);
@@ -543,18 +544,19 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   float* skw = at<float>(ws, L->splitk);
   GemmArgs g;
   if (L->recompute_fc1) {
-    // u = c @ W_fc1,r + b_fc1,r again, straight into the du buffer
+    // GeLU'(c @ W_fc1,r + b_fc1,r) again, straight into the du buffer
     g = gemm_base(L);
     g.M = n; g.N = fl; g.K = h;
     g.A = c_act; g.lda = h; g.a_kmajor = 1;
     g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 0;
     g.bias = p->b_fc1;
+    g.epi = EPI_GELU_GRAD;
     g.C = at<void>(ws, L->du); g.ldc = fl;
     if ((e = run_gemm(L, g, s))) return e;
   }
-  // du = (dout @ W_fc2,r^T) * GeLU'(u); with recompute u is in the du buffer
-  // and is overwritten in place (each element is read, then written, by the
-  // same thread of the epilogue)
+  // du = (dout @ W_fc2,r^T) * GeLU'(u), GeLU'(u) kept by the forward (in the
+  // u buffer) or recomputed into the du buffer, then overwritten in place
+  // (each element is read, then written, by the same thread of the epilogue)
   // side stream: db2 and dW2 (need only dout and z) while du is computed
   hipStream_t sd = side_stream(L, s);
   if ((e = fork_to(L, s, sd))) return e;
@@ -1129,7 +1131,7 @@ int tp_layer_tap(const tp_layer* L, int tap, size_t* offset, size_t* bytes) {
     case TP_TAP_LSE: r = &L->lse2; break;
     case TP_TAP_H_MID: r = &L->h_mid; break;
     case TP_TAP_LN2_OUT: r = &L->c; break;
-    case TP_TAP_FC1_PRE:
+    case TP_TAP_FC1_DGELU:
       if (L->recompute_fc1) return TP_ERR_UNSUPPORTED;  // not kept
       r = &L->u;
       break;

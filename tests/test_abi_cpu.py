@@ -132,8 +132,8 @@ def test_recompute_fc1_workspace(lib):
     rc, h1, ws1 = create(opts={"recompute": B.TP_RECOMPUTE_FC1}, **kw)
     assert rc == B.TP_OK
     assert ws0 - ws1 >= n * fl * 2
-    assert B.tp_layer_tap(h1, B.TAPS["u"])[0] == B.TP_ERR_UNSUPPORTED
-    assert B.tp_layer_tap(h0, B.TAPS["u"])[0] == B.TP_OK
+    assert B.tp_layer_tap(h1, B.TAPS["dgelu"])[0] == B.TP_ERR_UNSUPPORTED
+    assert B.tp_layer_tap(h0, B.TAPS["dgelu"])[0] == B.TP_OK
     B.tp_layer_destroy(h0)
     B.tp_layer_destroy(h1)
 
