@@ -20,13 +20,13 @@
 // the accumulator holds C transposed: each lane owns one output row and 4
 // consecutive columns per 32x32 tile, which the epilogue writes as one vector.
 //
-// Tiles wholly inside the matrix (every tile of the layer's GEMMs) are loaded
-// from HBM straight into LDS (buffer_load_dword*4 ... lds): no staging
-// registers and no LDS store instructions. Those loads write 64 consecutive
-// 16-byte chunks per instruction, so the tiles are unpadded and their 16-byte
-// chunks XOR-swizzled to keep the fragment reads free of bank conflicts.
-// Edge tiles (ragged shapes) take a register-staged kernel with padded tiles
-// and bounds checks.
+// When K is a whole number of K steps (every GEMM of the layer's shards), the
+// operand tiles are loaded from HBM straight into LDS (buffer_load_dword*4
+// ... lds): no staging registers and no LDS store instructions. Those loads
+// write 64 consecutive 16-byte chunks per instruction, so the tiles are
+// unpadded and their 16-byte chunks XOR-swizzled to keep the fragment reads
+// free of bank conflicts. Other K take a register-staged kernel with padded
+// tiles and bounds checks.
 //
 // fp32 path: a plain tiled FMA kernel (exact fp32 arithmetic).
 #include "common.hpp"
@@ -184,7 +184,8 @@ __device__ __forceinline__ f16x8 frag(const uint16_t* tile, int r0, int ks, int 
   }
 }
 
-// Edge tiles: register-staged loads with bounds checks into padded tiles.
+// K not a multiple of the K step: register-staged loads with bounds checks
+// into padded tiles.
 template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKM>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int ktiles_per_split) {
   constexpr int NT = WM * WN * 64;
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
 }
 
 // ----------------------------------------------------------------------------
-// Interior tiles: HBM -> LDS direct loads, two stages of BK = 64
+// HBM -> LDS direct loads, two stages of BK = 64
 // ----------------------------------------------------------------------------
 // s_waitcnt vmcnt(N), other counters not waited.
 template <int N>
@@ -652,26 +653,31 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
   const int ktiles = (int)ceil_div(g.K, BK);
   const int per = (int)ceil_div(ktiles, split);
   const int real_split = (int)ceil_div(ktiles, per);
-  // every tile inside the matrix, and byte offsets of both operands within
-  // 31 bits: the direct-load kernel
-  const bool interior = g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0 &&
-                        (size_t)(g.a_kmajor ? g.M : g.K) * g.lda * 2 < (1u << 31) &&
-                        (size_t)(g.b_kmajor ? g.N : g.K) * g.ldb * 2 < (1u << 31);
+  // The direct-load kernel takes every GEMM whose K is a whole number of
+  // K steps and whose operand byte offsets (up to one tile past M and N) fit
+  // 31 bits. Its loads have no bounds checks: the buffer descriptor returns
+  // zero beyond an operand's last byte, and a partial tile's rows or columns
+  // past M or N only ever reach outputs past M or N, which the epilogue
+  // skips.
+  const bool direct =
+      g.K % BK == 0 &&
+      ((size_t)(g.a_kmajor ? g.M + BM : g.K) * g.lda + BM) * 2 < (1u << 31) &&
+      ((size_t)(g.b_kmajor ? g.N + BN : g.K) * g.ldb + BN) * 2 < (1u << 31);
   const size_t slices = (size_t)WM * WN * 32 * (BN / WN + 4) * sizeof(float);
   const size_t lds_pad = (size_t)2 *
                          (TilePitch<BM, BK, AK>::kElems + TilePitch<BN, BK, BKM>::kElems) *
                          sizeof(uint16_t);
   const size_t lds_ops = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);
   const size_t lds_dtl = lds_ops > slices ? lds_ops : slices;
-  const size_t lds = interior ? lds_dtl : lds_pad;
-  auto kern = interior ? gemm_f16_dtl_kernel<BM, BN, WM, WN, AK, BKM>
+  const size_t lds = direct ? lds_dtl : lds_pad;
+  auto kern = direct ? gemm_f16_dtl_kernel<BM, BN, WM, WN, AK, BKM>
                        : gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM>;
   static bool attr_set[2] = {false, false};  // per instantiation
-  if (!attr_set[interior]) {
+  if (!attr_set[direct]) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set[interior] = true;
+    attr_set[direct] = true;
   }
   dim3 grid((unsigned)(ceil_div(g.M, BM) * ceil_div(g.N, BN)), (unsigned)real_split);
   GemmArgs a = g;
