@@ -66,128 +66,178 @@ __device__ __forceinline__ f16x8 pack8v(const f32x16& a, int off) {
   return pack8(v);
 }
 
-// Register staging for a [R][D] row-major slice of global memory (row stride
-// ld), rows >= nrows read as zero; stored into an LDS tile of pitch P. The
-// address is clamped to the last row (nrows >= 1) and the value selected.
-template <int R, int D, int NT>
-struct RowTile {
-  static constexpr int kChunks = R * (D / 8);
-  static constexpr int kPer = (kChunks + NT - 1) / NT;
-  uint4 st[kPer];
-  __device__ __forceinline__ void load(const f16* __restrict__ src, long ld, int r0, int nrows,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), dc = c % (D / 8);
-      const bool ok = (kChunks % NT == 0 || c < kChunks) & (r0 + row < nrows);
-      const int rr = min(r0 + row, nrows - 1);
-      const int cc = (kChunks % NT == 0 || c < kChunks) ? dc : 0;
-      const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)rr * ld + 8 * cc);
-      st[i] = ok ? v : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(f16* dst, int P, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), dc = c % (D / 8);
-      if (kChunks % NT == 0 || c < kChunks)
-        *reinterpret_cast<uint4*>(dst + row * P + 8 * dc) = st[i];
-    }
-  }
-};
+// ---- 64-row LDS tiles loaded straight from HBM ------------------------------
+// A tile holds 64 rows of D fp16 columns, unpadded (pitch D). The 16-byte
+// chunk c of row r sits in slot c ^ tsw<D>(r), a swizzle that keeps both the
+// row reads (8 columns of 32 rows, ds_read_b128) and the transposing reads
+// (4 columns of 4 rows per 16 lanes, ds_read_b64_tr_b16) of the MFMA operands
+// on distinct LDS banks. It only permutes chunks within an aligned group of
+// 4 (D = 32, 96, 160), 8 (64) or 16 (128), so a row stays a row.
+template <int D>
+__device__ __forceinline__ int tsw(int r) {
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 2) & 3;
+}
+template <int D>
+constexpr int kSwzMask = D == 64 ? 7 : D == 128 ? 15 : 3;
 
-// Workgroup barrier that leaves global loads in flight: this wave's LDS
-// traffic is drained (lgkmcnt(0)) but vmcnt is not waited, so tiles fetched
-// into registers for later blocks keep streaming across it. The empty asm
-// statements keep the compiler from moving memory operations across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+// Element offset of (row r, column col) in a swizzled tile; the chunk bits
+// the swizzle leaves alone are added separately so that unrolled constant
+// columns fold into the LDS instruction's immediate offset.
+template <int D>
+__device__ __forceinline__ int toff(int r, int col) {
+  const int c = col >> 3;
+  return r * D + 8 * (c & ~kSwzMask<D>) + 8 * ((c & kSwzMask<D>) ^ tsw<D>(r)) + (col & 7);
 }
 
-// K and V (and the K residual) tiles of one 64-key block, staged in registers.
-template <int D, bool SPLIT>
-struct KVRegs {
-  RowTile<64, D, 256> k, v, kl;
-  __device__ __forceinline__ void load(const f16* Kp, const f16* Vp, const f16* Klp, long ldq,
-                                       int r0, int seq, int tid) {
-    k.load(Kp, ldq, r0, seq, tid);
-    v.load(Vp, ldq, r0, seq, tid);
-    if constexpr (SPLIT) kl.load(Klp, ldq, r0, seq, tid);
-  }
-  __device__ __forceinline__ void store(f16* base, int P, int TILE, int tid) const {
-    k.store(base, P, tid);
-    v.store(base + TILE, P, tid);
-    if constexpr (SPLIT) kl.store(base + 2 * TILE, P, tid);
-  }
-};
+// Columns col .. col+7 (col a multiple of 8) of tile row r.
+template <int D>
+__device__ __forceinline__ f16x8 ld8s(const f16* T, int r, int col) {
+  return ld8(T + toff<D>(r, col));
+}
 
-// Block pipeline shared by the kernels that stream 64-row tiles through two
-// LDS buffers. Memory latency on this part runs to microseconds, longer than
-// one block's MFMA work, so when registers allow (DEEP) the tile of block
-// ib+1 is fetched two blocks ahead, at ib-2, into one of two register
-// stages; otherwise one block ahead. `fetch(stage, blk)` issues the global
-// loads, `put(stage, buf)` writes a staged tile to LDS buffer `buf`, and
-// `compute(ib)` consumes LDS buffer ib & 1.
-template <bool DEEP, typename Stage, typename Fetch, typename Put, typename Compute>
-__device__ __forceinline__ void block_pipeline(int nblk, Stage& sa, Stage& sb, Fetch fetch, Put put,
-                                               Compute compute) {
-  if (nblk <= 0) return;
-  fetch(sa, 0);
-  put(sa, 0);
-  if constexpr (DEEP) {
-    if (nblk > 1) fetch(sa, 1);
-    if (nblk > 2) fetch(sb, 2);
-    lds_barrier();
-    auto step = [&](int ib, Stage& st) {
-      compute(ib);
-      if (ib + 1 < nblk) put(st, (ib + 1) & 1);
-      if (ib + 3 < nblk) fetch(st, ib + 3);
-      lds_barrier();
-    };
-    for (int ib = 0; ib < nblk; ib += 2) {
-      step(ib, sa);
-      if (ib + 1 < nblk) step(ib + 1, sb);
-    }
-  } else {
-    lds_barrier();
-    for (int ib = 0; ib < nblk; ++ib) {
-      if (ib + 1 < nblk) fetch(sa, ib + 1);
-      compute(ib);
-      if (ib + 1 < nblk) put(sa, (ib + 1) & 1);
-      lds_barrier();
-    }
+// tr_frag (common.hpp) on a swizzled tile: MFMA operand whose rows are the
+// tile's columns m0 .. m0+31 and whose 8 reduction slots are tile rows
+// kA + 0..3 then kB + 0..3.
+template <int D>
+__device__ __forceinline__ f16x8 tr_frag_s(const f16* T, int m0, int kA, int kB, int lane) {
+  const int g = lane >> 4, L = lane & 15;
+  const int col = m0 + 16 * (g & 1) + 4 * (L & 3);
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TPL_LDS_V4S(T + toff<D>(kA + (L >> 2), col)));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TPL_LDS_V4S(T + toff<D>(kB + (L >> 2), col)));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  return __builtin_bit_cast(f16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
+}
+
+// buffer_load_dwordx4 ... lds (16 bytes per lane from the buffer into LDS at
+// lds + 16 * lane) written as inline asm. Issued through the builtin, the
+// compiler makes every later LDS read that carries no alias information (the
+// transposing reads among them) wait for all loads into LDS still in flight,
+// which would put each prefetch back in series with the MFMAs. The kernels
+// order these loads themselves: wait_groups / wait_vm, then a barrier, before
+// a stage is read. The s_nop covers the wait states a VMEM instruction needs
+// after a VALU write of an SGPR it reads (the descriptor), which the compiler
+// does not check for inline asm.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const void* lds, int voff) {
+  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(a)
+               : "memory");
+}
+
+// Issues this wave's share, D/32 loads of 16 bytes per lane, of the tile whose
+// row i is src[(r0 + i) * ld + 0 .. D-1]; the four waves of the workgroup
+// together load the whole tile. Rows at or past `rows` (r0 < rows) read as
+// zero: the buffer descriptor ends at the last valid row's last column.
+// wid is the wave index 0..3 (wave-uniform); ld * 128 < 2^31.
+template <int D>
+__device__ __forceinline__ void tile_dtl(const f16* src, long ld, int r0, int rows, f16* tile,
+                                         int wid, int lane) {
+  constexpr int CPR = D / 8;  // chunks per row; the tile is CPR loads of 64 chunks
+  static_assert(CPR % 4 == 0, "tile loads split evenly over four waves");
+  const int nr = min(rows - r0, 64);
+  const __amdgpu_buffer_rsrc_t rs =
+      buffer_rsrc(src + (size_t)r0 * ld, (int)(((nr - 1) * ld + D) * 2));
+#pragma unroll
+  for (int t = 0; t < CPR / 4; ++t) {
+    const int q = wid + 4 * t;
+    const int p = 64 * q + lane;
+    const int row = p / CPR, c = (p % CPR) ^ tsw<D>(row);
+    dma16(rs, tile + 8 * 64 * q, (row * (int)ld + 8 * c) * 2);
   }
 }
 
-// Waves per SIMD requested from the compiler: two where the registers fit
-// without spilling (forward and dQ up to head dim 96, dK/dV up to 64, without
-// the split-score residuals), else no constraint.
+// buffer_load_dword ... lds (4 bytes per lane into lds + 4 * lane), as dma16.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, const void* lds, int voff) {
+  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(a)
+               : "memory");
+}
+
+// One load per wave: 64 fp32 values src[r0 .. r0+63] into dst; entries at or
+// past `rows` (r0 < rows) read as zero.
+__device__ __forceinline__ void row_f32_dtl(const float* src, int r0, int rows, float* dst,
+                                            int lane) {
+  dma4(buffer_rsrc(src + r0, min(rows - r0, 64) * 4), dst, lane * 4);
+}
+
+// Block pipeline over S LDS stages for tiles loaded straight from HBM.
+// issue(blk, stage) issues block blk's loads (exactly LPB vector-memory
+// instructions per wave) into LDS stage `stage`; compute(blk, stage) consumes
+// it. dtl_prologue issues blocks 0 .. S-2; the caller then loads its register
+// operands and waits for all its loads (vmcnt(0)), so that no load the
+// compiler tracks is pending inside the loop (its own waits would then also
+// wait for the prefetches). In the loop, block ib+S-1 is issued, into the
+// stage block ib-1 used, before the MFMAs of block ib: S-1 blocks of loads are
+// in flight during the MFMAs. Each iteration waits for this wave's loads of
+// block ib, then a barrier makes every wave's loads visible and orders the
+// overwrite after all reads of block ib-1.
+template <int S, typename Issue>
+__device__ __forceinline__ void dtl_prologue(int nblk, Issue issue) {
+  static_assert(S >= 2 && S <= 4, "stage count");
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (i < nblk) issue(i, i);
+}
+template <int S, int LPB, typename Issue, typename Compute>
+__device__ __forceinline__ void dtl_loop(int nblk, Issue issue, Compute compute) {
+  int stage = 0;
+  for (int ib = 0; ib < nblk; ++ib) {
+    wait_groups<LPB>(min(S - 2, nblk - 1 - ib));
+    lds_barrier();
+    if (ib + S - 1 < nblk) issue(ib + S - 1, stage == 0 ? S - 1 : stage - 1);
+    compute(ib, stage);
+    stage = stage == S - 1 ? 0 : stage + 1;
+  }
+}
+
+// LDS stages: three when three stages of the workgroups that share a compute
+// unit (one per wave per SIMD) fit its 160 KB, else two.
+constexpr int attn_stages(int stage_bytes, int waves) {
+  return 3 * stage_bytes * waves <= 160 * 1024 ? 3 : 2;
+}
+
+// Waves per SIMD requested from the compiler where the registers fit without
+// spilling, else no constraint.
 template <int D, bool SPLIT>
-constexpr int kAttnWaves = (D <= 96 && !SPLIT) ? 2 : 1;
+constexpr int kFwdWaves = (D <= 96 && !SPLIT) ? 3 : 1;
 template <int D, bool SPLIT>
-constexpr int kDkdvWaves = (D <= 64 && !SPLIT) ? 2 : 1;
+constexpr int kDqWaves = (D <= 96 && !SPLIT) ? 2 : 1;
+template <int D, bool SPLIT>
+constexpr int kDkdvWaves = (D <= 96 && !SPLIT) ? 2 : 1;
+
+// Stage counts. Without a wave hint, two workgroups per compute unit are
+// assumed (the register use of those kernels allows two or one).
+template <int D, bool SPLIT>
+constexpr int kKvStageBytes = (SPLIT ? 3 : 2) * 64 * D * 2;  // K, V (, K residual)
+template <int D, bool SPLIT>
+constexpr int kQgStageBytes = (SPLIT ? 3 : 2) * 64 * D * 2 + 2 * 64 * 4;  // Q, dO (, Q res.), lse2, delta
+template <int D, bool SPLIT>
+constexpr int kFwdStages =
+    attn_stages(kKvStageBytes<D, SPLIT>, kFwdWaves<D, SPLIT> > 1 ? kFwdWaves<D, SPLIT> : 2);
+template <int D, bool SPLIT>
+constexpr int kDqStages =
+    attn_stages(kKvStageBytes<D, SPLIT>, kDqWaves<D, SPLIT> > 1 ? kDqWaves<D, SPLIT> : 2);
+template <int D, bool SPLIT>
+constexpr int kDkdvStages =
+    attn_stages(kQgStageBytes<D, SPLIT>, kDkdvWaves<D, SPLIT> > 1 ? kDkdvWaves<D, SPLIT> : 2);
 
 // ============================================================================
 // fp16 forward
 // ============================================================================
 // A workgroup owns 128 queries (32 per wave) of one (sequence, head) and
-// sweeps 64-key blocks; K and V tiles are double-buffered in LDS through
-// registers (the next block's loads are in flight during the current MFMAs).
+// sweeps 64-key blocks; the K and V tiles of the next blocks load straight
+// from HBM into LDS stages while the current block's MFMAs run.
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<D, SPLIT>))) void attn_fwd_f16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFwdWaves<D, SPLIT>))) void attn_fwd_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, f16* __restrict__ o,
     float* __restrict__ lse2, const int* __restrict__ valid_len, int seq, int Hl, int causal,
     float sl2) {
-  constexpr int KB = 64, P = D + 8, TILE = KB * P, NT = SPLIT ? 3 : 2;
+  constexpr int KB = 64, TILE = KB * D, NT = SPLIT ? 3 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* lds = reinterpret_cast<f16*>(smem);  // [2][K tile, V tile (, K residual tile)]
+  f16* lds = reinterpret_cast<f16*>(smem);  // [stages][K tile, V tile (, K residual tile)]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int qb = causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
   const int head = blockIdx.y, b = blockIdx.z;
@@ -205,6 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
   const int lim = causal ? min(q + 1, seq) : L;  // this lane's keys are [0, lim)
 
   f16x8 qf[D / 16], ql[SPLIT ? D / 16 : 1];
+  auto load_regs = [&]() {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -216,6 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
       ql[ks] = __builtin_bit_cast(f16x8, r);
     }
   }
+  };
   f32x16 O[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -224,14 +276,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
   float m_run = -INFINITY, l_run = 0.f;
 
   const int nblk = (kv_end + KB - 1) / KB;
-  KVRegs<D, SPLIT> sa, sb;
-  auto fetch = [&](KVRegs<D, SPLIT>& st, int blk) {
-    st.load(Kp, Vp, Klp, ldq, blk * KB, seq, tid);
+  auto issue = [&](int blk, int stg) {
+    f16* base = lds + stg * NT * TILE;
+    tile_dtl<D>(Kp, ldq, blk * KB, seq, base, w, lane);
+    tile_dtl<D>(Vp, ldq, blk * KB, seq, base + TILE, w, lane);
+    if constexpr (SPLIT) tile_dtl<D>(Klp, ldq, blk * KB, seq, base + 2 * TILE, w, lane);
   };
-  auto put = [&](const KVRegs<D, SPLIT>& st, int buf) { st.store(lds + buf * NT * TILE, P, TILE, tid); };
-  auto compute = [&](int ib) {
+  auto compute = [&](int ib, int stg) {
     const int kb0 = ib * KB;
-    const f16* Ks = lds + (ib & 1) * NT * TILE;
+    const f16* Ks = lds + stg * NT * TILE;
     const f16* Vs = Ks + TILE;
     const f16* Kls = Ks + 2 * TILE;  // residual tile (SPLIT only)
     if (!(causal && kb0 > qw0 + 31)) {  // some key of this block precedes a query of this wave
@@ -242,11 +295,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
         for (int e = 0; e < 16; ++e) S[st][e] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const int off = (32 * st + l32) * P + 16 * ks + 8 * hh;
-          const f16x8 kh = ld8(Ks + off);
+          const int r = 32 * st + l32, col = 16 * ks + 8 * hh;
+          const f16x8 kh = ld8s<D>(Ks, r, col);
           S[st] = mfma32(kh, qf[ks], S[st]);
           if constexpr (SPLIT) {
-            S[st] = mfma32(ld8(Kls + off), qf[ks], S[st]);
+            S[st] = mfma32(ld8s<D>(Kls, r, col), qf[ks], S[st]);
             S[st] = mfma32(kh, ql[ks], S[st]);
           }
         }
@@ -308,12 +361,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
         const f16x8 pf = pack8v(S[c >> 1], 8 * (c & 1));
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
-          O[t] = mfma32(tr_frag(Vs, P, 32 * t, 16 * c + 4 * hh, 16 * c + 8 + 4 * hh, lane), pf,
+          O[t] = mfma32(tr_frag_s<D>(Vs, 32 * t, 16 * c + 4 * hh, 16 * c + 8 + 4 * hh, lane), pf,
                         O[t]);
       }
     }
   };
-  block_pipeline<(D <= 128)>(nblk, sa, sb, fetch, put, compute);
+  dtl_prologue<kFwdStages<D, SPLIT>>(nblk, issue);
+  load_regs();
+  wait_vm<0>();
+  dtl_loop<kFwdStages<D, SPLIT>, NT * D / 32>(nblk, issue, compute);
 
   if (q < seq) {
     const float inv = 1.f / l_run;
@@ -376,21 +432,22 @@ __global__ __launch_bounds__(64) void attn_delta_kernel(const T* __restrict__ o,
 // ============================================================================
 // fp16 backward: dK, dV (a workgroup owns 128 keys, 32 per wave)
 // ============================================================================
-// Sweeps 64-query blocks (two 32-query halves per MFMA step); Q and dO tiles
-// are double-buffered in LDS through registers. Q^T and dO^T operands are
-// read from the row-major tiles with transposing LDS reads.
+// Sweeps 64-query blocks (two 32-query halves per MFMA step); the Q and dO
+// tiles (with the blocks' lse2 and delta) of the next blocks load straight
+// from HBM into LDS stages. Q^T and dO^T operands are read from the row-major
+// tiles with transposing LDS reads.
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D, SPLIT>))) void attn_bwd_dkdv_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
     const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale) {
-  constexpr int QB = 64, P = D + 8, TILE = QB * P, NT = SPLIT ? 3 : 2;
+  constexpr int QB = 64, TILE = QB * D, NT = SPLIT ? 3 : 2;
+  constexpr int SE = kQgStageBytes<D, SPLIT> / 2;  // stage size in f16 elements
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* lds = reinterpret_cast<f16*>(smem);                          // [2][Q, dO (, Q residual)]
-  float* ls = reinterpret_cast<float*>(lds + 2 * NT * TILE);        // [2][QB]
-  float* dl = ls + 2 * QB;                                          // [2][QB]
+  // [stages][Q tile, dO tile (, Q residual tile), lse2[QB], delta[QB] (fp32)]
+  f16* lds = reinterpret_cast<f16*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int kblk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int kw0 = kblk * 128 + w * 32;
@@ -407,6 +464,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
   const int L = causal ? seq : min(max(valid_len[b], 0), seq);
 
   f16x8 kf[D / 16], vf[D / 16], kl[SPLIT ? D / 16 : 1];
+  auto load_regs = [&]() {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
@@ -423,6 +481,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
       kl[ks] = __builtin_bit_cast(f16x8, r);
     }
   }
+  };
   f32x16 dK[D / 32], dV[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -432,39 +491,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
   const bool wave_keys_valid = kw0 < (causal ? seq : L);
   const int q_begin = causal ? kblk * 128 : 0;
   const int nblk = (seq - q_begin + QB - 1) / QB;
-  struct QGRegs {
-    RowTile<QB, D, 256> q, g, ql;
-    float ls, dl;
-  };
-  QGRegs sa, sb;
-  auto fetch = [&](QGRegs& st, int blk) {
+  // every wave issues the same loads per block: its share of each tile and
+  // one 64-entry row, lse2 (even waves) or delta (odd waves)
+  auto issue = [&](int blk, int stg) {
     const int q0 = q_begin + blk * QB;
-    st.q.load(Qp, ldq, q0, seq, tid);
-    st.g.load(dOp, ldo, q0, seq, tid);
-    if constexpr (SPLIT) st.ql.load(Qlp, ldq, q0, seq, tid);
-    if (tid < QB) {
-      const int qq = q0 + tid;
-      st.ls = qq < seq ? lsp[qq] : 0.f;
-      st.dl = qq < seq ? dlp[qq] : 0.f;
-    }
+    f16* base = lds + stg * SE;
+    tile_dtl<D>(Qp, ldq, q0, seq, base, w, lane);
+    tile_dtl<D>(dOp, ldo, q0, seq, base + TILE, w, lane);
+    if constexpr (SPLIT) tile_dtl<D>(Qlp, ldq, q0, seq, base + 2 * TILE, w, lane);
+    float* rows = reinterpret_cast<float*>(base + NT * TILE);
+    row_f32_dtl((w & 1) ? dlp : lsp, q0, seq, rows + (w & 1) * QB, lane);
   };
-  auto put = [&](const QGRegs& st, int buf) {
-    f16* base = lds + buf * NT * TILE;
-    st.q.store(base, P, tid);
-    st.g.store(base + TILE, P, tid);
-    if constexpr (SPLIT) st.ql.store(base + 2 * TILE, P, tid);
-    if (tid < QB) {
-      ls[buf * QB + tid] = st.ls;
-      dl[buf * QB + tid] = st.dl;
-    }
-  };
-  auto compute = [&](int ib) {
+  auto compute = [&](int ib, int stg) {
     const int q0 = q_begin + ib * QB;
-    const f16* Qs = lds + (ib & 1) * NT * TILE;
+    const f16* Qs = lds + stg * SE;
     const f16* Gs = Qs + TILE;
     const f16* Qls = Qs + 2 * TILE;  // residual tile (SPLIT only)
-    const float* lsb = ls + (ib & 1) * QB;
-    const float* dlb = dl + (ib & 1) * QB;
+    const float* lsb = reinterpret_cast<const float*>(Qs + NT * TILE);
+    const float* dlb = lsb + QB;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int qh0 = q0 + 32 * qs;  // first query of this half
@@ -474,14 +518,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
       for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const int off = (32 * qs + l32) * P + 16 * ks + 8 * hh;
-        const f16x8 qh = ld8(Qs + off);
+        const int r = 32 * qs + l32, col = 16 * ks + 8 * hh;
+        const f16x8 qh = ld8s<D>(Qs, r, col);
         S = mfma32(qh, kf[ks], S);
         if constexpr (SPLIT) {
-          S = mfma32(ld8(Qls + off), kf[ks], S);
+          S = mfma32(ld8s<D>(Qls, r, col), kf[ks], S);
           S = mfma32(qh, kl[ks], S);
         }
-        dP = mfma32(ld8(Gs + off), vf[ks], dP);
+        dP = mfma32(ld8s<D>(Gs, r, col), vf[ks], dP);
       }
       // element e: query qh0 + 8*(e>>2) + 4*hh + (e&3), key = this lane's key.
       // The lse / delta of those rows come as 4 vector reads; every element
@@ -524,13 +568,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
         const int kA = 32 * qs + 16 * c + 4 * hh, kB = kA + 8;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-          dV[t] = mfma32(tr_frag(Gs, P, 32 * t, kA, kB, lane), pf, dV[t]);
-          dK[t] = mfma32(tr_frag(Qs, P, 32 * t, kA, kB, lane), sf, dK[t]);
+          dV[t] = mfma32(tr_frag_s<D>(Gs, 32 * t, kA, kB, lane), pf, dV[t]);
+          dK[t] = mfma32(tr_frag_s<D>(Qs, 32 * t, kA, kB, lane), sf, dK[t]);
         }
       }
     }
   };
-  block_pipeline<(D <= 96 || (D <= 128 && !SPLIT))>(nblk, sa, sb, fetch, put, compute);
+  dtl_prologue<kDkdvStages<D, SPLIT>>(nblk, issue);
+  load_regs();
+  wait_vm<0>();
+  dtl_loop<kDkdvStages<D, SPLIT>, NT * D / 32 + 1>(nblk, issue, compute);
 
   if (key < seq) {
     f16* dk = dqkv + (tok0 + key) * ldq + (size_t)head * 3 * D + D;
@@ -555,15 +602,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
 // fp16 backward: dQ (a workgroup owns 128 queries, 32 per wave)
 // ============================================================================
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<D, SPLIT>))) void attn_bwd_dq_f16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D, SPLIT>))) void attn_bwd_dq_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
     const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale) {
-  constexpr int KB = 64, P = D + 8, TILE = KB * P, NT = SPLIT ? 3 : 2;
+  constexpr int KB = 64, TILE = KB * D, NT = SPLIT ? 3 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
-  f16* lds = reinterpret_cast<f16*>(smem);  // [2][K tile, V tile (, K residual tile)]
+  f16* lds = reinterpret_cast<f16*>(smem);  // [stages][K tile, V tile (, K residual tile)]
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int qb = causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
   const int head = blockIdx.y, b = blockIdx.z;
@@ -579,12 +626,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
   const int kv_end = causal ? min(seq, qb * 128 + 128) : L;
   const int lim = causal ? min(q + 1, seq) : L;
   const bool qok = q < seq;
-  const float lq = qok ? lse2[((size_t)b * Hl + head) * seq + q] : 0.f;
-  const float dq_ = qok ? delta[((size_t)b * Hl + head) * seq + q] : 0.f;
+  float lq, dq_;
   const f16* Qlp = SPLIT ? qkv_lo + tok0 * ldq + (size_t)head * 3 * D : nullptr;
   const f16* Klp = SPLIT ? Qlp + D : nullptr;
 
   f16x8 qf[D / 16], gf[D / 16], ql[SPLIT ? D / 16 : 1];
+  auto load_regs = [&]() {
+  lq = qok ? lse2[((size_t)b * Hl + head) * seq + q] : 0.f;
+  dq_ = qok ? delta[((size_t)b * Hl + head) * seq + q] : 0.f;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
@@ -600,6 +649,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
       ql[ks] = __builtin_bit_cast(f16x8, r);
     }
   }
+  };
   f32x16 dQ[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -607,14 +657,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
     for (int e = 0; e < 16; ++e) dQ[t][e] = 0.f;
 
   const int nblk = (kv_end + KB - 1) / KB;
-  KVRegs<D, SPLIT> sa, sb;
-  auto fetch = [&](KVRegs<D, SPLIT>& st, int blk) {
-    st.load(Kp, Vp, Klp, ldq, blk * KB, seq, tid);
+  auto issue = [&](int blk, int stg) {
+    f16* base = lds + stg * NT * TILE;
+    tile_dtl<D>(Kp, ldq, blk * KB, seq, base, w, lane);
+    tile_dtl<D>(Vp, ldq, blk * KB, seq, base + TILE, w, lane);
+    if constexpr (SPLIT) tile_dtl<D>(Klp, ldq, blk * KB, seq, base + 2 * TILE, w, lane);
   };
-  auto put = [&](const KVRegs<D, SPLIT>& st, int buf) { st.store(lds + buf * NT * TILE, P, TILE, tid); };
-  auto compute = [&](int ib) {
+  auto compute = [&](int ib, int stg) {
     const int kb0 = ib * KB;
-    const f16* Ks = lds + (ib & 1) * NT * TILE;
+    const f16* Ks = lds + stg * NT * TILE;
     const f16* Vs = Ks + TILE;
     const f16* Kls = Ks + 2 * TILE;  // residual tile (SPLIT only)
     if (!(causal && kb0 > qw0 + 31)) {
@@ -626,14 +677,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
         for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const int off = (32 * st + l32) * P + 16 * ks + 8 * hh;
-          const f16x8 kh = ld8(Ks + off);
+          const int r = 32 * st + l32, col = 16 * ks + 8 * hh;
+          const f16x8 kh = ld8s<D>(Ks, r, col);
           S = mfma32(kh, qf[ks], S);
           if constexpr (SPLIT) {
-            S = mfma32(ld8(Kls + off), qf[ks], S);
+            S = mfma32(ld8s<D>(Kls, r, col), qf[ks], S);
             S = mfma32(kh, ql[ks], S);
           }
-          dP = mfma32(ld8(Vs + off), gf[ks], dP);
+          dP = mfma32(ld8s<D>(Vs, r, col), gf[ks], dP);
         }
         // every (query, key) of this 32-key half allowed: no mask (a
         // wave-uniform test); otherwise masked elements get p = 0
@@ -659,12 +710,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves<
         const f16x8 sf = pack8(&dS[c >> 1][8 * (c & 1)]);
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
-          dQ[t] = mfma32(tr_frag(Ks, P, 32 * t, 16 * c + 4 * hh, 16 * c + 8 + 4 * hh, lane), sf,
+          dQ[t] = mfma32(tr_frag_s<D>(Ks, 32 * t, 16 * c + 4 * hh, 16 * c + 8 + 4 * hh, lane), sf,
                          dQ[t]);
       }
     }
   };
-  block_pipeline<(D <= 128)>(nblk, sa, sb, fetch, put, compute);
+  dtl_prologue<kDqStages<D, SPLIT>>(nblk, issue);
+  load_regs();
+  wait_vm<0>();
+  dtl_loop<kDqStages<D, SPLIT>, NT * D / 32>(nblk, issue, compute);
 
   if (qok) {
     f16* dq = dqkv + (tok0 + q) * ldq + (size_t)head * 3 * D;
@@ -820,13 +874,13 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(
 // ============================================================================
 // Host launchers
 // ============================================================================
-// Two buffers of two 64-row tiles (three with the score residuals).
+// Dynamic LDS: the kernels' stages of 64-row tiles.
 template <int D, bool SPLIT>
-static size_t fwd_lds() { return (size_t)(SPLIT ? 6 : 4) * 64 * (D + 8) * 2; }
+static size_t fwd_lds() { return (size_t)kFwdStages<D, SPLIT> * kKvStageBytes<D, SPLIT>; }
 template <int D, bool SPLIT>
-static size_t dkdv_lds() { return (size_t)(SPLIT ? 6 : 4) * 64 * (D + 8) * 2 + 4 * 64 * 4; }
+static size_t dkdv_lds() { return (size_t)kDkdvStages<D, SPLIT> * kQgStageBytes<D, SPLIT>; }
 template <int D, bool SPLIT>
-static size_t dq_lds() { return (size_t)(SPLIT ? 6 : 4) * 64 * (D + 8) * 2; }
+static size_t dq_lds() { return (size_t)kDqStages<D, SPLIT> * kKvStageBytes<D, SPLIT>; }
 
 template <typename K>
 static hipError_t set_lds(K kern, size_t bytes) {

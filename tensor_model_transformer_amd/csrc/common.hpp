@@ -202,6 +202,40 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* red) {
   }
 }
 
+// ---- waits and barriers for loads that stay in flight ----------------------------
+// s_waitcnt vmcnt(N), other counters not waited.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// vmcnt(n * L) for a wave-uniform n in 0..3: wait until at most n groups of
+// L loads issued after the one waited for are still in flight.
+template <int L>
+__device__ __forceinline__ void wait_groups(int n) {
+  if (n >= 3) wait_vm<3 * L>();
+  else if (n == 2) wait_vm<2 * L>();
+  else if (n == 1) wait_vm<L>();
+  else wait_vm<0>();
+}
+
+// Workgroup barrier after this wave's LDS operations completed (lgkmcnt(0));
+// global loads (including loads into LDS) may stay in flight, unlike
+// __syncthreads(). The empty asm statements keep the compiler from moving
+// memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Buffer descriptor over `bytes` bytes from p: loads past the end read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
 // ---- GeLU (exact erf form, or the tanh approximation) ---------------------------
 // erf(x) for x >= 0 from Abramowitz & Stegun, Handbook of Mathematical
 // Functions, formula 7.1.26 (rational approximation in t = 1/(1 + p x) times

@@ -296,23 +296,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
 // ----------------------------------------------------------------------------
 // HBM -> LDS direct loads, two stages of BK = 64
 // ----------------------------------------------------------------------------
-// s_waitcnt vmcnt(N), other counters not waited.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier after this wave's LDS operations completed (lgkmcnt(0));
-// global loads may stay in flight, unlike __syncthreads(). The empty asm
-// statements keep the compiler from moving memory operations across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // One operand tile of ROWS (M or N) x BK in LDS, filled by direct loads.
 //  K-contiguous source: ROWS lines of BK elements; 16-byte chunk position p
 //    of line r holds source chunk p ^ ((r >> 1) & 7). A fragment read covers
