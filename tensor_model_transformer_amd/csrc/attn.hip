@@ -110,21 +110,6 @@ __device__ __forceinline__ f16x8 tr_frag_s(const f16* T, int m0, int kA, int kB,
   return __builtin_bit_cast(f16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
 }
 
-// buffer_load_dwordx4 ... lds (16 bytes per lane from the buffer into LDS at
-// lds + 16 * lane) written as inline asm. Issued through the builtin, the
-// compiler makes every later LDS read that carries no alias information (the
-// transposing reads among them) wait for all loads into LDS still in flight,
-// which would put each prefetch back in series with the MFMAs. The kernels
-// order these loads themselves: wait_groups / wait_vm, then a barrier, before
-// a stage is read. The s_nop covers the wait states a VMEM instruction needs
-// after a VALU write of an SGPR it reads (the descriptor), which the compiler
-// does not check for inline asm.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const void* lds, int voff) {
-  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(a)
-               : "memory");
-}
-
 // Issues this wave's share, D/32 loads of 16 bytes per lane, of the tile whose
 // row i is src[(r0 + i) * ld + 0 .. D-1]; the four waves of the workgroup
 // together load the whole tile. Rows at or past `rows` (r0 < rows) read as
@@ -138,6 +123,7 @@ __device__ __forceinline__ void tile_dtl(const f16* src, long ld, int r0, int ro
   const int nr = min(rows - r0, 64);
   const __amdgpu_buffer_rsrc_t rs =
       buffer_rsrc(src + (size_t)r0 * ld, (int)(((nr - 1) * ld + D) * 2));
+  dma_guard();
 #pragma unroll
   for (int t = 0; t < CPR / 4; ++t) {
     const int q = wid + 4 * t;
@@ -147,18 +133,13 @@ __device__ __forceinline__ void tile_dtl(const f16* src, long ld, int r0, int ro
   }
 }
 
-// buffer_load_dword ... lds (4 bytes per lane into lds + 4 * lane), as dma16.
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, const void* lds, int voff) {
-  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
-  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(a)
-               : "memory");
-}
-
 // One load per wave: 64 fp32 values src[r0 .. r0+63] into dst; entries at or
 // past `rows` (r0 < rows) read as zero.
 __device__ __forceinline__ void row_f32_dtl(const float* src, int r0, int rows, float* dst,
                                             int lane) {
-  dma4(buffer_rsrc(src + r0, min(rows - r0, 64) * 4), dst, lane * 4);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + r0, min(rows - r0, 64) * 4);
+  dma_guard();
+  dma4(rs, dst, lane * 4);
 }
 
 // Block pipeline over S LDS stages for tiles loaded straight from HBM.

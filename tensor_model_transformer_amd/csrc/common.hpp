@@ -236,6 +236,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 
+// buffer_load_dwordx4 ... lds (16 bytes per lane from the buffer into LDS at
+// lds + 16 * lane) written as inline asm. Issued through the builtin, the
+// compiler makes every later LDS read that carries no alias information (the
+// transposing reads among them) wait for all loads into LDS still in flight,
+// which would put each prefetch back in series with the MFMAs. The kernels
+// order these loads themselves: wait_groups / wait_vm, then a barrier, before
+// a stage is read. Call dma_guard() before a group of these loads.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const void* lds, int voff) {
+  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(a)
+               : "memory");
+}
+// buffer_load_dword ... lds (4 bytes per lane into lds + 4 * lane), as dma16.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, const void* lds, int voff) {
+  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(a)
+               : "memory");
+}
+// The wait states a VMEM instruction needs after a VALU write of an SGPR it
+// reads (a descriptor built from a readfirstlane value), which the compiler
+// does not insert in front of inline asm.
+__device__ __forceinline__ void dma_guard() { asm volatile("s_nop 4" ::: "memory"); }
+
 // ---- GeLU (exact erf form, or the tanh approximation) ---------------------------
 // erf(x) for x >= 0 from Abramowitz & Stegun, Handbook of Mathematical
 // Functions, formula 7.1.26 (rational approximation in t = 1/(1 + p x) times

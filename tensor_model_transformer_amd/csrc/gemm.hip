@@ -327,6 +327,7 @@ struct DtlOperand {
   // (K-contiguous) or k * ld + row; byte offsets fit 31 bits (host check).
   __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t rs, int ld, int row0, int k0,
                                               uint16_t* stage, int wid, int lane) {
+    dma_guard();
 #pragma unroll
     for (int t = 0; t < kPerWave; ++t) {
       int q = wid + NW * t;
@@ -336,8 +337,7 @@ struct DtlOperand {
       const int c = pos ^ swz(line);
       const int off = KMAJ ? ((row0 + line) * ld + k0 + 8 * c) * 2
                            : ((k0 + line) * ld + row0 + 8 * c) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(stage + 64 * q * 8), 16, off, 0, 0, 0);
+      dma16(rs, stage + 64 * q * 8, off);
     }
   }
 
