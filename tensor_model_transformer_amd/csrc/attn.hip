@@ -142,36 +142,6 @@ __device__ __forceinline__ void row_f32_dtl(const float* src, int r0, int rows, 
   dma4(rs, dst, lane * 4);
 }
 
-// Block pipeline over S LDS stages for tiles loaded straight from HBM.
-// issue(blk, stage) issues block blk's loads (exactly LPB vector-memory
-// instructions per wave) into LDS stage `stage`; compute(blk, stage) consumes
-// it. dtl_prologue issues blocks 0 .. S-2; the caller then loads its register
-// operands and waits for all its loads (vmcnt(0)), so that no load the
-// compiler tracks is pending inside the loop (its own waits would then also
-// wait for the prefetches). In the loop, block ib+S-1 is issued, into the
-// stage block ib-1 used, before the MFMAs of block ib: S-1 blocks of loads are
-// in flight during the MFMAs. Each iteration waits for this wave's loads of
-// block ib, then a barrier makes every wave's loads visible and orders the
-// overwrite after all reads of block ib-1.
-template <int S, typename Issue>
-__device__ __forceinline__ void dtl_prologue(int nblk, Issue issue) {
-  static_assert(S >= 2 && S <= 4, "stage count");
-#pragma unroll
-  for (int i = 0; i < S - 1; ++i)
-    if (i < nblk) issue(i, i);
-}
-template <int S, int LPB, typename Issue, typename Compute>
-__device__ __forceinline__ void dtl_loop(int nblk, Issue issue, Compute compute) {
-  int stage = 0;
-  for (int ib = 0; ib < nblk; ++ib) {
-    wait_groups<LPB>(min(S - 2, nblk - 1 - ib));
-    lds_barrier();
-    if (ib + S - 1 < nblk) issue(ib + S - 1, stage == 0 ? S - 1 : stage - 1);
-    compute(ib, stage);
-    stage = stage == S - 1 ? 0 : stage + 1;
-  }
-}
-
 // LDS stages: three when three stages of the workgroups that share a compute
 // unit (one per wave per SIMD) fit its 160 KB, else two.
 constexpr int attn_stages(int stage_bytes, int waves) {

@@ -361,10 +361,16 @@ struct DtlOperand {
   }
 };
 
-// Same tiling and epilogue as gemm_f16_kernel. Iteration j: wait for this
-// wave's loads of stage j, barrier (stage j complete in LDS; every wave done
-// with stage j-1), issue the loads of stage j+1 into stage j-1's buffer, then
-// the MFMAs of stage j.
+// LDS stages of the direct-load GEMM: two 64-deep K steps. A third stage of
+// the 256-row tiles would need 168 KB (256x192) or 192 KB (256x256), more
+// than the 160 KB of a compute unit.
+constexpr int kGemmStages = 2;
+
+// Same tiling and epilogue as gemm_f16_kernel, K steps streamed through
+// kGemmStages LDS stages (dtl_prologue / dtl_loop): iteration j waits for
+// this wave's loads of step j, a barrier publishes them (and ends every
+// wave's reads of step j-1), the loads of step j+1 go into step j-1's
+// stage, then the MFMAs of step j run.
 template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, int ktiles_per_split) {
   constexpr int BK = 64, NW = WM * WN;
@@ -373,9 +379,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
   using OA = DtlOperand<BM, BK, NW, AK>;
   using OB = DtlOperand<BN, BK, NW, BKM>;
 
+  constexpr int S = kGemmStages;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* As = reinterpret_cast<uint16_t*>(smem);  // [2][BM * BK]
-  uint16_t* Bs = As + 2 * BM * BK;                   // [2][BN * BK]
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);  // [S][BM * BK]
+  uint16_t* Bs = As + S * BM * BK;                   // [S][BN * BK]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -405,20 +412,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  if (nk > 0) {
-    OA::load(ra, lda, m0, kt0 * BK, As, wid, lane);
-    OB::load(rb, ldb, n0, kt0 * BK, Bs, wid, lane);
-  }
-  for (int j = 0; j < nk; ++j) {
-    wait_vm<0>();
-    lds_barrier();
-    if (j + 1 < nk) {
-      const int nb = (j + 1) & 1;
-      OA::load(ra, lda, m0, (kt0 + j + 1) * BK, As + nb * BM * BK, wid, lane);
-      OB::load(rb, ldb, n0, (kt0 + j + 1) * BK, Bs + nb * BN * BK, wid, lane);
-    }
-    const uint16_t* as = As + (j & 1) * BM * BK;
-    const uint16_t* bs = Bs + (j & 1) * BN * BK;
+  auto issue = [&](int j, int st) {
+    OA::load(ra, lda, m0, (kt0 + j) * BK, As + st * BM * BK, wid, lane);
+    OB::load(rb, ldb, n0, (kt0 + j) * BK, Bs + st * BN * BK, wid, lane);
+  };
+  auto compute = [&](int j, int st) {
+    const uint16_t* as = As + st * BM * BK;
+    const uint16_t* bs = Bs + st * BN * BK;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       f16x8 af[TM], bfr[TN];
@@ -432,7 +432,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
         for (int jj = 0; jj < TN; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[jj], af[i], acc[i][jj], 0, 0, 0);
     }
-  }
+  };
+  dtl_prologue<S>(nk, issue);
+  dtl_loop<S, OA::kPerWave + OB::kPerWave>(nk, issue, compute);
 
   // Epilogue through LDS slices (see gemm_f16_kernel).
   constexpr int CP = WTN + 4;
@@ -650,7 +652,7 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
   const size_t lds_pad = (size_t)2 *
                          (TilePitch<BM, BK, AK>::kElems + TilePitch<BN, BK, BKM>::kElems) *
                          sizeof(uint16_t);
-  const size_t lds_ops = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);
+  const size_t lds_ops = (size_t)kGemmStages * (BM + BN) * BK * sizeof(uint16_t);
   const size_t lds_dtl = lds_ops > slices ? lds_ops : slices;
   const size_t lds = direct ? lds_dtl : lds_pad;
   auto kern = direct ? gemm_f16_dtl_kernel<BM, BN, WM, WN, AK, BKM>
