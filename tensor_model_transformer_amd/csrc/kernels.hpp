@@ -59,10 +59,6 @@ size_t reduce_scratch_floats(int nblk, int nout, int width);
 // dst[k][i] = fp16(src[k][i]) for bf16 src, i < count[k], k < nseg (1..4).
 hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
                   hipStream_t s);
-// For bf16 matrices src[k] [rows[k], cols[k]] (k < nseg, 1..4): dst[k] = the
-// fp16 copy [rows, cols] and dstT[k] = its transpose [cols, rows] in fp16.
-hipError_t to_f16_pair(const void* const* src, void* const* dst, void* const* dstT,
-                       const int* rows, const int* cols, int nseg, hipStream_t s);
 
 // dst[i] = sum_p parts[p][i]  (fp32 sum in order), written as dst_dtype.
 hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts,

@@ -536,87 +536,6 @@ hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count,
   return hipGetLastError();
 }
 
-// bf16 matrices [R][C] -> fp16 copies [R][C] and transposed fp16 copies
-// [C][R], up to 4 matrices per launch. A workgroup converts one 64x64 tile:
-// 16-byte loads along the rows, the plain copy stored from registers, the
-// transposed copy through an LDS tile (16-byte stores along its rows).
-struct CvtPairSegs {
-  const bf16* src[4];
-  f16* dst[4];
-  f16* dstT[4];
-  int rows[4], cols[4], tiles_c[4];
-  int start[5];  // prefix sums of the tile counts
-  int nseg;
-};
-
-__global__ __launch_bounds__(256) void to_f16_pair_kernel(CvtPairSegs c) {
-  __shared__ f16 tile[64][64 + 8];
-  const int b = blockIdx.x;
-  int sg = 0;
-  while (sg + 1 < c.nseg && b >= c.start[sg + 1]) ++sg;
-  const int t = b - c.start[sg];
-  const int R = c.rows[sg], C = c.cols[sg];
-  const int r0 = (t / c.tiles_c[sg]) * 64, c0 = (t % c.tiles_c[sg]) * 64;
-  const int tid = threadIdx.x;
-  const int cc = 8 * (tid & 7);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int rr = (tid >> 3) + 32 * h;
-    const int r = r0 + rr, col = c0 + cc;
-    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (r < R) {
-      if (col + 8 <= C) {
-        Vec8<bf16>::load(c.src[sg] + (size_t)r * C + col, f);
-        Vec8<f16>::store(c.dst[sg] + (size_t)r * C + col, f);
-      } else {
-        for (int e = 0; e < 8 && col + e < C; ++e) {
-          f[e] = bf2f(c.src[sg][(size_t)r * C + col + e]);
-          c.dst[sg][(size_t)r * C + col + e] = (f16)f[e];
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[rr][cc + e] = (f16)f[e];
-  }
-  __syncthreads();
-  // transposed: row col of dstT holds column col of the tile
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int tc = (tid >> 3) + 32 * h;  // tile column = dstT row
-    const int col = c0 + tc, r = r0 + cc;
-    if (col >= C) continue;
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (float)tile[cc + e][tc];
-    if (r + 8 <= R) {
-      Vec8<f16>::store(c.dstT[sg] + (size_t)col * R + r, f);
-    } else {
-      for (int e = 0; e < 8 && r + e < R; ++e) c.dstT[sg][(size_t)col * R + r + e] = (f16)f[e];
-    }
-  }
-}
-
-hipError_t to_f16_pair(const void* const* src, void* const* dst, void* const* dstT,
-                       const int* rows, const int* cols, int nseg, hipStream_t s) {
-  if (nseg < 1 || nseg > 4) return hipErrorInvalidValue;
-  CvtPairSegs c = {};
-  c.nseg = nseg;
-  c.start[0] = 0;
-  for (int i = 0; i < nseg; ++i) {
-    if (rows[i] < 0 || cols[i] < 0) return hipErrorInvalidValue;
-    c.src[i] = (const bf16*)src[i];
-    c.dst[i] = (f16*)dst[i];
-    c.dstT[i] = (f16*)dstT[i];
-    c.rows[i] = rows[i];
-    c.cols[i] = cols[i];
-    c.tiles_c[i] = (cols[i] + 63) / 64;
-    c.start[i + 1] = c.start[i] + ((rows[i] + 63) / 64) * c.tiles_c[i];
-  }
-  if (!c.start[nseg]) return hipSuccess;
-  to_f16_pair_kernel<<<c.start[nseg], 256, 0, s>>>(c);
-  return hipGetLastError();
-}
-
 // ----------------------------------------------------------------------------
 // out = a + bias (per column) + r over a [rows, h] block: the bias and
 // residual that the sequence-parallel layout adds after a reduce-scatter.

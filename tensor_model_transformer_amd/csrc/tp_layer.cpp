@@ -31,12 +31,6 @@ constexpr size_t kAlign = 256;
 // moves softmax outputs by several tenths of a percent, visible in the
 // gradient of W_qkv; at hidden <= 3072 the spread is about 1.
 constexpr int kSplitScoresHidden = 8192;
-// Tokens per step from which the forward GEMMs read transposed fp16 weight
-// copies ([out, in], K-contiguous; about 7 % faster than the transposing LDS
-// reads of the [in, out] copies on the layer's shapes) besides the [in, out]
-// copies the backward reads: the extra copy costs one more write of the
-// weights per step, the gain scales with the tokens.
-constexpr long kTransposedWeightTokens = 4096;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -81,9 +75,6 @@ struct tp_layer {
   // fp16 copies of the bf16 weights (made by the forward, read again by the
   // backward) and of the upstream gradient: the MFMA GEMMs read fp16 only
   Region w16_qkv, w16_o, w16_fc1, w16_fc2, dout16;
-  // transposed fp16 copies [out, in] for the forward GEMMs (wt_fwd only)
-  Region wt16_qkv, wt16_o, wt16_fc1, wt16_fc2;
-  bool wt_fwd;
   size_t ws_bytes;
   int split_w2, split_w1, split_wo, split_wqkv;
   double attn_pairs;  // allowed query-key pairs (causal); 0 for padding (lengths on device)
@@ -219,11 +210,6 @@ void plan(tp_layer* L) {
   take(L->w16_fc1, cvt ? h * L->fl * 2 : 0);
   take(L->w16_fc2, cvt ? (size_t)L->fl * h * 2 : 0);
   take(L->dout16, cvt ? n * h * 2 : 0);
-  const bool wt = cvt && L->wt_fwd;
-  take(L->wt16_qkv, wt ? h * 3 * L->hl * 2 : 0);
-  take(L->wt16_o, wt ? (size_t)L->hl * h * 2 : 0);
-  take(L->wt16_fc1, wt ? h * L->fl * 2 : 0);
-  take(L->wt16_fc2, wt ? (size_t)L->fl * h * 2 : 0);
   L->ws_bytes = off;
 }
 
@@ -416,65 +402,6 @@ int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
   return TP_OK;
 }
 
-// fp16 copies of bf16 weight matrices W [in, out] for the forward: the
-// [in, out] copy (read by the backward) and, with wt_fwd, also the [out, in]
-// transpose the forward GEMMs read.
-struct WCopy {
-  const void* w;
-  const Region* plain;
-  const Region* trans;
-  int in, out;
-};
-int weight_copies(tp_layer* L, std::initializer_list<WCopy> ws_list, void* ws, hipStream_t s) {
-  if (L->sdt != DT_BF16) return TP_OK;
-  if (!L->wt_fwd) {
-    const void* sp[4];
-    void* dp[4];
-    size_t np[4];
-    int k = 0;
-    double bytes = 0;
-    for (const WCopy& c : ws_list) {
-      sp[k] = c.w;
-      dp[k] = at<void>(ws, *c.plain);
-      np[k] = (size_t)c.in * c.out;
-      bytes += 4.0 * np[k];
-      ++k;
-    }
-    Scope ps(L, s, TP_K_CONVERT, 0, bytes);
-    HIP_TRY(to_f16(sp, dp, np, k, s));
-    return TP_OK;
-  }
-  const void* sp[4];
-  void* dp[4];
-  void* tp[4];
-  int rows[4], cols[4];
-  int k = 0;
-  double bytes = 0;
-  for (const WCopy& c : ws_list) {
-    sp[k] = c.w;
-    dp[k] = at<void>(ws, *c.plain);
-    tp[k] = at<void>(ws, *c.trans);
-    rows[k] = c.in;
-    cols[k] = c.out;
-    bytes += 6.0 * c.in * c.out;
-    ++k;
-  }
-  Scope ps(L, s, TP_K_CONVERT, 0, bytes);
-  HIP_TRY(to_f16_pair(sp, dp, tp, rows, cols, k, s));
-  return TP_OK;
-}
-
-// B operand of a forward GEMM X @ W with W [in, out]: the transposed fp16
-// copy (K-contiguous) when kept, else the [in, out] copy (or the fp32 W).
-void fwd_weight(tp_layer* L, void* ws, const Region& trans, const Region& plain, const void* w,
-                int in, int out, GemmArgs& g) {
-  if (L->sdt == DT_BF16 && L->wt_fwd) {
-    g.B = at<void>(ws, trans); g.ldb = in; g.b_kmajor = 1;
-  } else {
-    g.B = wmat(L, ws, plain, w); g.ldb = out; g.b_kmajor = 0;
-  }
-}
-
 // ---- forward pieces --------------------------------------------------------
 // x -> a -> qkv -> o -> (o @ W_o) [+ b_o + x] into `dst` (fp32 [n, h]).
 // With a_in (the sequence-parallel layout) LN1 has run per chunk already and
@@ -484,8 +411,8 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   const int n = L->n, h = L->hidden, hl = L->hl;
   int e;
   const double nh = (double)n * h;
-  if ((e = weight_copies(L, {{p->w_qkv, &L->w16_qkv, &L->wt16_qkv, h, 3 * hl},
-                             {p->w_o, &L->w16_o, &L->wt16_o, hl, h}}, ws, s)))
+  if ((e = to_f16_copies(L, {p->w_qkv, p->w_o}, {&L->w16_qkv, &L->w16_o},
+                         {(size_t)h * 3 * hl, (size_t)hl * h}, ws, s)))
     return e;
   if (!a_in) {
   Scope ps(L, s, TP_K_LN_FWD, 0, nh * 2 * L->esz + 8.0 * n);
@@ -495,7 +422,7 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   GemmArgs g = gemm_base(L);
   g.M = n; g.N = 3 * hl; g.K = h;
   g.A = a_in ? a_in : at<void>(ws, L->a); g.lda = h; g.a_kmajor = 1;
-  fwd_weight(L, ws, L->wt16_qkv, L->w16_qkv, p->w_qkv, h, 3 * hl, g);
+  g.B = wmat(L, ws, L->w16_qkv, p->w_qkv); g.ldb = 3 * hl; g.b_kmajor = 0;
   g.bias = p->b_qkv;
   g.C = at<void>(ws, L->qkv); g.ldc = 3 * hl;
   if (L->split_scores) {
@@ -513,7 +440,7 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = hl;
   g.A = at<void>(ws, L->o); g.lda = hl; g.a_kmajor = 1;
-  fwd_weight(L, ws, L->wt16_o, L->w16_o, p->w_o, hl, h, g);
+  g.B = wmat(L, ws, L->w16_o, p->w_o); g.ldb = h; g.b_kmajor = 0;
   if (designated) {
     g.bias = p->b_o;
     g.resid = x; g.ldr = h; g.resid_dtype = L->sdt;
@@ -531,8 +458,8 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
   float* h_mid = at<float>(ws, L->h_mid);
-  if ((e = weight_copies(L, {{p->w_fc1, &L->w16_fc1, &L->wt16_fc1, h, fl},
-                             {p->w_fc2, &L->w16_fc2, &L->wt16_fc2, fl, h}}, ws, s)))
+  if ((e = to_f16_copies(L, {p->w_fc1, p->w_fc2}, {&L->w16_fc1, &L->w16_fc2},
+                         {(size_t)h * fl, (size_t)fl * h}, ws, s)))
     return e;
   if (!c_in) {
   Scope ps(L, s, TP_K_LN_FWD, 0,
@@ -544,7 +471,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   GemmArgs g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
   g.A = c_in ? c_in : at<void>(ws, L->c); g.lda = h; g.a_kmajor = 1;
-  fwd_weight(L, ws, L->wt16_fc1, L->w16_fc1, p->w_fc1, h, fl, g);
+  g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 0;
   g.bias = p->b_fc1;
   g.epi = EPI_BIAS_GELU;
   g.C = L->recompute_fc1 ? nullptr : at<void>(ws, L->u); g.ldc = fl;
@@ -553,7 +480,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = fl;
   g.A = at<void>(ws, L->z); g.lda = fl; g.a_kmajor = 1;
-  fwd_weight(L, ws, L->wt16_fc2, L->w16_fc2, p->w_fc2, fl, h, g);
+  g.B = wmat(L, ws, L->w16_fc2, p->w_fc2); g.ldb = h; g.b_kmajor = 0;
   if (designated) {
     g.bias = p->b_fc2;
     g.resid = h_mid; g.ldr = h; g.resid_dtype = DT_F32;
@@ -621,7 +548,7 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
     g = gemm_base(L);
     g.M = n; g.N = fl; g.K = h;
     g.A = c_act; g.lda = h; g.a_kmajor = 1;
-    fwd_weight(L, ws, L->wt16_fc1, L->w16_fc1, p->w_fc1, h, fl, g);
+    g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 0;
     g.bias = p->b_fc1;
     g.epi = EPI_GELU_GRAD;
     g.C = at<void>(ws, L->du); g.ldc = fl;
@@ -1000,7 +927,6 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   L->recompute_fc1 = recompute == TP_RECOMPUTE_FC1;
   L->sp = seq_par == 1;
   L->nc = (int)(n / t);
-  L->wt_fwd = dtype == TP_DTYPE_BF16 && n >= kTransposedWeightTokens;
   L->split_scores = dtype == TP_DTYPE_BF16 &&
                     (scores == TP_SCORES_SPLIT ||
                      (scores == TP_SCORES_AUTO && hidden >= kSplitScoresHidden));

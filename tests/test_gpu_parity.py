@@ -75,16 +75,6 @@ def test_small_bf16_split_scores(w):
     _run(w, taps=True, scores=B.TP_SCORES_SPLIT)
 
 
-def test_transposed_weight_copies():
-    """At >= 4096 tokens the forward GEMMs read transposed fp16 weight copies
-    (made with the [in, out] copies by one conversion kernel in 64x64 tiles);
-    weight sides of 320, 480 and 160 columns leave partial tiles."""
-    w = Workload("d32_t2_4096tok", LayerDims(8, 512, 320, 10, 1280, t=2, dtype="bf16",
-                                            mask="causal"),
-                 rank=1, seed=26, affine="perturbed")
-    _run(w, taps=True)
-
-
 def test_small_fp32_d160_padding():
     w = SMALL_BF16[4].with_(name="d160_padding_f32",
                             dims=LayerDims(2, 40, 320, 2, 640, t=1, dtype="f32", mask="padding"),
