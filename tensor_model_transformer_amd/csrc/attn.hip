@@ -151,7 +151,7 @@ constexpr int attn_stages(int stage_bytes, int waves) {
 // Waves per SIMD requested from the compiler where the registers fit without
 // spilling, else no constraint.
 template <int D, bool SPLIT>
-constexpr int kFwdWaves = (D <= 96 && !SPLIT) ? 3 : 1;
+constexpr int kFwdWaves = (D <= 96 && !SPLIT) ? 2 : 1;
 template <int D, bool SPLIT>
 constexpr int kDqWaves = (D <= 96 && !SPLIT) ? 2 : 1;
 template <int D, bool SPLIT>
