@@ -142,6 +142,31 @@ __device__ __forceinline__ void row_f32_dtl(const float* src, int r0, int rows, 
   dma4(rs, dst, lane * 4);
 }
 
+// Workgroup coordinates on a 1-D grid of nblk * Hl * batch workgroups of
+// 128 rows each: (block along the sequence, head, sequence). Workgroup i runs
+// on XCD i % 8 (round-robin dispatch). When the (sequence, head) pairs divide
+// evenly over the 8 XCDs, each XCD takes whole pairs, so the workgroups that
+// stream one pair's K and V (or Q and dO) share that XCD's L2 instead of each
+// XCD reading every pair; an XCD starts the blocks of rank 0 of all its pairs
+// first, then rank 1, and so on. Block = rank, or nblk-1-rank with `reverse`
+// (the causal forward and dQ put their longest query blocks first).
+struct AttnWG {
+  int blk, head, b;
+};
+__device__ __forceinline__ AttnWG attn_wg(int nblk, int Hl, int batch, bool reverse) {
+  const int i = blockIdx.x, npairs = Hl * batch;
+  int rank, pair;
+  if (npairs % 8 == 0) {
+    const int per = npairs / 8, s = i / 8;
+    rank = s / per;
+    pair = (i % 8) + 8 * (s % per);
+  } else {
+    rank = i % nblk;
+    pair = i / nblk;
+  }
+  return AttnWG{reverse ? nblk - 1 - rank : rank, pair % Hl, pair / Hl};
+}
+
 // LDS stages: three when three stages of the workgroups that share a compute
 // unit (one per wave per SIMD) fit its 160 KB, else two.
 constexpr int attn_stages(int stage_bytes, int waves) {
@@ -182,16 +207,16 @@ constexpr int kDkdvStages =
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFwdWaves<D, SPLIT>))) void attn_fwd_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, f16* __restrict__ o,
-    float* __restrict__ lse2, const int* __restrict__ valid_len, int seq, int Hl, int causal,
-    float sl2) {
+    float* __restrict__ lse2, const int* __restrict__ valid_len, int batch, int seq, int Hl,
+    int causal, float sl2) {
   constexpr int KB = 64, TILE = KB * D, NT = SPLIT ? 3 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
   f16* lds = reinterpret_cast<f16*>(smem);  // [stages][K tile, V tile (, K residual tile)]
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qb = causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
-  const int head = blockIdx.y, b = blockIdx.z;
+  const AttnWG wg = attn_wg((seq + 127) / 128, Hl, batch, causal);
+  const int qb = wg.blk, head = wg.head, b = wg.b;
   const int qw0 = qb * 128 + w * 32;
   const int q = qw0 + l32;
   const long ldq = 3L * Hl * D, ldo = (long)Hl * D;
@@ -391,7 +416,8 @@ template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D, SPLIT>))) void attn_bwd_dkdv_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
-    const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale) {
+    const int* __restrict__ valid_len, int batch, int seq, int Hl, int causal, float sl2,
+    float scale) {
   constexpr int QB = 64, TILE = QB * D, NT = SPLIT ? 3 : 2;
   constexpr int SE = kQgStageBytes<D, SPLIT> / 2;  // stage size in f16 elements
   extern __shared__ __align__(16) unsigned char smem[];
@@ -400,7 +426,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int kblk = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const AttnWG wg = attn_wg((seq + 127) / 128, Hl, batch, false);
+  const int kblk = wg.blk, head = wg.head, b = wg.b;
   const int kw0 = kblk * 128 + w * 32;
   const int key = kw0 + l32;
   const long ldq = 3L * Hl * D, ldo = (long)Hl * D;
@@ -556,15 +583,16 @@ template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D, SPLIT>))) void attn_bwd_dq_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
-    const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale) {
+    const int* __restrict__ valid_len, int batch, int seq, int Hl, int causal, float sl2,
+    float scale) {
   constexpr int KB = 64, TILE = KB * D, NT = SPLIT ? 3 : 2;
   extern __shared__ __align__(16) unsigned char smem[];
   f16* lds = reinterpret_cast<f16*>(smem);  // [stages][K tile, V tile (, K residual tile)]
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qb = causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
-  const int head = blockIdx.y, b = blockIdx.z;
+  const AttnWG wg = attn_wg((seq + 127) / 128, Hl, batch, causal);
+  const int qb = wg.blk, head = wg.head, b = wg.b;
   const int qw0 = qb * 128 + w * 32;
   const int q = qw0 + l32;
   const long ldq = 3L * Hl * D, ldo = (long)Hl * D;
@@ -848,9 +876,9 @@ static hipError_t fwd_f16(const void* qkv, const void* qkv_lo, void* o, float* l
   const size_t lds = fwd_lds<D, SPLIT>();
   hipError_t e = set_lds(k, lds);
   if (e != hipSuccess) return e;
-  dim3 grid((seq + 127) / 128, Hl, batch);
+  dim3 grid((unsigned)((seq + 127) / 128 * Hl * batch));
   hipLaunchKernelGGL(k, grid, dim3(256), lds, s, (const f16*)qkv,
-                     (const f16*)qkv_lo, (f16*)o, lse2, vl, seq, Hl, causal, sl2);
+                     (const f16*)qkv_lo, (f16*)o, lse2, vl, batch, seq, Hl, causal, sl2);
   return hipGetLastError();
 }
 
@@ -864,15 +892,15 @@ static hipError_t bwd_f16(const void* qkv, const void* qkv_lo, const void* dO, c
   hipError_t e = set_lds(k1, lds1);
   if (e == hipSuccess) e = set_lds(k2, lds2);
   if (e != hipSuccess) return e;
-  dim3 grid((seq + 127) / 128, Hl, batch);
+  dim3 grid((unsigned)((seq + 127) / 128 * Hl * batch));
   hipLaunchKernelGGL(k1, grid, dim3(256), lds1, s, (const f16*)qkv,
-                     (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, seq, Hl,
-                     causal, sl2, scale);
+                     (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, batch, seq,
+                     Hl, causal, sl2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k2, grid, dim3(256), lds2, s, (const f16*)qkv,
-                     (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, seq, Hl,
-                     causal, sl2, scale);
+                     (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, batch, seq,
+                     Hl, causal, sl2, scale);
   return hipGetLastError();
 }
 
