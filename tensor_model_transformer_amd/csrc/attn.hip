@@ -148,21 +148,24 @@ __device__ __forceinline__ void row_f32_dtl(const float* src, int r0, int rows, 
 // evenly over the 8 XCDs, each XCD takes whole pairs, so the workgroups that
 // stream one pair's K and V (or Q and dO) share that XCD's L2 instead of each
 // XCD reading every pair; an XCD starts the blocks of rank 0 of all its pairs
-// first, then rank 1, and so on. Block = rank, or nblk-1-rank with `reverse`
-// (the causal forward and dQ put their longest query blocks first).
+// first, then rank 1, and so on. Otherwise, when the workgroups divide by 8,
+// XCD x takes the x-th eighth of the pair-major order (a pair straddles at
+// most two XCDs). Block = rank, or nblk-1-rank with `reverse` (the causal
+// forward and dQ put their longest query blocks first).
 struct AttnWG {
   int blk, head, b;
 };
 __device__ __forceinline__ AttnWG attn_wg(int nblk, int Hl, int batch, bool reverse) {
-  const int i = blockIdx.x, npairs = Hl * batch;
+  const int i = blockIdx.x, npairs = Hl * batch, nwg = nblk * npairs;
   int rank, pair;
   if (npairs % 8 == 0) {
     const int per = npairs / 8, s = i / 8;
     rank = s / per;
     pair = (i % 8) + 8 * (s % per);
   } else {
-    rank = i % nblk;
-    pair = i / nblk;
+    const int l = nwg % 8 == 0 ? (i % 8) * (nwg / 8) + i / 8 : i;
+    rank = l % nblk;
+    pair = l / nblk;
   }
   return AttnWG{reverse ? nblk - 1 - rank : rank, pair % Hl, pair / Hl};
 }
