@@ -437,6 +437,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
   dtl_loop<S, OA::kPerWave + OB::kPerWave>(nk, issue, compute);
 
   // Epilogue through LDS slices (see gemm_f16_kernel).
+  const bool plain = gridDim.y == 1 && g.C && !g.accumulate;
+  const bool pre_r = plain && g.resid && g.epi == EPI_STORE;
+  const bool pre_a = plain && !g.resid && g.epi == EPI_DGELU;
   constexpr int CP = WTN + 4;
   float* cs = reinterpret_cast<float*>(smem) + wid * 32 * CP;
   const int lrow = lane & 31, half = lane >> 5;
@@ -450,9 +453,41 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
         *reinterpret_cast<float4*>(cs + lrow * CP + j * 32 + 8 * jj + 4 * half) =
             make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
                         acc[i][j][4 * jj + 3]);
-    constexpr int LPR = WTN / 4;
+    constexpr int LPR = WTN / 4, RPI = 64 / LPR, NIT = 32 / RPI;
+    if (pre_r || pre_a) {
+      // Plain store with a residual, or the product with the kept GeLU':
+      // that operand (and the bias) for all NIT rows of this lane is loaded
+      // before the row loop, so its memory latency is paid once per slice.
+      // Same arithmetic, in the same order, as epilogue4.
+      const int c = 4 * (lane % LPR), n = n0 + wn * WTN + c;
+      const int mr = m0 + wm * WTM + i * 32 + lane / LPR;
+      const void* src = pre_r ? g.resid : g.aux;
+      const int sdt = pre_r ? g.resid_dtype : g.aux_dtype;
+      const long sld = pre_r ? g.ldr : g.ldaux;
+      float pp[NIT][4], bs[4] = {0.f, 0.f, 0.f, 0.f};
+      if (g.bias && n < g.N) load4_dt(g.bias, g.bias_dtype, n, bs);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int m = mr + it * RPI;
+        if (m < g.M && n < g.N) load4_dt(src, sdt, (size_t)m * sld + n, pp[it]);
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int m = mr + it * RPI;
+        const float4 q = *reinterpret_cast<const float4*>(cs + (lane / LPR + it * RPI) * CP + c);
+        float v[4] = {q.x, q.y, q.z, q.w};
+        if (g.bias) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += bs[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = pre_r ? v[e] + pp[it][e] : v[e] * pp[it][e];
+        if (m < g.M && n < g.N) store4_dt(g.C, g.c_dtype, (size_t)m * g.ldc + n, v);
+      }
+      continue;
+    }
 #pragma unroll 1
-    for (int r = lane / LPR; r < 32; r += 64 / LPR) {
+    for (int r = lane / LPR; r < 32; r += RPI) {
       const int c = 4 * (lane % LPR);
       const float4 q = *reinterpret_cast<const float4*>(cs + r * CP + c);
       float v[4] = {q.x, q.y, q.z, q.w};
