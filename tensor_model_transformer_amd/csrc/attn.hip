@@ -23,9 +23,10 @@
 // Scores are kept in the log2 domain (scale * log2(e) folded into S) and the
 // per-row normaliser is saved as lse2 = max + log2(sum).
 //
-// Backward (deterministic, no atomics): delta = rowsum(dO * O); one kernel
-// owns a block of keys and sweeps the queries (dK, dV); another owns a block
-// of queries and sweeps the keys (dQ). P is recomputed from lse2.
+// Backward (deterministic, no atomics): one kernel owns a block of queries
+// and sweeps the keys (dQ); it runs first and also writes delta =
+// rowsum(dO * O) of its queries. Another owns a block of keys and sweeps the
+// queries (dK, dV), reading delta. P is recomputed from lse2.
 //
 // fp32 path: one thread per query (forward, dQ) or key (dK, dV) with exact
 // fp32 arithmetic.
@@ -584,7 +585,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D, SPLIT>))) void attn_bwd_dq_f16_kernel(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
-    const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
+    const f16* __restrict__ o, const float* __restrict__ lse2, float* __restrict__ delta,
+    f16* __restrict__ dqkv,
     const int* __restrict__ valid_len, int batch, int seq, int Hl, int causal, float sl2,
     float scale) {
   constexpr int KB = 64, TILE = KB * D, NT = SPLIT ? 3 : 2;
@@ -603,6 +605,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D,
   const f16* Kp = Qp + D;
   const f16* Vp = Qp + 2 * D;
   const f16* dOp = dO + tok0 * ldo + (size_t)head * D;
+  const f16* Op = o + tok0 * ldo + (size_t)head * D;
   const int L = causal ? seq : min(max(valid_len[b], 0), seq);
   const int kv_end = causal ? min(seq, qb * 128 + 128) : L;
   const int lim = causal ? min(q + 1, seq) : L;
@@ -614,22 +617,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D,
   f16x8 qf[D / 16], gf[D / 16], ql[SPLIT ? D / 16 : 1];
   auto load_regs = [&]() {
   lq = qok ? lse2[((size_t)b * Hl + head) * seq + q] : 0.f;
-  dq_ = qok ? delta[((size_t)b * Hl + head) * seq + q] : 0.f;
+  // delta = rowsum(dO * O) of this query: each lane half sums its columns
+  float dsum = 0.f;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
+    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0), ov = make_uint4(0, 0, 0, 0);
     if (qok) {
       a = *reinterpret_cast<const uint4*>(Qp + (size_t)q * ldq + 16 * ks + 8 * hh);
       c = *reinterpret_cast<const uint4*>(dOp + (size_t)q * ldo + 16 * ks + 8 * hh);
+      ov = *reinterpret_cast<const uint4*>(Op + (size_t)q * ldo + 16 * ks + 8 * hh);
     }
     qf[ks] = __builtin_bit_cast(f16x8, a);
     gf[ks] = __builtin_bit_cast(f16x8, c);
+    const f16x8 of = __builtin_bit_cast(f16x8, ov);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)gf[ks][e], (float)of[e], dsum);
     if constexpr (SPLIT) {
       uint4 r = make_uint4(0, 0, 0, 0);
       if (qok) r = *reinterpret_cast<const uint4*>(Qlp + (size_t)q * ldq + 16 * ks + 8 * hh);
       ql[ks] = __builtin_bit_cast(f16x8, r);
     }
   }
+  dsum += __shfl_xor(dsum, 32, 64);
+  dq_ = dsum;
+  if (qok && hh == 0) delta[((size_t)b * Hl + head) * seq + q] = dsum;
   };
   f32x16 dQ[D / 32];
 #pragma unroll
@@ -885,9 +896,10 @@ static hipError_t fwd_f16(const void* qkv, const void* qkv_lo, void* o, float* l
 }
 
 template <int D, bool SPLIT>
-static hipError_t bwd_f16(const void* qkv, const void* qkv_lo, const void* dO, const float* lse2,
-                          const float* delta, void* dqkv, const int* vl, int batch, int seq,
-                          int Hl, int causal, float sl2, float scale, hipStream_t s) {
+// dQ runs first: it also computes delta = rowsum(dO * O), which dK/dV reads.
+static hipError_t bwd_f16(const void* qkv, const void* qkv_lo, const void* o, const void* dO,
+                          const float* lse2, float* delta, void* dqkv, const int* vl, int batch,
+                          int seq, int Hl, int causal, float sl2, float scale, hipStream_t s) {
   auto k1 = attn_bwd_dkdv_f16_kernel<D, SPLIT>;
   auto k2 = attn_bwd_dq_f16_kernel<D, SPLIT>;
   const size_t lds1 = dkdv_lds<D, SPLIT>(), lds2 = dq_lds<D, SPLIT>();
@@ -895,12 +907,12 @@ static hipError_t bwd_f16(const void* qkv, const void* qkv_lo, const void* dO, c
   if (e == hipSuccess) e = set_lds(k2, lds2);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((seq + 127) / 128 * Hl * batch));
-  hipLaunchKernelGGL(k1, grid, dim3(256), lds1, s, (const f16*)qkv,
-                     (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, batch, seq,
-                     Hl, causal, sl2, scale);
+  hipLaunchKernelGGL(k2, grid, dim3(256), lds2, s, (const f16*)qkv,
+                     (const f16*)qkv_lo, (const f16*)dO, (const f16*)o, lse2, delta, (f16*)dqkv,
+                     vl, batch, seq, Hl, causal, sl2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k2, grid, dim3(256), lds2, s, (const f16*)qkv,
+  hipLaunchKernelGGL(k1, grid, dim3(256), lds1, s, (const f16*)qkv,
                      (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, batch, seq,
                      Hl, causal, sl2, scale);
   return hipGetLastError();
@@ -922,15 +934,15 @@ static hipError_t fwd_d(int dtype, const void* qkv, const void* qkv_lo, void* o,
 }
 
 template <int D>
-static hipError_t bwd_d(int dtype, const void* qkv, const void* qkv_lo, const void* dO,
-                        const float* lse2, const float* delta, void* dqkv, const int* vl,
-                        int batch, int seq, int Hl, int causal, float sl2, float scale,
-                        hipStream_t s) {
+static hipError_t bwd_d(int dtype, const void* qkv, const void* qkv_lo, const void* o,
+                        const void* dO, const float* lse2, float* delta, void* dqkv,
+                        const int* vl, int batch, int seq, int Hl, int causal, float sl2,
+                        float scale, hipStream_t s) {
   if (dtype == DT_F16) {
     if (qkv_lo)
-      return bwd_f16<D, true>(qkv, qkv_lo, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal,
+      return bwd_f16<D, true>(qkv, qkv_lo, o, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal,
                               sl2, scale, s);
-    return bwd_f16<D, false>(qkv, nullptr, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal,
+    return bwd_f16<D, false>(qkv, nullptr, o, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal,
                              sl2, scale, s);
   } else {
     const long n = (long)batch * Hl * seq;
@@ -969,23 +981,22 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* qkv_lo, const void* 
                     int seq, int Hl, int D, int mask, hipStream_t s) {
   if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
   if (qkv_lo && dtype != DT_F16) return hipErrorInvalidValue;
-  if (dtype == DT_F16)
-    attn_delta_kernel<f16><<<(unsigned)(batch * seq), 64, (size_t)Hl * D / 8 * 4, s>>>(
-        (const f16*)o, (const f16*)dO, delta, seq, Hl, D);
-  else
+  // fp32: delta by its own kernel; fp16: the dQ kernel computes it
+  if (dtype != DT_F16) {
     attn_delta_kernel<float><<<(unsigned)(batch * seq), 64, (size_t)Hl * D / 4 * 4, s>>>(
         (const float*)o, (const float*)dO, delta, seq, Hl, D);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int causal = mask == 0;
   const double sc = 1.0 / sqrt((double)D);
   const float sl2 = (float)(1.4426950408889634 * sc), scale = (float)sc;
   switch (D) {
-    case 32: return bwd_d<32>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
-    case 64: return bwd_d<64>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
-    case 96: return bwd_d<96>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
-    case 128: return bwd_d<128>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
-    case 160: return bwd_d<160>(dtype, qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 32: return bwd_d<32>(dtype, qkv, qkv_lo, o, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 64: return bwd_d<64>(dtype, qkv, qkv_lo, o, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 96: return bwd_d<96>(dtype, qkv, qkv_lo, o, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 128: return bwd_d<128>(dtype, qkv, qkv_lo, o, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
+    case 160: return bwd_d<160>(dtype, qkv, qkv_lo, o, dO, lse2, delta, dqkv, valid_len, batch, seq, Hl, causal, sl2, scale, s);
     default: return hipErrorInvalidValue;
   }
 }
