@@ -145,23 +145,34 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) dg[i][e] = db[i][e] = ds[i][e] = 0.f;
 
-  // Rows of up to 512 threads: row r + 1's inputs are fetched while row r is
-  // reduced and written. Wider rows (1024 threads) have no registers for the
-  // second copy and load each row in turn.
+  // Rows of up to 512 threads: row r + 1's inputs (with its mean and rstd)
+  // are fetched while row r is reduced and written, and gamma is loaded once.
+  // Wider rows (1024 threads) have no registers for the second copy and load
+  // each row in turn.
   if constexpr (NT <= 512) {
-  float nd[NV][8], nx[NV][8], nr[NV][8];
+  float nd[NV][8], nx[NV][8], nr[NV][8], gm[NV][8];
+  float nmu = 0.f, nrs = 0.f;
 #define TPL_LNB_FETCH(ROW)                                                     \
-  _Pragma("unroll") for (int i = 0; i < NV; ++i) {                             \
-    const int j = tid + i * NT;                                                \
-    if (j < nvec) {                                                            \
-      Vec8<float>::load(dy + (size_t)(ROW) * h + 8 * j, nd[i]);               \
-      Vec8<Tx>::load(x + (size_t)(ROW) * h + 8 * j, nx[i]);                   \
-      Vec8<Tr>::load(dres + (size_t)(ROW) * h + 8 * j, nr[i]);                \
+  {                                                                            \
+    nmu = mean[ROW];                                                           \
+    nrs = rstd[ROW];                                                           \
+    _Pragma("unroll") for (int i = 0; i < NV; ++i) {                           \
+      const int j = tid + i * NT;                                              \
+      if (j < nvec) {                                                          \
+        Vec8<float>::load(dy + (size_t)(ROW) * h + 8 * j, nd[i]);             \
+        Vec8<Tx>::load(x + (size_t)(ROW) * h + 8 * j, nx[i]);                 \
+        Vec8<Tr>::load(dres + (size_t)(ROW) * h + 8 * j, nr[i]);              \
+      }                                                                        \
     }                                                                          \
   }
   if (r0 < r1) TPL_LNB_FETCH(r0)
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = tid + i * NT;
+    if (j < nvec) Vec8<T>::load(gamma + 8 * j, gm[i]);
+  }
   for (int row = r0; row < r1; ++row) {
-    const float mu = mean[row], rs = rstd[row];
+    const float mu = nmu, rs = nrs;
     float d[NV][8], xv[NV][8], rv[NV][8];
 #pragma unroll
     for (int i = 0; i < NV; ++i)
@@ -178,8 +189,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
     for (int i = 0; i < NV; ++i) {
       const int j = tid + i * NT;
       if (j < nvec) {
-        float g[8];
-        Vec8<T>::load(gamma + 8 * j, g);
+        const float* g = gm[i];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           xh[i][e] = (xv[i][e] - mu) * rs;
