@@ -68,6 +68,23 @@ def test_small_bf16_local(w):
     _run(w, taps=True)
 
 
+# Attention workgroup placement over the 8 XCDs: 6 (sequence, head) pairs x 4
+# query blocks (the pairs do not divide by 8, the 24 workgroups do: each XCD
+# takes a contiguous eighth of the pair-major order) and 16 pairs x 3 blocks
+# (whole pairs per XCD, three ranks of blocks).
+PLACEMENT = [
+    Workload("pairs6_blocks4", LayerDims(2, 400, 384, 6, 768, t=2, dtype="bf16", mask="causal"),
+             rank=1, seed=27, affine="perturbed"),
+    Workload("pairs16_blocks3", LayerDims(4, 300, 256, 4, 512, t=1, dtype="bf16", mask="causal"),
+             rank=0, seed=28, affine="perturbed"),
+]
+
+
+@pytest.mark.parametrize("w", PLACEMENT, ids=lambda w: w.name)
+def test_attention_placement(w):
+    _run(w, taps=True)
+
+
 @pytest.mark.parametrize("w", [SMALL_BF16[i] for i in (1, 3, 4)], ids=lambda w: w.name)
 def test_small_bf16_split_scores(w):
     # scores from the fp16 Q, K plus their rounding residuals
