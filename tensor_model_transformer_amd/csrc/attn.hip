@@ -964,6 +964,8 @@ hipError_t attn_fwd(int dtype, const void* qkv, const void* qkv_lo, void* o, flo
                     hipStream_t s) {
   if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
   if (qkv_lo && dtype != DT_F16) return hipErrorInvalidValue;
+  // direct tile loads address 64 rows of the qkv row stride in 31 bits
+  if (3L * Hl * D * 128 >= (1L << 31)) return hipErrorInvalidValue;
   const int causal = mask == 0;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
   switch (D) {
@@ -981,6 +983,7 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* qkv_lo, const void* 
                     int seq, int Hl, int D, int mask, hipStream_t s) {
   if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
   if (qkv_lo && dtype != DT_F16) return hipErrorInvalidValue;
+  if (3L * Hl * D * 128 >= (1L << 31)) return hipErrorInvalidValue;
   // fp32: delta by its own kernel; fp16: the dQ kernel computes it
   if (dtype != DT_F16) {
     attn_delta_kernel<float><<<(unsigned)(batch * seq), 64, (size_t)Hl * D / 4 * 4, s>>>(
