@@ -143,6 +143,20 @@ __device__ __forceinline__ void row_f32_dtl(const float* src, int r0, int rows, 
   dma4(rs, dst, lane * 4);
 }
 
+// x and the value of lane l ^ 32, as the two outputs of v_permlane32_swap
+// (gfx950: lanes 32-63 of the first operand trade places with lanes 0-31 of
+// the second). Both operands hold x; the second is an opaque copy so that
+// the compiler cannot treat the swap of one value with itself as a no-op.
+// max(a, b) or a + b of the pair combines each lane with its partner in the
+// other half without an LDS round trip.
+__device__ __forceinline__ void pair32(float x, float* a, float* b) {
+  unsigned y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(__builtin_bit_cast(unsigned, x)));
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), y, false, false);
+  *a = __builtin_bit_cast(float, (unsigned)r[0]);
+  *b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 // Workgroup coordinates on a 1-D grid of nblk * Hl * batch workgroups of
 // 128 rows each: (block along the sequence, head, sequence). Workgroup i runs
 // on XCD i % 8 (round-robin dispatch). When the (sequence, head) pairs divide
@@ -304,7 +318,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFwdWaves<D
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[st][e]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      {
+        float a, b;
+        pair32(mx, &a, &b);
+        mx = fmaxf(a, b);
+      }
       // Lazy rescaling: the reference point m_run (log2 domain) moves only
       // when this block's maximum exceeds it by more than kSlack, so p stays
       // below 2^kSlack (exact in fp32, and well inside fp16 for the P operand)
@@ -331,7 +349,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFwdWaves<D
           S[st][e] = p;
           ls += p;
         }
-      ls += __shfl_xor(ls, 32, 64);
+      {
+        float a, b;
+        pair32(ls, &a, &b);
+        ls = a + b;
+      }
       l_run += ls;
       // O^T[d][q] += sum_key V[key][d] P[q][key]; 16 keys per MFMA, slot order
       // {4h..4h+3, 8+4h..8+4h+3} within the 16 (the accumulator's row order)
