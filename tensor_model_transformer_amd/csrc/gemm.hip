@@ -37,11 +37,18 @@ namespace tpl {
 // ----------------------------------------------------------------------------
 // Epilogue on 4 consecutive columns n..n+3 of row m (N % 4 == 0).
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float v[4]) {
+// bias4, when given, holds bias[n .. n+3], already loaded.
+__device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float v[4],
+                                          const float* bias4 = nullptr) {
   if (m >= g.M || n >= g.N) return;
   if (g.bias) {
     float b[4];
-    load4_dt(g.bias, g.bias_dtype, n, b);
+    if (bias4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = bias4[e];
+    } else {
+      load4_dt(g.bias, g.bias_dtype, n, b);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] += b[e];
   }
@@ -486,14 +493,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
       }
       continue;
     }
+    // a lane's columns, hence its bias values, are the same in every row
+    const int c = 4 * (lane % LPR), n = n0 + wn * WTN + c;
+    float bs[4] = {0.f, 0.f, 0.f, 0.f};
+    if (g.bias && gridDim.y == 1 && n < g.N) load4_dt(g.bias, g.bias_dtype, n, bs);
 #pragma unroll 1
     for (int r = lane / LPR; r < 32; r += RPI) {
-      const int c = 4 * (lane % LPR);
       const float4 q = *reinterpret_cast<const float4*>(cs + r * CP + c);
       float v[4] = {q.x, q.y, q.z, q.w};
-      const int m = m0 + wm * WTM + i * 32 + r, n = n0 + wn * WTN + c;
+      const int m = m0 + wm * WTM + i * 32 + r;
       if (gridDim.y > 1) partial4(g, split_idx, m, n, v);
-      else epilogue4(g, m, n, v);
+      else epilogue4(g, m, n, v, bs);
     }
   }
 }
