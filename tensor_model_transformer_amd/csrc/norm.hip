@@ -30,12 +30,19 @@ __global__ __launch_bounds__(NT) void ln_fwd_kernel(
   const int tid = threadIdx.x;
   const int nvec = h >> 3;
   const Tin* xr = x + (size_t)row * h;
-  float v[NV][8];
+  // Up to two vectors per thread, gamma and beta are loaded with the row,
+  // ahead of the two reductions (wider rows have no registers to spare).
+  constexpr bool kEarly = NV <= 2;
+  float v[NV][8], gm[kEarly ? NV : 1][8], bt[kEarly ? NV : 1][8];
   float acc[1] = {0.f};
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int j = tid + i * NT;
     if (j < nvec) {
+      if constexpr (kEarly) {
+        Vec8<T>::load(gamma + 8 * j, gm[i]);
+        Vec8<T>::load(beta + 8 * j, bt[i]);
+      }
       Vec8<Tin>::load(xr + 8 * j, v[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[0] += v[i][e];
@@ -65,8 +72,16 @@ __global__ __launch_bounds__(NT) void ln_fwd_kernel(
     const int j = tid + i * NT;
     if (j < nvec) {
       float g[8], b[8], o[8];
-      Vec8<T>::load(gamma + 8 * j, g);
-      Vec8<T>::load(beta + 8 * j, b);
+      if constexpr (kEarly) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          g[e] = gm[i][e];
+          b[e] = bt[i][e];
+        }
+      } else {
+        Vec8<T>::load(gamma + 8 * j, g);
+        Vec8<T>::load(beta + 8 * j, b);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = g[e] * ((v[i][e] - mu) * rstd) + b[e];
       Vec8<To>::store(y + (size_t)row * h + 8 * j, o);
