@@ -44,23 +44,63 @@ def algorithmic_flops(d, valid_len):
     return 3 * (gemm + 4 * d.head_dim * d.heads_local * pairs)
 
 
-def cpu_baseline(w, seqs, min_seconds):
-    """The fp64 oracle timed on the host on a bounded sample: the same layer
-    shard with `seqs` sequences (default: the whole micro-batch), forward +
-    backward, repeated until `min_seconds` of CPU work have run."""
+def _blas_info():
+    """Vendor, version and thread count of the BLAS NumPy runs the oracle on."""
+    try:
+        import numpy  # noqa: F401  (loads the BLAS that threadpoolctl inspects)
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"blas": f"{i.get('internal_api')} {i.get('version')}",
+                        "threads": int(i.get("num_threads", 1))}
+    except Exception:
+        pass
+    return {"blas": "unknown", "threads": os.cpu_count() or 1}
+
+
+def _physical_cores():
+    """Physical cores of the host (distinct (package, core) pairs), or None."""
+    try:
+        seen = set()
+        base = "/sys/devices/system/cpu"
+        for c in os.listdir(base):
+            if not (c.startswith("cpu") and c[3:].isdigit()):
+                continue
+            topo = os.path.join(base, c, "topology")
+            with open(os.path.join(topo, "physical_package_id")) as f:
+                pkg = f.read().strip()
+            with open(os.path.join(topo, "core_id")) as f:
+                core = f.read().strip()
+            seen.add((pkg, core))
+        return len(seen) or None
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, tokens, min_seconds, params=None):
+    """The fp64 oracle timed on the host on a bounded sample of the shard:
+    the same layer shard (same hidden, heads, FFN, t, rank, weights) over
+    `tokens` tokens -- whole sequences when the micro-batch has several, else
+    the first `tokens` positions of the sequence -- forward + backward, repeated
+    until `min_seconds` of CPU work have run. The rate is the sample's
+    algorithmic FLOPs over the time, the same count the GPU figure uses."""
     from oracle import layer as OL
     from tensor_model_transformer_amd.synth import layer_inputs, rank_params
 
     d = w.dims
-    seqs = min(seqs or d.batch, d.batch)
-    ws = w.with_(dims=d.__class__(seqs, d.seq, d.hidden, d.heads, d.ffn, d.t, d.dtype, d.mask))
-    params = rank_params(ws)
+    if d.batch > 1:
+        seqs = max(1, min(d.batch, tokens // d.seq))
+        dims = d.__class__(seqs, d.seq, d.hidden, d.heads, d.ffn, d.t, d.dtype, d.mask)
+        what = f"{seqs} of {d.batch} sequences"
+    else:
+        s = max(1, min(d.seq, tokens))
+        dims = d.__class__(1, s, d.hidden, d.heads, d.ffn, d.t, d.dtype, d.mask)
+        what = f"the first {s} of {d.seq} positions"
+    ws = w.with_(dims=dims)
+    if params is None:
+        params = rank_params(ws)
     x, dout, vl = layer_inputs(ws)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    info = _blas_info()
     reps, dt = 0, 0.0
     while reps == 0 or dt < min_seconds:
         t0 = time.perf_counter()
@@ -68,10 +108,83 @@ def cpu_baseline(w, seqs, min_seconds):
         dt += time.perf_counter() - t0
         reps += 1
     f = algorithmic_flops(ws.dims, vl)
-    return {"value": reps * f / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"{seqs} of {d.batch} sequences of the {w.name} shard, fp64 NumPy oracle "
-                      f"(LOCAL mode, fwd+bwd, {f / 1e9:.1f} GFLOP), run {reps}x"}
+    return {"value": reps * f / dt / 1e12, "unit": "TFLOP/s", "cores": info["threads"],
+            "kind": "oracle", "seconds": dt, "blas": info["blas"],
+            "physical_cores": _physical_cores(), "logical_cpus": os.cpu_count(),
+            "sample": f"{what} of the {w.name} shard ({ws.dims.tokens} tokens; same weights "
+                      f"and widths), fp64 NumPy oracle, LOCAL mode, fwd+bwd, "
+                      f"{f / 1e9:.1f} GFLOP, run {reps}x"}
+
+
+class SclkSampler:
+    """Samples the GPU's graphics clock (SCLK) from sysfs during a timed
+    region: the current level of pp_dpm_sclk of the device's PCI function,
+    read every few milliseconds on a host thread (no GPU call, no process)."""
+
+    def __init__(self, device_index=0, period_s=0.005):
+        self.path, self.err = self._find(device_index), None
+        self.period = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _find(idx):
+        import glob
+        import torch
+        try:
+            p = torch.cuda.get_device_properties(idx)
+            bdf = "%04x:%02x:%02x.0" % (int(getattr(p, "pci_domain_id")),
+                                        int(getattr(p, "pci_bus_id")),
+                                        int(getattr(p, "pci_device_id")))
+            cand = f"/sys/bus/pci/devices/{bdf}/pp_dpm_sclk"
+            if os.path.exists(cand):
+                return cand
+        except Exception:
+            pass
+        found = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        return found[0] if len(found) == 1 else None
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if "*" in line:
+                    tok = line.split(":", 1)[1].strip().split()[0].lower()
+                    return float(tok.replace("mhz", ""))
+        return None
+
+    def start(self):
+        import threading
+        if not self.path:
+            self.err = "no pp_dpm_sclk found for the device"
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    v = self._read()
+                    if v:
+                        self.samples.append(v)
+                except Exception as e:  # noqa: BLE001
+                    self.err = str(e)
+                    return
+                time.sleep(self.period)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+        if not self.samples:
+            return {"mhz_median": None, "samples": 0, "source": self.path,
+                    "note": self.err or "no samples"}
+        v = sorted(self.samples)
+        return {"mhz_median": v[len(v) // 2], "mhz_min": v[0], "mhz_max": v[-1],
+                "samples": len(v), "source": self.path}
 
 
 def source_digest(paths):
@@ -284,63 +397,60 @@ def bench_decode(args):
     sh.close()
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 30; 1000 for --mode decode)")
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt_1p2b_t1")
-    ap.add_argument("--cpu-seqs", type=int, default=0,
-                    help="sequences in the oracle sample (default: the whole micro-batch)")
-    ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--layout", choices=("tp", "sp"), default="tp",
-                    help="tp: TP_ALL forward + backward of one rank; sp: one rank's share of the "
-                         "sequence-parallel phases (its kernels only, exchanges excluded)")
-    ap.add_argument("--recompute", action="store_true",
-                    help="recompute the FC1 pre-activation in backward (TP_RECOMPUTE_FC1)")
-    ap.add_argument("--mode", choices=("train", "decode"), default="train",
-                    help="train: forward + backward (the headline); decode: one decode step")
-    ap.add_argument("--cache-len", type=int, default=0,
-                    help="decode: KV cache rows per sequence (default: the workload's seq)")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
-                    help="only run a plain copy of BYTES (counter calibration) and exit")
-    args = ap.parse_args()
-    if args.steps is None:
-        args.steps = 1000 if args.mode == "decode" else 30
-    if args.gpus != 1:
-        print(f"bench.py: this build runs one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU tensor parallelism is described in DESIGN.md, not launched.",
-              file=sys.stderr)
-        sys.exit(2)
+# The shard the headline is quoted on: the largest single-GPU configuration,
+# the 1T GPT's rank 0 of 8 (b 1, s 2048, h 25600, 160 heads, FFN 102400). The
+# other measured shards are reported beside it.
+DEFAULT_WORKLOAD = "gpt_1t_t8"
+OTHER_WORKLOADS = ("gpt_1p2b_t1", "gpt_8p3b_t8", "bert_3p9b_t4")
 
+
+def timed_steps(step, steps, warmup, sclk=None):
+    """Runs `warmup` untimed steps, then `steps` steps each bracketed by its
+    own pair of HIP events on the launch stream (no host sync in between).
+    Returns the per-step milliseconds, the whole bracket's milliseconds, the
+    wall seconds and the clock samples."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    if sclk:
+        sclk.start()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    clock = sclk.stop() if sclk else None
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return per, ev[0].elapsed_time(ev[steps]), wall, clock
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def make_train_step(w, sp=False, recompute=False, params=None):
+    """Uploads the workload and returns (step, shard, valid_len, cleanup)."""
     import torch
     from tensor_model_transformer_amd import binding as B
     from tensor_model_transformer_amd.shard import Shard, _check
-    from tensor_model_transformer_amd.synth import WORKLOADS, layer_inputs, rank_params
+    from tensor_model_transformer_amd.synth import layer_inputs, rank_params
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    if args.copy_probe:
-        copy_probe(args.copy_probe, 10)
-        return
-    if args.mode == "decode":
-        bench_decode(args)
-        return
-    w = WORKLOADS[args.workload]
     d = w.dims
-    params = rank_params(w)
+    if params is None:
+        params = rank_params(w)
     x, dout, vl = layer_inputs(w)
-    sp = args.layout == "sp"
-    sh = Shard(d, w.rank, recompute=B.TP_RECOMPUTE_FC1 if args.recompute else B.TP_RECOMPUTE_NONE,
+    sh = Shard(d, w.rank, recompute=B.TP_RECOMPUTE_FC1 if recompute else B.TP_RECOMPUTE_NONE,
                sequence_parallel=sp)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()
     grads = sh.zero_grads()
-    del params
 
     def step():
         _check("tp_layer_fwd", sh.fwd(p, out, x=xd))
@@ -378,28 +488,47 @@ def main():
                                      phase=B.TP_BWD_SP_ATTN))
             _check("sp bwd ln1", Bw(p, grads, da=red, x=x_r, dx=dx_r, phase=B.TP_BWD_SP_LN1))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end)
-    ms_per_step = ms / args.steps
+    def cleanup():
+        sh.close()
+
+    return step, sh, vl, cleanup
+
+
+def step_stats(per, flops):
+    med = _median(per)
+    return {"ms_per_step": med, "ms_min": min(per), "ms_max": max(per),
+            "ms_mean": sum(per) / len(per), "value": flops / (med * 1e-3) / 1e12,
+            "pct_of_peak": 100.0 * flops / (med * 1e-3) / 1e12 / PEAK["bf16"][0]}
+
+
+def bench_train(args):
+    import torch
+    from tensor_model_transformer_amd import binding as B
+    from tensor_model_transformer_amd.shard import _check
+    from tensor_model_transformer_amd.synth import WORKLOADS, rank_params
+
+    w = WORKLOADS[args.workload]
+    d = w.dims
+    sp = args.layout == "sp"
+    params = rank_params(w)
+    step, sh, vl, cleanup = make_train_step(w, sp, args.recompute, params)
     flops = algorithmic_flops(d, vl)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    print(f"[bench] {w.name}: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s "
-          f"(wall {wall:.2f} s for {args.steps} steps)", file=sys.stderr, flush=True)
+    sclk = None if args.no_sclk else SclkSampler()
+    per, bracket_ms, wall, clock = timed_steps(step, args.steps, args.warmup, sclk)
+    st = step_stats(per, flops)
+    value = st["value"]
+    ms_per_step = st["ms_per_step"]
+    print(f"[bench] {w.name}: median {ms_per_step:.3f} ms/step (min {st['ms_min']:.3f}, max "
+          f"{st['ms_max']:.3f}, bracket mean {bracket_ms / args.steps:.3f}), {value:.1f} TFLOP/s, "
+          f"SCLK {clock and clock.get('mhz_median')} MHz (wall {wall:.2f} s for {args.steps} "
+          "steps)", file=sys.stderr, flush=True)
 
     # Per-kernel-class event timing over the same number of steps. While
     # profiling, the library runs the backward on one stream (no overlap of
-    # the weight gradients), so each launch group is timed alone.
-    _check("tp_layer_profile", B.tp_layer_profile(sh.handle, 1))
+    # the weight gradients), so each launch group is timed alone. A padding
+    # mask's allowed pairs are handed over for the attention classes' FLOPs.
+    pairs = (d.seq * int(sum(int(v) for v in vl))) if d.mask == "padding" else 0
+    _check("tp_layer_profile", B.tp_layer_profile(sh.handle, 1, pairs))
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
@@ -420,7 +549,8 @@ def main():
         roof = {"kernel": dom, "bound": "mfma" if d.dtype == "bf16" else "alu",
                 "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                 "traffic": stored_traffic(dom, w.name),
-                "algorithmic_bytes_per_launch": bd["gbyte_per_step"] * 1e9 / bd["launches_per_step"]}
+                "algorithmic_bytes_per_launch": bd["gbyte_per_step"] * 1e9 / bd["launches_per_step"],
+                "algorithmic_flop_per_launch": bd["gflop_per_step"] * 1e9 / bd["launches_per_step"]}
     else:
         achieved = bd["gbyte_per_step"] / bd["ms_per_step"] * 1e3  # GB/s
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -430,29 +560,105 @@ def main():
     roof["launches_per_step"] = bd["launches_per_step"]
     roof["avg_launch_ms"] = bd["ms_per_step"] / bd["launches_per_step"]
     roof["timing"] = "HIP events on the launch stream, profiled pass with a serial backward"
+    ws_bytes = sh.ws_bytes
+    cleanup()
+    del step, sh
+    torch.cuda.empty_cache()
+
+    others = {}
+    if not args.no_other_workloads and args.workload == DEFAULT_WORKLOAD and not sp:
+        for name in OTHER_WORKLOADS:
+            ow = WORKLOADS[name]
+            ostep, osh, ovl, oclean = make_train_step(ow, False, args.recompute)
+            oper, _, _, _ = timed_steps(ostep, max(args.steps, 50), args.warmup)
+            ost = step_stats(oper, algorithmic_flops(ow.dims, ovl))
+            others[name] = {k: ost[k] for k in ("value", "pct_of_peak", "ms_per_step", "ms_min",
+                                                 "ms_max")}
+            others[name]["gflop_per_step"] = algorithmic_flops(ow.dims, ovl) / 1e9
+            print(f"[bench] {name}: median {ost['ms_per_step']:.3f} ms/step, "
+                  f"{ost['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            oclean()
+            del ostep, osh
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seqs, args.cpu_min_seconds)
+        cpu = cpu_baseline(w, args.cpu_tokens, args.cpu_min_seconds, params)
         print(f"[bench] cpu oracle: {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['cores']} threads "
-              f"({cpu['seconds']:.1f} s)", file=sys.stderr, flush=True)
+              f"({cpu['seconds']:.1f} s; {cpu['sample']})", file=sys.stderr, flush=True)
+    del params
 
-    peak = PEAK[d.dtype][0]
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": d.dtype, "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights)",
-        "pct_of_peak": 100.0 * value / peak,
+        "pct_of_peak": st["pct_of_peak"],
+        "timing": {"statistic": "median of per-step HIP event pairs", "ms_min": st["ms_min"],
+                   "ms_max": st["ms_max"], "ms_mean": st["ms_mean"],
+                   "ms_bracket_mean": bracket_ms / args.steps, "wall_s": wall,
+                   "sclk": clock},
+        "mfma_operands": "fp16" if d.dtype == "bf16" else None,
+        "accumulate": "fp32",
         "config": {"workload": w.name, "micro_batch": d.batch, "seq_len": d.seq,
                    "hidden": d.hidden, "heads": d.heads, "ffn": d.ffn, "t": d.t,
                    "rank": w.rank, "mask": d.mask, "gflop_per_step": flops / 1e9,
                    "recompute": "fc1" if args.recompute else "none", "layout": args.layout,
-                   "workspace_bytes": sh.ws_bytes},
+                   "workspace_bytes": ws_bytes},
         "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown,
+        "other_workloads": others or None,
     }
     print(json.dumps(line))
-    sh.close()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; 1000 for --mode decode)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-tokens", type=int, default=512,
+                    help="tokens in the oracle's sample (whole sequences, or the first positions "
+                         "of a single sequence)")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only --workload (by default the headline run also times the "
+                         "1.2B, 8.3B and BERT 3.9B shards)")
+    ap.add_argument("--no-sclk", action="store_true", help="do not sample the GPU clock")
+    ap.add_argument("--layout", choices=("tp", "sp"), default="tp",
+                    help="tp: TP_ALL forward + backward of one rank; sp: one rank's share of the "
+                         "sequence-parallel phases (its kernels only, exchanges excluded)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="recompute the FC1 pre-activation in backward (TP_RECOMPUTE_FC1)")
+    ap.add_argument("--mode", choices=("train", "decode"), default="train",
+                    help="train: forward + backward (the headline); decode: one decode step")
+    ap.add_argument("--cache-len", type=int, default=0,
+                    help="decode: KV cache rows per sequence (default: the workload's seq)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 1000 if args.mode == "decode" else 50
+    if args.gpus != 1:
+        print(f"bench.py: this build runs one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU tensor parallelism is described in DESIGN.md, not launched.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 10)
+        return
+    if args.mode == "decode":
+        bench_decode(args)
+        return
+    bench_train(args)
 
 
 if __name__ == "__main__":

@@ -94,7 +94,8 @@ enum {
   TP_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
   TP_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than required */
   TP_ERR_HIP = -6,          /* a HIP launch or runtime call failed */
-  TP_ERR_PHASE = -7         /* phase out of range */
+  TP_ERR_PHASE = -7,        /* phase out of range */
+  TP_ERR_NOMEM = -8         /* host memory for the handle could not be allocated */
 };
 
 enum { TP_DTYPE_F32 = 0, TP_DTYPE_BF16 = 1 };
@@ -251,7 +252,11 @@ typedef struct {
 
 /* Create a handle for rank `rank` of a t-way split of a layer with hidden
  * size `hidden`, `heads` attention heads, FFN size `ffn`, sequence length
- * `seq` and micro-batch `micro_batch`.
+ * `seq` and micro-batch `micro_batch`. These are the problem statement of
+ * "Megatron-LM: GPU-Cluster Training Parallelism", sections "Paper 1: The f/g
+ * Conjugate Operators" (t-way split of both blocks) and "Paper 1: QKV
+ * Column-Parallel Splitting in Detail" (whole heads per rank, so heads % t
+ * == 0; 3h/t QKV columns per rank).
  *   dtype: TP_DTYPE_F32 or TP_DTYPE_BF16. mask: TP_MASK_CAUSAL/TP_MASK_PADDING.
  *   opts: NULL for the defaults (eps 1e-5, exact-erf GeLU, fp32 dx, automatic
  *     score precision); opts->dx_dtype other than TP_DTYPE_F32 or `dtype`,
@@ -262,21 +267,41 @@ typedef struct {
  * (ffn/t) % 8 == 0; 0 <= rank < t; head dim in {32, 64, 96, 128, 160}
  * (TP_ERR_UNSUPPORTED otherwise). Allocates no device memory. On success
  * writes the handle to *out and the workspace size the fwd/bwd calls need to
- * *workspace_bytes; on failure sets *out = NULL. */
+ * *workspace_bytes; on failure sets *out = NULL (TP_ERR_NOMEM if the host
+ * allocation of the handle failed). Parameter gradients are always written
+ * in fp32 (there is no storage-dtype gradient option): they are what an
+ * optimizer accumulates over micro-batches before its step. */
 int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch,
                     int t, int rank, int dtype, int mask,
                     const tp_layer_opts *opts, tp_layer **out,
                     size_t *workspace_bytes);
 
-/* Enqueue a forward phase (TP_ALL, TP_FWD_ATTN or TP_FWD_MLP). */
+/* Enqueue a forward phase (TP_ALL, TP_FWD_ATTN or TP_FWD_MLP). The layer
+ * computed is the pre-LN block of "Megatron-LM: GPU-Cluster Training
+ * Parallelism", section "Paper 1: BERT LayerNorm Rearrangement", sharded as
+ * in section "Paper 1: The f/g Conjugate Operators", with the fusions of
+ * section "Fused Transformer Kernels" (bias + GeLU after FC1, bias + residual
+ * after the row-parallel GEMMs, scale-mask-softmax attention read in place).
+ * The phases end at the two g exchanges of the forward. */
 int tp_layer_fwd(tp_layer *L, int phase, const tp_fwd_io *io, void *hip_stream);
 
-/* Enqueue a backward phase (TP_ALL, TP_BWD_MLP, TP_BWD_ATTN or TP_BWD_LN1).
+/* Enqueue a backward phase (TP_ALL, TP_BWD_MLP, TP_BWD_ATTN or TP_BWD_LN1):
+ * the exact gradient of sum(out * dout) for the forward above; the phases end
+ * at the two f exchanges of the backward ("Megatron-LM: GPU-Cluster Training
+ * Parallelism", section "Paper 1: The f/g Conjugate Operators": f sums the
+ * input gradients of the column-parallel GEMMs, g is the identity).
  * Needs the workspace of the matching forward (TP_ALL after TP_ALL; the split
- * phases after both split forward phases), untouched since. */
+ * phases after both split forward phases), untouched since, and the backward
+ * phases run in order on it: TP_BWD_MLP (or TP_ALL) derives from dout the
+ * power of two S (max|S dout| in [1, 2); 1 for TP_DTYPE_F32) by which the
+ * fp16 gradient tensors kept inside the layer are scaled, and TP_BWD_ATTN
+ * reads it from the workspace. Every output is unscaled: the scaling only
+ * keeps bf16 gradients of any magnitude inside fp16's range (scaling dout by
+ * 2^k scales every gradient by exactly 2^k). */
 int tp_layer_bwd(tp_layer *L, int phase, const tp_bwd_io *io, void *hip_stream);
 
-/* Free the handle (host memory only). NULL is allowed. */
+/* Free the handle (host memory, the backward's side stream and events; no
+ * device memory is owned). NULL is allowed. */
 int tp_layer_destroy(tp_layer *L);
 
 /* Single-GPU stand-in for the f/g all-reduce: dst[i] = sum_p parts[p][i] for
@@ -368,13 +393,24 @@ int tp_layer_kv_fill(const tp_layer *L, const void *workspace, size_t workspace_
  *                                      backward; TP_ERR_UNSUPPORTED with
  *                                      TP_RECOMPUTE_FC1)
  *   TP_TAP_FC1_OUT  z      [n, f_l]    act
- *   TP_TAP_DQKV     dqkv   [n, 3*h_l]  act (after a backward)
+ *   TP_TAP_DQKV     S * dqkv [n, 3*h_l] act (after a backward; S as below)
  *   TP_TAP_DH       dh     [n, h]      fp32 (residual-stream grad, after TP_BWD_ATTN)
+ *   TP_TAP_GRAD_SCALE  S, 1/S          2 x fp32 (TP_DTYPE_BF16 only, after a
+ *                                      TP_ALL or TP_BWD_MLP backward): the power
+ *                                      of two the backward's fp16 gradient chain
+ *                                      is scaled by (see tp_layer_bwd);
+ *                                      TP_ERR_UNSUPPORTED for TP_DTYPE_F32,
+ *                                      where S = 1
+ *   TP_TAP_QKV_LO   qkv - fp16(qkv) [n, 3*h_l] fp16: the score residuals kept
+ *                                      with split scores (TP_SCORES_*);
+ *                                      TP_ERR_UNSUPPORTED when the handle forms
+ *                                      scores from qkv alone (this is how a
+ *                                      caller learns what TP_SCORES_AUTO chose)
  * Returns TP_ERR_ARG for an unknown id. */
 enum {
   TP_TAP_LN1_OUT = 0, TP_TAP_QKV = 1, TP_TAP_ATTN_OUT = 2, TP_TAP_LSE = 3,
   TP_TAP_H_MID = 4, TP_TAP_LN2_OUT = 5, TP_TAP_FC1_DGELU = 6, TP_TAP_FC1_OUT = 7,
-  TP_TAP_DQKV = 8, TP_TAP_DH = 9
+  TP_TAP_DQKV = 8, TP_TAP_DH = 9, TP_TAP_GRAD_SCALE = 10, TP_TAP_QKV_LO = 11
 };
 int tp_layer_tap(const tp_layer *L, int tap, size_t *offset, size_t *bytes);
 
@@ -398,7 +434,13 @@ enum {
   TP_K_CONVERT = 6,   /* bf16 -> fp16 copies of the weights and the upstream gradient */
   TP_K_COUNT = 7
 };
-int tp_layer_profile(tp_layer *L, int enable);
+/* attn_pairs: for a TP_MASK_PADDING handle, the number of allowed query-key
+ * pairs per forward of the inputs the profiled calls will see (the sum over
+ * sequences of seq * valid_len; the valid lengths are device data the library
+ * does not read back), used only for the attention classes' FLOP counts;
+ * 0 = unknown (those classes then report 0 FLOPs). Ignored for causal
+ * handles, whose pair count follows from seq and micro_batch. */
+int tp_layer_profile(tp_layer *L, int enable, double attn_pairs);
 
 /* Totals for one class since profiling was enabled: number of launch groups,
  * summed event time in milliseconds, summed algorithmic FLOPs and bytes.

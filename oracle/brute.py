@@ -45,9 +45,11 @@ def _vecmat(row, w, bias):
     return out
 
 
-def forward(params, x, heads, mask="causal", valid_len=None, eps=1e-5):
+def forward(params, x, heads, mask="causal", valid_len=None, eps=1e-5, want_lse=False):
     """params: dict of arrays/lists (rank slice or unsharded); x [b][s][h].
-    Returns out as nested lists [b][s][h]."""
+    Returns out as nested lists [b][s][h]; with want_lse also the natural-log
+    softmax normaliser of every attention row, lse[b][head][i] =
+    log(sum over allowed keys of exp(scaled score)), from the same loop."""
     p = {k: _tolist(v) for k, v in params.items()}
     x = _tolist(x)
     b = len(x)
@@ -59,8 +61,10 @@ def forward(params, x, heads, mask="causal", valid_len=None, eps=1e-5):
     valid_len = [int(v) for v in _tolist(valid_len)]
     scale = 1.0 / math.sqrt(dh)
     out = []
+    lse = []
     for bi in range(b):
         rows = x[bi]
+        lse_b = [[0.0] * s for _ in range(heads)]
         a = [_layernorm_row(r, p["ln1_gamma"], p["ln1_beta"], eps) for r in rows]
         qkv = [_vecmat(ar, p["w_qkv"], p["b_qkv"]) for ar in a]
         o = [[0.0] * hl for _ in range(s)]
@@ -80,6 +84,7 @@ def forward(params, x, heads, mask="causal", valid_len=None, eps=1e-5):
                 tot = 0.0
                 for v in ex:
                     tot += v
+                lse_b[j][i] = m + math.log(tot)
                 for e in range(dh):
                     acc = 0.0
                     for w_, kk in zip(ex, keys):
@@ -97,4 +102,5 @@ def forward(params, x, heads, mask="causal", valid_len=None, eps=1e-5):
             y = _vecmat(z, p["w_fc2"], p["b_fc2"])
             seq_out.append([h_mid[i][c] + y[c] for c in range(len(y))])
         out.append(seq_out)
-    return out
+        lse.append(lse_b)
+    return (out, lse) if want_lse else out

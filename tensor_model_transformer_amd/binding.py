@@ -23,8 +23,10 @@ TP_ERR_ALIGN = -4
 TP_ERR_WORKSPACE = -5
 TP_ERR_HIP = -6
 TP_ERR_PHASE = -7
+TP_ERR_NOMEM = -8
 ERROR_NAMES = {0: "TP_OK", -1: "TP_ERR_ARG", -2: "TP_ERR_SHAPE", -3: "TP_ERR_UNSUPPORTED",
-               -4: "TP_ERR_ALIGN", -5: "TP_ERR_WORKSPACE", -6: "TP_ERR_HIP", -7: "TP_ERR_PHASE"}
+               -4: "TP_ERR_ALIGN", -5: "TP_ERR_WORKSPACE", -6: "TP_ERR_HIP", -7: "TP_ERR_PHASE",
+               -8: "TP_ERR_NOMEM"}
 
 TP_DTYPE_F32, TP_DTYPE_BF16 = 0, 1
 TP_SCORES_AUTO, TP_SCORES_FP16, TP_SCORES_SPLIT = 0, 1, 2
@@ -36,7 +38,7 @@ TP_GELU_ERF, TP_GELU_TANH = 0, 1
 TP_ALL, TP_FWD_ATTN, TP_FWD_MLP = 0, 1, 2
 TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1 = 1, 2, 3
 TAPS = {"a": 0, "qkv": 1, "o": 2, "lse2": 3, "h_mid": 4, "c": 5, "dgelu": 6, "z": 7,
-        "dqkv": 8, "dh": 9}
+        "dqkv": 8, "dh": 9, "grad_scale": 10, "qkv_lo": 11}
 
 PARAM_FIELDS = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_o", "b_o",
                 "ln2_gamma", "ln2_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
@@ -105,7 +107,7 @@ def lib():
         L.tp_exchange_sum.restype = c_int
         L.tp_layer_tap.argtypes = [c_void_p, c_int, POINTER(c_size_t), POINTER(c_size_t)]
         L.tp_layer_tap.restype = c_int
-        L.tp_layer_profile.argtypes = [c_void_p, c_int]
+        L.tp_layer_profile.argtypes = [c_void_p, c_int, ctypes.c_double]
         L.tp_layer_profile.restype = c_int
         L.tp_layer_profile_read.argtypes = [c_void_p, c_int, POINTER(ctypes.c_long),
                                             POINTER(ctypes.c_double), POINTER(ctypes.c_double),
@@ -164,8 +166,8 @@ def tp_layer_tap(handle, tap):
     return rc, off.value, nb.value
 
 
-def tp_layer_profile(handle, enable):
-    return lib().tp_layer_profile(handle, int(enable))
+def tp_layer_profile(handle, enable, attn_pairs=0.0):
+    return lib().tp_layer_profile(handle, int(enable), float(attn_pairs))
 
 
 def tp_layer_profile_read(handle, kclass):

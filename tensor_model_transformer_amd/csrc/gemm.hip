@@ -29,6 +29,8 @@
 // tiles and bounds checks.
 //
 // fp32 path: a plain tiled FMA kernel (exact fp32 arithmetic).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,10 +39,15 @@ namespace tpl {
 // ----------------------------------------------------------------------------
 // Epilogue on 4 consecutive columns n..n+3 of row m (N % 4 == 0).
 // ----------------------------------------------------------------------------
-// bias4, when given, holds bias[n .. n+3], already loaded.
+// bias4, when given, holds bias[n .. n+3], already loaded; sc is *g.scale
+// (1 without one), loaded once by the caller.
 __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float v[4],
-                                          const float* bias4 = nullptr) {
+                                          const float* bias4, float sc) {
   if (m >= g.M || n >= g.N) return;
+  if (g.scale) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= sc;
+  }
   if (g.bias) {
     float b[4];
     if (bias4) {
@@ -277,6 +284,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
   static_assert(2 * (AE + BE) * 2 >= WM * WN * 32 * CP * 4, "epilogue slices fit in LDS");
   float* cs = reinterpret_cast<float*>(smem) + wid * 32 * CP;
   const int half = lane >> 5;
+  const float sc = g.scale ? g.scale[0] : 1.f;
   __syncthreads();  // every wave is done with the operand tiles
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmArgs g, int 
       float v[4] = {q.x, q.y, q.z, q.w};
       const int m = m0 + wm * WTM + i * 32 + r, n = n0 + wn * WTN + c;
       if (gridDim.y > 1) partial4(g, split_idx, m, n, v);
-      else epilogue4(g, m, n, v);
+      else epilogue4(g, m, n, v, nullptr, sc);
     }
   }
 }
@@ -378,8 +386,16 @@ constexpr int kGemmStages = 2;
 // this wave's loads of step j, a barrier publishes them (and ends every
 // wave's reads of step j-1), the loads of step j+1 go into step j-1's
 // stage, then the MFMAs of step j run.
+//
+// One call computes K steps [kt0, kt1) of the output tile at (m0, n0) and
+// writes either the epilogue's result (pdst == null, no split), a split-K
+// partial (split index split_idx, pdst == null, gridDim.y > 1) or the raw
+// [BM][BN] accumulator tile to pdst (a stream-K segment). The caller must
+// separate two calls on one workgroup with a barrier (the epilogue's LDS
+// slices overlap the operand stages).
 template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, int ktiles_per_split) {
+__device__ __forceinline__ void dtl_tile(const GemmArgs& g, int m0, int n0, int kt0, int kt1,
+                                         int split_idx, float* pdst, unsigned char* smem) {
   constexpr int BK = 64, NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -387,20 +403,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
   using OB = DtlOperand<BN, BK, NW, BKM>;
 
   constexpr int S = kGemmStages;
-  extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);  // [S][BM * BK]
   uint16_t* Bs = As + S * BM * BK;                   // [S][BN * BK]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / WN, wn = wid % WN;
-  int tm, tn;
-  tile_coords(g.M, g.N, BM, BN, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int split_idx = blockIdx.y;
-  const int ktiles = g.K / BK;
-  const int kt0 = split_idx * ktiles_per_split;
-  const int kt1 = min(ktiles, kt0 + ktiles_per_split);
   const int nk = kt1 - kt0;
 
   const int a_bytes = (int)((AK ? (long)g.M : (long)g.K) * g.lda * 2);
@@ -444,12 +452,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
   dtl_loop<S, OA::kPerWave + OB::kPerWave>(nk, issue, compute);
 
   // Epilogue through LDS slices (see gemm_f16_kernel).
-  const bool plain = gridDim.y == 1 && g.C && !g.accumulate;
+  const bool split = gridDim.y > 1;
+  const bool plain = !pdst && !split && g.C && !g.accumulate;
   const bool pre_r = plain && g.resid && g.epi == EPI_STORE;
   const bool pre_a = plain && !g.resid && g.epi == EPI_DGELU;
   constexpr int CP = WTN + 4;
   float* cs = reinterpret_cast<float*>(smem) + wid * 32 * CP;
   const int lrow = lane & 31, half = lane >> 5;
+  const float sc = g.scale ? g.scale[0] : 1.f;
   __syncthreads();  // every wave is done with the operand tiles
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -461,6 +471,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
             make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
                         acc[i][j][4 * jj + 3]);
     constexpr int LPR = WTN / 4, RPI = 64 / LPR, NIT = 32 / RPI;
+    if (pdst) {
+      // stream-K segment: the raw accumulators, tile-local [BM][BN] rows
+      const int c = 4 * (lane % LPR);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int r = lane / LPR + it * RPI;
+        const float4 q = *reinterpret_cast<const float4*>(cs + r * CP + c);
+        *reinterpret_cast<float4*>(pdst + (size_t)(wm * WTM + i * 32 + r) * BN + wn * WTN + c) = q;
+      }
+      continue;
+    }
     if (pre_r || pre_a) {
       // Plain store with a residual, or the product with the kept GeLU':
       // that operand (and the bias) for all NIT rows of this lane is loaded
@@ -483,6 +504,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
         const int m = mr + it * RPI;
         const float4 q = *reinterpret_cast<const float4*>(cs + (lane / LPR + it * RPI) * CP + c);
         float v[4] = {q.x, q.y, q.z, q.w};
+        if (g.scale) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= sc;
+        }
         if (g.bias) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] += bs[e];
@@ -496,15 +521,106 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
     // a lane's columns, hence its bias values, are the same in every row
     const int c = 4 * (lane % LPR), n = n0 + wn * WTN + c;
     float bs[4] = {0.f, 0.f, 0.f, 0.f};
-    if (g.bias && gridDim.y == 1 && n < g.N) load4_dt(g.bias, g.bias_dtype, n, bs);
+    if (g.bias && !split && n < g.N) load4_dt(g.bias, g.bias_dtype, n, bs);
 #pragma unroll 1
     for (int r = lane / LPR; r < 32; r += RPI) {
       const float4 q = *reinterpret_cast<const float4*>(cs + r * CP + c);
       float v[4] = {q.x, q.y, q.z, q.w};
       const int m = m0 + wm * WTM + i * 32 + r;
-      if (gridDim.y > 1) partial4(g, split_idx, m, n, v);
-      else epilogue4(g, m, n, v, bs);
+      if (split) partial4(g, split_idx, m, n, v);
+      else epilogue4(g, m, n, v, bs, sc);
     }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, int ktiles_per_split) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int tm, tn;
+  tile_coords(g.M, g.N, BM, BN, &tm, &tn);
+  const int split_idx = blockIdx.y;
+  const int ktiles = g.K / 64;
+  const int kt0 = split_idx * ktiles_per_split;
+  const int kt1 = min(ktiles, kt0 + ktiles_per_split);
+  dtl_tile<BM, BN, WM, WN, AK, BKM>(g, tm * BM, tn * BN, kt0, kt1, split_idx, nullptr, smem);
+}
+
+// ----------------------------------------------------------------------------
+// Stream-K schedule for GEMMs whose tile grid leaves the last round of
+// workgroups part empty (the 1T shard's M = 2048 GEMMs: 400 or 800 tiles on
+// 256 compute units). The work, a column of U = ceil(M / BM) output tiles
+// times kI K steps per tile column, is split evenly over S = 256 / U slots:
+// slot j takes the column K steps [j T / S, (j+1) T / S) of the
+// column-major order (T = columns * kI). The U workgroups of a slot compute
+// the U row tiles of the same column over the same K steps at the same time,
+// and sit on one XCD (workgroup w runs on XCD w mod 8), so each K step of
+// the column's B panel is fetched into that XCD's L2 once and read by all U.
+// A column a slot covers whole gets its epilogue at once; a column split
+// between slots has each piece's raw accumulators stored in the partial
+// buffer ([S][2][U][BM][BN]: a slot's first and last columns) and
+// gemm_sk_fixup_kernel sums the pieces in slot order (deterministic) and
+// applies the epilogue. No workgroup waits for another.
+// ----------------------------------------------------------------------------
+struct SkPlan {
+  int U, S, cols, kI;
+  long T;
+};
+
+__device__ __forceinline__ long sk_begin(const SkPlan& p, int slot) {
+  return (long)slot * p.T / p.S;
+}
+
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_sk_kernel(GemmArgs g, SkPlan p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int xcd = blockIdx.x % kXCDs, local = blockIdx.x / kXCDs;
+  const int per_xcd = p.S / kXCDs;  // slots per XCD (p.S = 256 / U, U divides 32)
+  const int slot = xcd * per_xcd + local / p.U, r = local % p.U;
+  const long s0 = sk_begin(p, slot), s1 = sk_begin(p, slot + 1);
+  if (s0 >= s1) return;
+  const int c_first = (int)(s0 / p.kI), c_last = (int)((s1 - 1) / p.kI);
+  for (int c = c_first; c <= c_last; ++c) {
+    const long cb = (long)c * p.kI;
+    const int k0 = (int)(max(s0, cb) - cb), k1 = (int)(min(s1, cb + p.kI) - cb);
+    float* pdst = nullptr;
+    if (k1 - k0 < p.kI) {
+      const int which = c == c_first ? 0 : 1;
+      pdst = g.ws + ((size_t)(slot * 2 + which) * p.U + r) * (size_t)(BM * BN);
+    }
+    if (c != c_first) __syncthreads();  // the last epilogue's LDS reads are done
+    dtl_tile<BM, BN, WM, WN, AK, BKM>(g, r * BM, c * BN, k0, k1, 0, pdst, smem);
+  }
+}
+
+// Columns split between slots, and their slot range (host-computed).
+constexpr int kSkMaxSplitCols = 64;
+struct SkFix {
+  int n;
+  int col[kSkMaxSplitCols], j0[kSkMaxSplitCols], j1[kSkMaxSplitCols];
+};
+
+// Sums the pieces of each split column in slot order and applies the
+// epilogue. Workgroup (q, r, chunk): rows [chunk*32, chunk*32+32) of row tile
+// r of split column q; a thread handles 4 consecutive columns of a row.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_sk_fixup_kernel(GemmArgs g, SkPlan p, SkFix f) {
+  constexpr int RCH = BM / 32;
+  const int q = blockIdx.x / (p.U * RCH);
+  const int r = (blockIdx.x / RCH) % p.U, chunk = blockIdx.x % RCH;
+  const int c = f.col[q];
+  const float sc = g.scale ? g.scale[0] : 1.f;
+  constexpr int LPR = BN / 4;  // threads per tile row
+  for (int e = threadIdx.x; e < 32 * LPR; e += 256) {
+    const int rr = chunk * 32 + e / LPR, cc = 4 * (e % LPR);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = f.j0[q]; j <= f.j1[q]; ++j) {
+      if (sk_begin(p, j) == sk_begin(p, j + 1)) continue;  // an empty slot wrote nothing
+      const int which = (int)(sk_begin(p, j) / p.kI) == c ? 0 : 1;
+      const float4 v = *reinterpret_cast<const float4*>(
+          g.ws + ((size_t)(j * 2 + which) * p.U + r) * (size_t)(BM * BN) + (size_t)rr * BN + cc);
+      acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+    }
+    epilogue4(g, r * BM + rr, c * BN + cc, acc, nullptr, sc);
   }
 }
 
@@ -560,11 +676,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, int ktiles_pe
     }
     __syncthreads();
   }
+  const float sc = g.scale ? g.scale[0] : 1.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
     if (gridDim.y > 1) partial4(g, blockIdx.y, m0 + ty * 4 + i, n0 + tx * 4, v);
-    else epilogue4(g, m0 + ty * 4 + i, n0 + tx * 4, v);
+    else epilogue4(g, m0 + ty * 4 + i, n0 + tx * 4, v, nullptr, sc);
   }
 }
 
@@ -590,6 +707,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += x[u][e];
   }
+  if (g.scale) {
+    const float sc = g.scale[0];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= sc;
+  }
   float* c = (float*)g.C + (size_t)m * g.ldc + n;
   if (g.accumulate) {
     Vec4<float>::load(c, v);
@@ -611,6 +733,12 @@ static constexpr TileCfg kBig = {256, 256, 1, 1.0};
 static constexpr TileCfg kWide = {256, 192, 1, 0.95};
 static constexpr TileCfg kSmall = {128, 128, 2, 0.8};
 static constexpr int kCUs = 256;
+// Time model constants: MACs per second of one CU inside a full round of the
+// 256x256 kernel (about half the CU's dense fp16 MFMA rate, measured on the
+// 1T shard's long-K GEMMs), and the HBM rate of the partial-sum traffic.
+static constexpr double kMacPerCU = 2.4e12;
+static constexpr double kPartialBW = 5.0e12;
+static constexpr double kLaunch = 5e-6;  // one more launch and pipeline fills
 
 static long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
@@ -634,50 +762,135 @@ static TileCfg choose_tile(int M, int N, int split) {
   return best;
 }
 
-// Split-K factor of a weight-gradient GEMM (few output tiles, long K). When
-// some tile shape and split fill one round of the CUs to at least 70 %, the
-// fullest such single round wins (fewest splits on ties): measured on the
-// layer's weight gradients, one full round beats several rounds plus the
-// partial-sum traffic of a larger split. Otherwise the split that best fills
-// whole rounds of 256x256 tiles.
+// Estimated seconds of a GEMM on tile t with a split-K factor s: rounds of
+// resident workgroups times one workgroup's MACs, plus (s > 1) the fp32
+// partials written by the main kernel and read by the reduce, and the reduce's
+// output (read too when accumulating).
+static double split_cost(const TileCfg& t, const GemmArgs& g, int s) {
+  const long ktiles = ceil_div(g.K, 64);
+  const long per = ceil_div(ktiles, s), real = ceil_div(ktiles, per);
+  const long wgs = ceil_div(g.M, t.bm) * ceil_div(g.N, t.bn) * real;
+  const long rounds = ceil_div(wgs, (long)kCUs * t.per_cu);
+  double sec = (double)rounds * t.per_cu * t.bm * t.bn * (double)(per * 64) / t.eff / kMacPerCU;
+  if (real > 1)
+    sec += (2.0 * real + 1 + (g.accumulate ? 1 : 0)) * (double)g.M * g.N * 4 / kPartialBW + kLaunch;
+  return sec;
+}
+
+// Split-K factor of a weight-gradient GEMM (few output tiles, long K): the
+// factor with the lowest modelled time over the tile shapes, where a split
+// costs its fp32 partial traffic (so a split that only rounds up the last
+// round of a many-round grid is not taken).
 int gemm_choose_split(const GemmArgs& g) {
   if (g.math != DT_F16) return 1;
   if (g.epi != EPI_STORE || g.bias || g.resid || g.c_dtype != DT_F32) return 1;
   const long ktiles = ceil_div(g.K, 64);
-  double best_fill = 0.0;
-  int one_round = 0;
-  for (const TileCfg& t : {kBig, kWide}) {
-    const long tiles = ceil_div(g.M, t.bm) * ceil_div(g.N, t.bn);
-    for (int s = 1; s <= 16; ++s) {
-      if (s > 1 && ktiles / s < 8) break;  // keep >= 8 K-tiles per split
-      const long w = tiles * s;
-      if (w > kCUs) break;
-      const double fill = (double)w / kCUs;
-      if (fill > best_fill + 1e-9) {
-        best_fill = fill;
-        one_round = s;
+  int best = 1;
+  double bc = 1e30;
+  for (int s = 1; s <= 16; ++s) {
+    if (s > 1 && ktiles / s < 8) break;  // keep >= 8 K-tiles per split
+    for (const TileCfg& t : {kBig, kWide, kSmall}) {
+      const double c = split_cost(t, g, s);
+      if (c < bc * 0.98) {  // a split must win by more than the model's noise
+        bc = c;
+        best = s;
       }
     }
-  }
-  if (best_fill >= 0.7) return one_round;
-  const long tiles = ceil_div(g.M, kBig.bm) * ceil_div(g.N, kBig.bn);
-  int best = 1;
-  double best_util = 0.0;
-  for (int s = 1; s <= 16; ++s) {
-    if (ktiles / s < 8) break;
-    const long w = tiles * s;
-    const double util = (double)w / (double)(kCUs * ceil_div(w, kCUs));
-    if (util > best_util + 0.05) {
-      best_util = util;
-      best = s;
-    }
-    if (util >= 0.85) break;
   }
   return best;
 }
 
+// ---- stream-K planning --------------------------------------------------------
+// Rows of tiles per slot and slots: U must divide the 32 CUs of an XCD.
+static bool sk_shape(const GemmArgs& g, const TileCfg& t, SkPlan* p) {
+  const long U = ceil_div(g.M, t.bm);
+  if (t.per_cu != 1 || U > 32 || (32 % U) != 0) return false;
+  p->U = (int)U;
+  p->S = kCUs / (int)U;
+  p->cols = (int)ceil_div(g.N, t.bn);
+  p->kI = g.K / 64;
+  p->T = (long)p->cols * p->kI;
+  return true;
+}
+
+// The slot whose K-step range holds column K step i: the largest j with
+// j T / S <= i (empty slots, possible only when T < S, are skipped this way).
+static int sk_slot_of(const SkPlan& p, long i) {
+  return (int)(((i + 1) * p.S + p.T - 1) / p.T) - 1;
+}
+
+// The split columns and, for each, the first and last slot covering it.
+static void sk_fix(const SkPlan& p, SkFix* f) {
+  f->n = 0;
+  for (int j = 1; j < p.S; ++j) {
+    const long b = (long)j * p.T / p.S;  // slot j starts here
+    if (b % p.kI == 0 || b >= p.T) continue;  // on a column edge: nothing split there
+    const int c = (int)(b / p.kI);
+    if (f->n && f->col[f->n - 1] == c) continue;
+    if (f->n == kSkMaxSplitCols) {  // too many to list: the caller rejects the plan
+      f->n = kSkMaxSplitCols + 1;
+      return;
+    }
+    f->col[f->n] = c;
+    f->j0[f->n] = sk_slot_of(p, (long)c * p.kI);
+    f->j1[f->n] = sk_slot_of(p, (long)(c + 1) * p.kI - 1);
+    ++f->n;
+  }
+}
+
+static double sk_cost(const TileCfg& t, const SkPlan& p) {
+  const long iters = ceil_div(p.T, p.S);
+  const double mac = (double)iters * t.bm * t.bn * 64 / t.eff;
+  // at most two pieces per slot and row tile, written then read
+  const double part = 2.0 * 2.0 * p.S * p.U * (double)t.bm * t.bn * 4;
+  return mac / kMacPerCU + part / kPartialBW + kLaunch;
+}
+
+// Whether g runs stream-K (and on which tile): K a whole number of long
+// enough K steps, no split-K, a partial buffer, and a modelled time at
+// least 3 % below the best data-parallel grid's.
+static bool sk_choose(const GemmArgs& g, TileCfg* tile, SkPlan* plan, bool need_ws) {
+  if (g.math != DT_F16 || g.split > 1 || g.K % 64 || g.K / 64 < 128) return false;
+  if (need_ws && !g.ws) return false;
+  const TileCfg dp = choose_tile(g.M, g.N, 1);
+  const double dp_cost = tile_cost(dp, g.M, g.N, 1) * (double)g.K / kMacPerCU;
+  bool found = false;
+  double best = dp_cost * 0.97;
+  for (const TileCfg& t : {kBig, kWide}) {
+    SkPlan p;
+    if (!sk_shape(g, t, &p)) continue;
+    const size_t need = (size_t)p.S * 2 * p.U * t.bm * t.bn;
+    if (need_ws && need > g.ws_floats) continue;
+    SkFix f;
+    sk_fix(p, &f);
+    if (f.n > kSkMaxSplitCols) continue;
+    const double c = sk_cost(t, p);
+    if (c < best) {
+      best = c;
+      *tile = t;
+      *plan = p;
+      found = true;
+    }
+  }
+  return found;
+}
+
+size_t gemm_ws_floats(const GemmArgs& g) {
+  size_t need = 0;
+  const int split = g.split < 1 ? 1 : g.split;
+  if (split > 1 && g.math == DT_F16) {
+    const long ktiles = ceil_div(g.K, 64), per = ceil_div(ktiles, split);
+    need = (size_t)ceil_div(ktiles, per) * g.M * g.N;
+  }
+  TileCfg t;
+  SkPlan p;
+  if (sk_choose(g, &t, &p, false)) need = std::max(need, (size_t)p.S * 2 * p.U * t.bm * t.bn);
+  return need;
+}
+
 template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
-static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
+static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s,
+                             const SkPlan* sk = nullptr) {
   constexpr int BK = 64;
   constexpr int NT = WM * WN * 64;
   const int ktiles = (int)ceil_div(g.K, BK);
@@ -693,6 +906,7 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
       g.K % BK == 0 &&
       ((size_t)(g.a_kmajor ? g.M + BM : g.K) * g.lda + BM) * 2 < (1u << 31) &&
       ((size_t)(g.b_kmajor ? g.N + BN : g.K) * g.ldb + BN) * 2 < (1u << 31);
+  if (sk && !direct) return hipErrorInvalidValue;
   const size_t slices = (size_t)WM * WN * 32 * (BN / WN + 4) * sizeof(float);
   const size_t lds_pad = (size_t)2 *
                          (TilePitch<BM, BK, AK>::kElems + TilePitch<BN, BK, BKM>::kElems) *
@@ -700,6 +914,26 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
   const size_t lds_ops = (size_t)kGemmStages * (BM + BN) * BK * sizeof(uint16_t);
   const size_t lds_dtl = lds_ops > slices ? lds_ops : slices;
   const size_t lds = direct ? lds_dtl : lds_pad;
+  if (sk) {
+    auto kern = gemm_f16_sk_kernel<BM, BN, WM, WN, AK, BKM>;
+    static bool sk_attr = false;
+    if (!sk_attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      sk_attr = true;
+    }
+    SkFix f;
+    sk_fix(*sk, &f);
+    GemmArgs a = g;
+    a.split = 1;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(sk->S * sk->U)), dim3(NT), lds, s, a, *sk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || f.n == 0) return e;
+    hipLaunchKernelGGL((gemm_sk_fixup_kernel<BM, BN>), dim3((unsigned)(f.n * sk->U * (BM / 32))),
+                       dim3(256), 0, s, a, *sk, f);
+    return hipGetLastError();
+  }
   auto kern = direct ? gemm_f16_dtl_kernel<BM, BN, WM, WN, AK, BKM>
                        : gemm_f16_kernel<BM, BN, BK, WM, WN, AK, BKM>;
   static bool attr_set[2] = {false, false};  // per instantiation
@@ -722,6 +956,12 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s) {
 
 template <bool AK, bool BKM>
 static hipError_t dispatch_f16(const GemmArgs& g, int split, hipStream_t s) {
+  TileCfg skt;
+  SkPlan plan;
+  if (split == 1 && sk_choose(g, &skt, &plan, true)) {
+    if (skt.bn == 256) return launch_f16<256, 256, 4, 4, AK, BKM>(g, 1, s, &plan);
+    return launch_f16<256, 192, 4, 3, AK, BKM>(g, 1, s, &plan);
+  }
   const TileCfg t = choose_tile(g.M, g.N, split);
   if (t.bm == 256 && t.bn == 256) return launch_f16<256, 256, 4, 4, AK, BKM>(g, split, s);
   if (t.bm == 256) return launch_f16<256, 192, 4, 3, AK, BKM>(g, split, s);
@@ -750,6 +990,11 @@ hipError_t gemm(const GemmArgs& g, hipStream_t s) {
   int split = g.split < 1 ? 1 : g.split;
   if (split > 1 && (!g.ws || g.epi != EPI_STORE || g.bias || g.resid || g.c_dtype != DT_F32))
     return hipErrorInvalidValue;
+  if (split > 1 && g.math == DT_F16) {  // the partials must fit the scratch given
+    GemmArgs q = g;
+    q.split = split;
+    if (gemm_ws_floats(q) > g.ws_floats) return hipErrorInvalidValue;
+  }
   if (g.math == DT_F16) {
     if (g.a_dtype != DT_F16 || g.b_dtype != DT_F16) return hipErrorInvalidValue;
     // 16-byte operand chunks: the contiguous dimension must be a multiple of 8

@@ -26,14 +26,15 @@ hipError_t ln_fwd(int x_dtype, int p_dtype, int y_dtype, const void* x, const vo
 // LayerNorm backward plus the residual-gradient add:
 //   dx = rstd * (g - mean(g) - xhat * mean(g * xhat)) + dres,  g = dy * gamma
 // dy fp32; x is `x_dtype`; dres is `dres_dtype`; gamma is `p_dtype`.
-// Writes dx as fp32 (dx_f32, optional) and/or `st_dtype` (dx_st, optional).
+// Writes dx as fp32 (dx_f32, optional) and/or `st_dtype` (dx_st, optional);
+// st_scale (optional, device fp32) multiplies the dx_st copy only.
 // Column partial sums over row blocks go to part [nblk][3][h]:
 //   0: sum dy*xhat (dgamma), 1: sum dy (dbeta), 2: sum dx (if want_dsum).
 hipError_t ln_bwd(int p_dtype, const float* dy, int x_dtype, const void* x,
                   const float* mean, const float* rstd, const void* gamma,
                   int dres_dtype, const void* dres, float* dx_f32, int st_dtype, void* dx_st,
-                  float* part, int rows_per_blk, int rows, int h, int want_dsum,
-                  hipStream_t s);
+                  const float* st_scale, float* part, int rows_per_blk, int rows, int h,
+                  int want_dsum, hipStream_t s);
 int ln_bwd_blocks(int rows, int h, int* rows_per_blk);
 
 // Column partial sums of a [rows, cols] matrix (leading dim ld) over row
@@ -48,17 +49,22 @@ hipError_t residual_add(const float* a, int bias_dtype, const void* bias, int r_
                         const void* r, int out_dtype, void* out, int rows, int h,
                         hipStream_t s);
 
-// out_k[j] (+)= sum_b part[b][k][j] for k < nout (part is [nblk][nout][width]).
-// The buffer must hold reduce_scratch_floats(nblk, nout, width) floats: the
-// block partials followed by room for the group partials of stage 1.
+// out_k[j] (+)= scale * sum_b part[b][k][j] for k < nout (part is
+// [nblk][nout][width]; scale: optional device fp32, 1 when null). The buffer
+// must hold reduce_scratch_floats(nblk, nout, width) floats: the block
+// partials followed by room for the group partials of stage 1.
 hipError_t reduce_partials(const float* part, int nblk, int nout, int width,
                            float* out0, float* out1, float* out2, int accumulate,
-                           hipStream_t s);
+                           hipStream_t s, const float* scale = nullptr);
 size_t reduce_scratch_floats(int nblk, int nout, int width);
 
 // dst[k][i] = fp16(src[k][i]) for bf16 src, i < count[k], k < nseg (1..4).
+// With amax_part (kAmaxFloats floats of scratch) and scale_out (2 floats),
+// nseg must be 1 and dst = fp16(S * src) with the power of two S that puts
+// max|S src| in [1, 2); scale_out receives S and 1/S (device fp32).
+constexpr int kAmaxFloats = 256;
 hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
-                  hipStream_t s);
+                  hipStream_t s, float* amax_part = nullptr, float* scale_out = nullptr);
 
 // dst[i] = sum_p parts[p][i]  (fp32 sum in order), written as dst_dtype.
 hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts,
@@ -93,11 +99,23 @@ struct GemmArgs {
   int gelu_tanh;
   int accumulate;
   int split;                           // split-K factor (>= 1)
-  float* ws;                           // split*M*N fp32 when split > 1
+  // fp32 scratch of ws_floats floats: split-K partials (split > 1), or the
+  // stream-K pieces of a GEMM the launcher schedules that way (gemm_ws_floats
+  // tells how much either needs; without enough the launcher does not use
+  // stream-K). Null: neither.
+  float* ws;
+  size_t ws_floats;
+  // optional device fp32 factor applied to the accumulator first (v = scale *
+  // acc, before bias and residual): undoes the power-of-two scaling of the
+  // backward's fp16 gradient chain in the GEMMs that leave it
+  const float* scale;
 };
 hipError_t gemm(const GemmArgs& g, hipStream_t s);
-// Split-K factor and workspace floats the launcher will use for g.
+// Split-K factor the launcher would pick for a weight-gradient GEMM g.
 int gemm_choose_split(const GemmArgs& g);
+// Scratch floats g needs (split-K partials for g.split > 1, stream-K pieces
+// when its shape is scheduled that way); 0 for neither.
+size_t gemm_ws_floats(const GemmArgs& g);
 
 // ---------------------------------------------------------------------------
 // Attention (attn.hip). qkv: [batch*seq, 3*Hl*D] head-interleaved;

@@ -143,22 +143,37 @@ hipError_t ln_fwd(int x_dtype, int p_dtype, int y_dtype, const void* x, const vo
 // rows; each thread owns the same columns in every row and accumulates the
 // column sums (dgamma, dbeta, dx) for them, written once per block.
 // ----------------------------------------------------------------------------
-template <typename T, typename Tx, typename Tr, typename Ts, int NT, int NV>
+template <typename T, typename Tx, typename Tr, typename Ts, int NT, int NV, bool DSUM>
 __global__ __launch_bounds__(NT) void ln_bwd_kernel(
     const float* __restrict__ dy, const Tx* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const T* __restrict__ gamma, const Tr* __restrict__ dres,
-    float* __restrict__ dx_f32, Ts* __restrict__ dx_st, float* __restrict__ part,
-    int rows_per_blk, int rows, int h, int want_dsum) {
+    float* __restrict__ dx_f32, Ts* __restrict__ dx_st, const float* __restrict__ st_scale,
+    float* __restrict__ part, int rows_per_blk, int rows, int h) {
   __shared__ float red[32];
   const int tid = threadIdx.x;
+  // power-of-two factor of the storage-dtype copy (exact; 1 when not given)
+  const float sts = st_scale ? st_scale[0] : 1.f;
   const int nvec = h >> 3;
   const int r0 = blockIdx.x * rows_per_blk;
   const int r1 = min(rows, r0 + rows_per_blk);
-  float dg[NV][8], db[NV][8], ds[NV][8];
+  // Column sums over the block's rows: dgamma, dbeta and (DSUM) dx. Rows of
+  // 1024 threads keep the dx sums in LDS, each thread its own entries (no
+  // barrier needed), so the other two fit the registers.
+  constexpr bool kLdsSum = DSUM && NT > 512;
+  __shared__ float4 dsl[kLdsSum ? 2 * NV * NT : 1];
+  float dg[NV][8], db[NV][8], ds[(DSUM && !kLdsSum) ? NV : 1][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dg[i][e] = db[i][e] = ds[i][e] = 0.f;
+    for (int e = 0; e < 8; ++e) dg[i][e] = db[i][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < ((DSUM && !kLdsSum) ? NV : 1); ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ds[i][e] = 0.f;
+  if constexpr (kLdsSum) {
+#pragma unroll
+    for (int i = 0; i < 2 * NV; ++i) dsl[i * NT + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 
   // Rows of up to 512 threads: row r + 1's inputs (with its mean and rstd)
   // are fetched while row r is reduced and written, and gamma is loaded once.
@@ -226,17 +241,26 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           o[e] = rs * (gy[i][e] - mg - xh[i][e] * mgx) + rv[i][e];
-          ds[i][e] += o[e];
+          if constexpr (DSUM) ds[i][e] += o[e];
         }
         if (dx_f32) Vec8<float>::store(dx_f32 + (size_t)row * h + 8 * j, o);
-        if (dx_st) Vec8<Ts>::store(dx_st + (size_t)row * h + 8 * j, o);
+        if (dx_st) {
+          float q[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = o[e] * sts;
+          Vec8<Ts>::store(dx_st + (size_t)row * h + 8 * j, q);
+        }
       }
     }
   }
   } else {
+  // Rows of 1024 threads (hidden above 16384): the column sums of up to 4
+  // vectors per thread take 96 registers, which leaves no room to keep the
+  // row between its reduction and its output (the first version did and
+  // spilled). The row is read once for the two row sums and again, from
+  // L2 or the last-level cache, for the output.
   for (int row = r0; row < r1; ++row) {
     const float mu = mean[row], rs = rstd[row];
-    float gy[NV][8], xh[NV][8];
     float sums[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -248,11 +272,10 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
         Vec8<T>::load(gamma + 8 * j, g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          xh[i][e] = (xv[e] - mu) * rs;
-          gy[i][e] = d[e] * g[e];
-          sums[0] += gy[i][e];
-          sums[1] += gy[i][e] * xh[i][e];
-          dg[i][e] += d[e] * xh[i][e];
+          const float xh = (xv[e] - mu) * rs, gy = d[e] * g[e];
+          sums[0] += gy;
+          sums[1] += gy * xh;
+          dg[i][e] += d[e] * xh;
           db[i][e] += d[e];
         }
       }
@@ -263,15 +286,31 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
     for (int i = 0; i < NV; ++i) {
       const int j = tid + i * NT;
       if (j < nvec) {
-        float r[8], o[8];
+        float d[8], xv[8], g[8], r[8], o[8];
+        Vec8<float>::load(dy + (size_t)row * h + 8 * j, d);
+        Vec8<Tx>::load(x + (size_t)row * h + 8 * j, xv);
+        Vec8<T>::load(gamma + 8 * j, g);
         Vec8<Tr>::load(dres + (size_t)row * h + 8 * j, r);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          o[e] = rs * (gy[i][e] - mg - xh[i][e] * mgx) + r[e];
-          ds[i][e] += o[e];
+          const float xh = (xv[e] - mu) * rs;
+          o[e] = rs * (d[e] * g[e] - mg - xh * mgx) + r[e];
+          if constexpr (DSUM && !kLdsSum) ds[i][e] += o[e];
+        }
+        if constexpr (kLdsSum) {
+          float4 a = dsl[(2 * i) * NT + tid], b = dsl[(2 * i + 1) * NT + tid];
+          a.x += o[0]; a.y += o[1]; a.z += o[2]; a.w += o[3];
+          b.x += o[4]; b.y += o[5]; b.z += o[6]; b.w += o[7];
+          dsl[(2 * i) * NT + tid] = a;
+          dsl[(2 * i + 1) * NT + tid] = b;
         }
         if (dx_f32) Vec8<float>::store(dx_f32 + (size_t)row * h + 8 * j, o);
-        if (dx_st) Vec8<Ts>::store(dx_st + (size_t)row * h + 8 * j, o);
+        if (dx_st) {
+          float q[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = o[e] * sts;
+          Vec8<Ts>::store(dx_st + (size_t)row * h + 8 * j, q);
+        }
       }
     }
   }
@@ -284,7 +323,13 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
     if (j < nvec) {
       Vec8<float>::store(pb + 8 * j, dg[i]);
       Vec8<float>::store(pb + h + 8 * j, db[i]);
-      if (want_dsum) Vec8<float>::store(pb + 2 * h + 8 * j, ds[i]);
+      if constexpr (kLdsSum) {
+        const float4 a = dsl[(2 * i) * NT + tid], b = dsl[(2 * i + 1) * NT + tid];
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        Vec8<float>::store(pb + 2 * h + 8 * j, v);
+      } else if constexpr (DSUM) {
+        Vec8<float>::store(pb + 2 * h + 8 * j, ds[i]);
+      }
     }
   }
 }
@@ -299,17 +344,22 @@ int ln_bwd_blocks(int rows, int h, int* rows_per_blk) {
 template <typename T, typename Tx, typename Tr, typename Ts>
 static hipError_t ln_bwd_t(const float* dy, const void* x, const float* mean,
                            const float* rstd, const void* gamma, const void* dres,
-                           float* dx_f32, void* dx_st, float* part, int rows_per_blk,
-                           int rows, int h, int want_dsum, hipStream_t s) {
+                           float* dx_f32, void* dx_st, const float* st_scale, float* part,
+                           int rows_per_blk, int rows, int h, int want_dsum, hipStream_t s) {
   int nt, nv;
   if (!row_config(h, &nt, &nv)) return hipErrorInvalidValue;
   const int nblk = (rows + rows_per_blk - 1) / rows_per_blk;
   if (nblk == 0) return hipSuccess;
 #define TPL_LNB(NT_, NV_)                                                                  \
   if (nt == NT_ && nv == NV_) {                                                            \
-    ln_bwd_kernel<T, Tx, Tr, Ts, NT_, NV_><<<nblk, NT_, 0, s>>>(                           \
-        dy, (const Tx*)x, mean, rstd, (const T*)gamma, (const Tr*)dres, dx_f32, (Ts*)dx_st, \
-        part, rows_per_blk, rows, h, want_dsum);                                           \
+    if (want_dsum)                                                                         \
+      ln_bwd_kernel<T, Tx, Tr, Ts, NT_, NV_, true><<<nblk, NT_, 0, s>>>(                   \
+          dy, (const Tx*)x, mean, rstd, (const T*)gamma, (const Tr*)dres, dx_f32,          \
+          (Ts*)dx_st, st_scale, part, rows_per_blk, rows, h);                              \
+    else                                                                                   \
+      ln_bwd_kernel<T, Tx, Tr, Ts, NT_, NV_, false><<<nblk, NT_, 0, s>>>(                  \
+          dy, (const Tx*)x, mean, rstd, (const T*)gamma, (const Tr*)dres, dx_f32,          \
+          (Ts*)dx_st, st_scale, part, rows_per_blk, rows, h);                              \
     return hipGetLastError();                                                              \
   }
   TPL_LNB(256, 1) TPL_LNB(256, 2) TPL_LNB(512, 2) TPL_LNB(1024, 2) TPL_LNB(1024, 4)
@@ -319,20 +369,22 @@ static hipError_t ln_bwd_t(const float* dy, const void* x, const float* mean,
 
 hipError_t ln_bwd(int p_dtype, const float* dy, int x_dtype, const void* x,
                   const float* mean, const float* rstd, const void* gamma, int dres_dtype,
-                  const void* dres, float* dx_f32, int st_dtype, void* dx_st, float* part,
-                  int rows_per_blk, int rows, int h, int want_dsum, hipStream_t s) {
+                  const void* dres, float* dx_f32, int st_dtype, void* dx_st,
+                  const float* st_scale, float* part, int rows_per_blk, int rows, int h,
+                  int want_dsum, hipStream_t s) {
   if (p_dtype == DT_F32 && x_dtype == DT_F32 && dres_dtype == DT_F32 && st_dtype == DT_F32)
     return ln_bwd_t<float, float, float, float>(dy, x, mean, rstd, gamma, dres, dx_f32, dx_st,
-                                                part, rows_per_blk, rows, h, want_dsum, s);
+                                                st_scale, part, rows_per_blk, rows, h, want_dsum,
+                                                s);
   if (p_dtype != DT_BF16) return hipErrorInvalidValue;
   // LN2 backward: x = h_mid (fp32), dres = upstream gradient (bf16), dx -> fp32 + fp16
   if (x_dtype == DT_F32 && dres_dtype == DT_BF16 && st_dtype == DT_F16)
-    return ln_bwd_t<bf16, float, bf16, f16>(dy, x, mean, rstd, gamma, dres, dx_f32, dx_st, part,
-                                            rows_per_blk, rows, h, want_dsum, s);
+    return ln_bwd_t<bf16, float, bf16, f16>(dy, x, mean, rstd, gamma, dres, dx_f32, dx_st,
+                                            st_scale, part, rows_per_blk, rows, h, want_dsum, s);
   // LN1 backward: x = layer input (bf16), dres = dh (fp32), dx -> bf16
   if (x_dtype == DT_BF16 && dres_dtype == DT_F32 && st_dtype == DT_BF16)
-    return ln_bwd_t<bf16, bf16, float, bf16>(dy, x, mean, rstd, gamma, dres, dx_f32, dx_st, part,
-                                             rows_per_blk, rows, h, want_dsum, s);
+    return ln_bwd_t<bf16, bf16, float, bf16>(dy, x, mean, rstd, gamma, dres, dx_f32, dx_st,
+                                             st_scale, part, rows_per_blk, rows, h, want_dsum, s);
   return hipErrorInvalidValue;
 }
 
@@ -416,7 +468,7 @@ __global__ __launch_bounds__(256) void reduce_stage1_kernel(const float* __restr
 __global__ __launch_bounds__(256) void reduce_stage2_kernel(const float* __restrict__ grp,
                                                             int ngrp, int nout, int width,
                                                             float* out0, float* out1, float* out2,
-                                                            int accumulate) {
+                                                            const float* scale, int accumulate) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int total = nout * width;
   if (idx >= total) return;
@@ -429,6 +481,7 @@ __global__ __launch_bounds__(256) void reduce_stage2_kernel(const float* __restr
     for (int u = 0; u < 8; ++u)
       if (g0 + u < ngrp) acc += x[u];
   }
+  if (scale) acc *= scale[0];
   const int k = idx / width, j = idx - k * width;
   float* o = k == 0 ? out0 : (k == 1 ? out1 : out2);
   if (!o) return;
@@ -441,7 +494,8 @@ size_t reduce_scratch_floats(int nblk, int nout, int width) {
 }
 
 hipError_t reduce_partials(const float* part, int nblk, int nout, int width, float* out0,
-                           float* out1, float* out2, int accumulate, hipStream_t s) {
+                           float* out1, float* out2, int accumulate, hipStream_t s,
+                           const float* scale) {
   const int total = nout * width;
   if (total == 0) return hipSuccess;
   const int ngrp = (nblk + kGroup - 1) / kGroup;
@@ -450,7 +504,7 @@ hipError_t reduce_partials(const float* part, int nblk, int nout, int width, flo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   reduce_stage2_kernel<<<(total + 255) / 256, 256, 0, s>>>(grp, ngrp, nout, width, out0, out1,
-                                                            out2, accumulate);
+                                                            out2, scale, accumulate);
   return hipGetLastError();
 }
 
@@ -514,16 +568,73 @@ hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts, int
 // upstream gradient the fp16 MFMA GEMMs read). Round to nearest even; every
 // bf16 value inside fp16's normal range converts exactly. 8 elements per
 // thread per step, grid-stride; tails (count % 8) element by element.
+//
+// With amax_part (the upstream gradient), the copy is multiplied by a power
+// of two S = 2^-e, e = floor(log2(max|x|)) clamped to [-126, 126], taken from
+// the kAmaxBlocks partial maxima of amax_kernel: max|S x| lies in [1, 2), so
+// the fp16 gradient chain keeps its range and precision whatever the scale
+// of the bf16 gradient (bf16 has fp32's exponent range, fp16 only 2^-24 ..
+// 65504). Multiplying by S is exact; block 0 writes S and 1/S to scale_out.
 // ----------------------------------------------------------------------------
+constexpr int kAmaxBlocks = kAmaxFloats;  // one partial maximum per workgroup
+static_assert(kAmaxBlocks == 256, "pow2_scale reduces one partial per thread of a 256-thread block");
+
 struct CvtSegs {
   const bf16* src[4];
   f16* dst[4];
   size_t n[4];
   size_t start[5];  // prefix sums of the vector counts
   int nseg;
+  const float* amax_part;  // [kAmaxBlocks] or null
+  float* scale_out;        // [2]: S, 1/S (with amax_part)
 };
 
+// Partial maxima of |x| over a bf16 tensor of n elements: part[b] for each of
+// the kAmaxBlocks workgroups (grid-stride over 8-element vectors).
+__global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, size_t n,
+                                                   float* __restrict__ part) {
+  __shared__ float red[4];
+  const size_t nvec = n / 8;
+  float m = 0.f;
+  for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += (size_t)gridDim.x * 256) {
+    float f[8];
+    Vec8<bf16>::load(x + 8 * v, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[e]));
+  }
+  if (blockIdx.x == 0)
+    for (size_t i = 8 * nvec + threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf(bf2f(x[i])));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// S from the partial maxima (every block of the conversion computes it).
+__device__ float pow2_scale(const float* part, float* red) {
+  float m = threadIdx.x < kAmaxBlocks ? part[threadIdx.x] : 0.f;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (!(m > 0.f) || !(m <= 3.4028235e38f)) return 1.f;  // zero, inf or NaN: no scaling
+  int e = (int)((__float_as_uint(m) >> 23) & 0xff) - 127;  // floor(log2 m) for normal m
+  e = e < -126 ? -126 : (e > 126 ? 126 : e);
+  return __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+}
+
 __global__ __launch_bounds__(256) void to_f16_kernel(CvtSegs c) {
+  __shared__ float red[4];
+  float sc = 1.f;
+  if (c.amax_part) {
+    sc = pow2_scale(c.amax_part, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      c.scale_out[0] = sc;
+      c.scale_out[1] = 1.f / sc;  // exact: sc is a power of two in [2^-126, 2^126]
+    }
+  }
   const size_t total = c.start[c.nseg];
   for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < total;
        v += (size_t)gridDim.x * 256) {
@@ -535,16 +646,19 @@ __global__ __launch_bounds__(256) void to_f16_kernel(CvtSegs c) {
     if (i + 8 <= c.n[sg]) {
       float f[8];
       Vec8<bf16>::load(src, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= sc;
       Vec8<f16>::store(dst, f);
     } else {
-      for (size_t e = i; e < c.n[sg]; ++e) c.dst[sg][e] = (f16)bf2f(c.src[sg][e]);
+      for (size_t e = i; e < c.n[sg]; ++e) c.dst[sg][e] = (f16)(bf2f(c.src[sg][e]) * sc);
     }
   }
 }
 
 hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
-                  hipStream_t s) {
+                  hipStream_t s, float* amax_part, float* scale_out) {
   if (nseg < 1 || nseg > 4) return hipErrorInvalidValue;
+  if ((amax_part == nullptr) != (scale_out == nullptr)) return hipErrorInvalidValue;
   CvtSegs c = {};
   c.nseg = nseg;
   c.start[0] = 0;
@@ -554,9 +668,19 @@ hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count,
     c.n[i] = count[i];
     c.start[i + 1] = c.start[i] + (count[i] + 7) / 8;
   }
+  c.amax_part = amax_part;
+  c.scale_out = scale_out;
+  if (amax_part) {
+    // the maximum over every segment, one launch per segment (the upstream
+    // gradient is a single segment)
+    if (nseg != 1) return hipErrorInvalidValue;
+    amax_kernel<<<kAmaxBlocks, 256, 0, s>>>((const bf16*)src[0], count[0], amax_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const size_t total = c.start[nseg];
-  if (!total) return hipSuccess;
-  const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 8192);
+  if (!total && !amax_part) return hipSuccess;  // (with a scale, one block still writes it)
+  const unsigned grid = (unsigned)std::max<size_t>(1, std::min<size_t>((total + 255) / 256, 8192));
   to_f16_kernel<<<grid, 256, 0, s>>>(c);
   return hipGetLastError();
 }

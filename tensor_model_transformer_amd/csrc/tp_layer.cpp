@@ -70,14 +70,25 @@ struct tp_layer {
   // workspace regions
   Region mean1, rstd1, a, qkv, qkv_lo, o, lse2, h_mid, mean2, rstd2, c, u, z;
   Region du, dc, dh_f, dh_s, dO, delta, dqkv, da, part, splitk;
+  // stream-K pieces of the GEMMs on the caller's stream (forward, data
+  // gradients); splitk holds the weight gradients' split-K partials
+  Region skp;
   // column-sum partials of the bias gradients that run on the side stream
   Region part2;
   // fp16 copies of the bf16 weights (made by the forward, read again by the
   // backward) and of the upstream gradient: the MFMA GEMMs read fp16 only
   Region w16_qkv, w16_o, w16_fc1, w16_fc2, dout16;
+  // Power-of-two scale S of the backward's fp16 gradient chain (bf16 layers):
+  // the partial maxima of |dout| and then S, 1/S. The MLP backward derives S
+  // from dout; every fp16 gradient tensor (the dout copy, du, the fp16 copy
+  // of dh, dO, dqkv) holds S times its value, and every GEMM or reduction
+  // that leaves the chain for fp32 multiplies by 1/S (exact).
+  Region gscale;
   size_t ws_bytes;
   int split_w2, split_w1, split_wo, split_wqkv;
-  double attn_pairs;  // allowed query-key pairs (causal); 0 for padding (lengths on device)
+  // allowed query-key pairs per forward, for the profile's attention FLOPs:
+  // causal from the shape; padding as given to tp_layer_profile (0 = unknown)
+  double attn_pairs;
   Prof prof;
   // Side stream of the backward: the weight gradients (and bias column sums)
   // run on it concurrently with the data-gradient chain on the caller's
@@ -198,18 +209,29 @@ void plan(tp_layer* L) {
   for (auto& w : ws) {
     GemmArgs g = wgrad_args(L, w.M, w.N, nullptr, nullptr, nullptr, 0);
     *w.split = gemm_choose_split(g);
-    if (*w.split > 1) {
-      const size_t b = (size_t)(*w.split) * w.M * w.N * 4;
-      if (b > sk) sk = b;
-    }
+    g.split = *w.split;
+    sk = std::max(sk, gemm_ws_floats(g) * 4);
   }
   take(L->splitk, sk);
+  // the other GEMMs (M = n tokens): forward QKV, W_o, FC1, FC2 and the data
+  // gradients of FC2, FC1, W_o, QKV
+  size_t skp = 0;
+  const int MNK[8][2] = {{3 * L->hl, L->hidden}, {L->hidden, L->hl}, {L->fl, L->hidden},
+                         {L->hidden, L->fl}, {L->fl, L->hidden}, {L->hidden, L->fl},
+                         {L->hl, L->hidden}, {L->hidden, 3 * L->hl}};
+  for (auto& d : MNK) {
+    GemmArgs g = gemm_base(L);
+    g.M = L->n; g.N = d[0]; g.K = d[1];
+    skp = std::max(skp, gemm_ws_floats(g) * 4);
+  }
+  take(L->skp, skp);
   const bool cvt = L->sdt == DT_BF16;
   take(L->w16_qkv, cvt ? h * 3 * L->hl * 2 : 0);
   take(L->w16_o, cvt ? (size_t)L->hl * h * 2 : 0);
   take(L->w16_fc1, cvt ? h * L->fl * 2 : 0);
   take(L->w16_fc2, cvt ? (size_t)L->fl * h * 2 : 0);
   take(L->dout16, cvt ? n * h * 2 : 0);
+  take(L->gscale, cvt ? (kAmaxFloats + 2) * 4 : 0);
   L->ws_bytes = off;
 }
 
@@ -332,7 +354,14 @@ double gemm_bytes(const tp_layer* L, const GemmArgs& g) {
   return b;
 }
 
-int run_gemm(tp_layer* L, const GemmArgs& g, hipStream_t s) {
+// Runs one GEMM with its scratch: the weight gradients (the backward's side
+// stream) use the split-K region, every other GEMM (the caller's stream) the
+// stream-K region, so GEMMs running concurrently on the two streams never
+// share scratch.
+int run_gemm(tp_layer* L, GemmArgs g, hipStream_t s, void* ws, bool wgrad = false) {
+  const Region& r = wgrad ? L->splitk : L->skp;
+  g.ws = r.bytes ? at<float>(ws, r) : nullptr;
+  g.ws_floats = r.bytes / sizeof(float);
   Scope ps(L, s, TP_K_GEMM, 2.0 * g.M * g.N * (double)g.K, gemm_bytes(L, g));
   HIP_TRY(gemm(g, s));
   return TP_OK;
@@ -378,10 +407,20 @@ int join_from(tp_layer* L, hipStream_t s, hipStream_t side) {
   return TP_OK;
 }
 
-// bf16 -> fp16 copies (nothing to do for an fp32 layer).
+// The gradient chain's S and 1/S (device fp32), or null for an fp32 layer.
+const float* chain_scale(tp_layer* L, void* ws) {
+  return L->sdt == DT_BF16 ? at<float>(ws, L->gscale) + kAmaxFloats : nullptr;
+}
+const float* chain_unscale(tp_layer* L, void* ws) {
+  return L->sdt == DT_BF16 ? at<float>(ws, L->gscale) + kAmaxFloats + 1 : nullptr;
+}
+
+// bf16 -> fp16 copies (nothing to do for an fp32 layer). With scaled, the
+// single tensor is the upstream gradient, copied times the chain's S (which
+// this call derives from it and stores in the workspace).
 int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
                   std::initializer_list<const Region*> dst, std::initializer_list<size_t> count,
-                  void* ws, hipStream_t s) {
+                  void* ws, hipStream_t s, bool scaled = false) {
   if (L->sdt != DT_BF16) return TP_OK;
   const void* sp[4];
   void* dp[4];
@@ -397,8 +436,10 @@ int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
     bytes += 4.0 * np[k];
     ++k;
   }
+  if (scaled) bytes += 2.0 * np[0];  // the maximum's pass over the gradient
   Scope ps(L, s, TP_K_CONVERT, 0, bytes);
-  HIP_TRY(to_f16(sp, dp, np, k, s));
+  float* gs = scaled ? at<float>(ws, L->gscale) : nullptr;
+  HIP_TRY(to_f16(sp, dp, np, k, s, gs, scaled ? gs + kAmaxFloats : nullptr));
   return TP_OK;
 }
 
@@ -429,7 +470,7 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
     g.epi = EPI_SPLIT16;
     g.C2 = qkv_lo(L, ws); g.ldc2 = 3 * hl; g.c2_dtype = DT_F16;
   }
-  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = run_gemm(L, g, s, ws))) return e;
   {
   Scope ps(L, s, TP_K_ATTN_FWD, 4.0 * L->dh * L->Hl * L->attn_pairs,
            (double)n * 4 * hl * L->esz + 4.0 * n * L->Hl);
@@ -446,7 +487,7 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
     g.resid = x; g.ldr = h; g.resid_dtype = L->sdt;
   }
   g.C = dst; g.ldc = h; g.c_dtype = DT_F32;
-  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = run_gemm(L, g, s, ws))) return e;
   return TP_OK;
 }
 
@@ -476,7 +517,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   g.epi = EPI_BIAS_GELU;
   g.C = L->recompute_fc1 ? nullptr : at<void>(ws, L->u); g.ldc = fl;
   g.C2 = at<void>(ws, L->z); g.ldc2 = fl;
-  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = run_gemm(L, g, s, ws))) return e;
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = fl;
   g.A = at<void>(ws, L->z); g.lda = fl; g.a_kmajor = 1;
@@ -486,7 +527,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
     g.resid = h_mid; g.ldr = h; g.resid_dtype = DT_F32;
   }
   g.C = out; g.ldc = h; g.c_dtype = out_f32 ? DT_F32 : L->sdt;
-  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = run_gemm(L, g, s, ws))) return e;
   return TP_OK;
 }
 
@@ -494,14 +535,14 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
 // Bias gradient: out (+)= column sums of y [n, cols] (two-stage, deterministic).
 // Bias gradient (column sums of y) on the side stream, with its own partials.
 int bias_grad(tp_layer* L, const void* y, int y_dtype, int cols, float* out, int accumulate,
-              void* ws, hipStream_t s, int rows = -1) {
+              void* ws, hipStream_t s, int rows = -1, const float* scale = nullptr) {
   if (rows < 0) rows = L->n;
   Scope ps(L, s, TP_K_REDUCE, 0, (double)rows * cols * L->esz + 4.0 * cols);
   float* part = at<float>(ws, L->part2);
   int rpb;
   const int nb = colsum_blocks(rows, cols, &rpb);
   HIP_TRY(colsum_partial(y_dtype, y, rows, cols, cols, part, rpb, s));
-  HIP_TRY(reduce_partials(part, nb, 1, cols, out, nullptr, nullptr, accumulate, s));
+  HIP_TRY(reduce_partials(part, nb, 1, cols, out, nullptr, nullptr, accumulate, s, scale));
   return TP_OK;
 }
 
@@ -510,7 +551,8 @@ int bias_grad(tp_layer* L, const void* y, int y_dtype, int cols, float* out, int
 int ln_backward(tp_layer* L, const float* dy, int x_dtype, const void* x, const float* mean,
                 const float* rstd, const void* gamma, int dres_dtype, const void* dres,
                 float* dx_f32, int st_dtype, void* dx_st, float* dgamma, float* dbeta,
-                float* dsum, int accumulate, void* ws, hipStream_t s, int rows = -1) {
+                float* dsum, int accumulate, void* ws, hipStream_t s, int rows = -1,
+                const float* st_scale = nullptr) {
   const int n = rows < 0 ? L->n : rows, h = L->hidden;
   float* part = at<float>(ws, L->part);
   int rpb;
@@ -520,7 +562,7 @@ int ln_backward(tp_layer* L, const float* dy, int x_dtype, const void* x, const 
     const double out_sz = (dx_f32 ? 4 : 0) + (dx_st ? L->esz : 0);
     Scope ps(L, s, TP_K_LN_BWD, 0, (double)n * h * (4 + x_sz + r_sz + out_sz) + 8.0 * n);
     HIP_TRY(ln_bwd(L->sdt, dy, x_dtype, x, mean, rstd, gamma, dres_dtype, dres, dx_f32, st_dtype,
-                   dx_st, part, rpb, n, h, dsum != nullptr, s));
+                   dx_st, st_scale, part, rpb, n, h, dsum != nullptr, s));
   }
   Scope ps(L, s, TP_K_REDUCE, 0, (double)nb * 3 * h * 4);
   HIP_TRY(reduce_partials(part, nb, 3, h, dgamma, dbeta, dsum, accumulate, s));
@@ -538,10 +580,10 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   int e;
   // the upstream gradient as the GEMMs read it (fp16 copy for a bf16 layer)
   const void* dout = dout_full ? dout_full : io->dout;
-  if ((e = to_f16_copies(L, {dout}, {&L->dout16}, {(size_t)n * h}, ws, s))) return e;
+  if ((e = to_f16_copies(L, {dout}, {&L->dout16}, {(size_t)n * h}, ws, s, true))) return e;
   if (L->sdt == DT_BF16) dout = at<void>(ws, L->dout16);
+  const float* unscale = chain_unscale(L, ws);
   const void* c_act = c_in ? c_in : at<void>(ws, L->c);
-  float* skw = at<float>(ws, L->splitk);
   GemmArgs g;
   if (L->recompute_fc1) {
     // GeLU'(c @ W_fc1,r + b_fc1,r) again, straight into the du buffer
@@ -552,7 +594,7 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
     g.bias = p->b_fc1;
     g.epi = EPI_GELU_GRAD;
     g.C = at<void>(ws, L->du); g.ldc = fl;
-    if ((e = run_gemm(L, g, s))) return e;
+    if ((e = run_gemm(L, g, s, ws))) return e;
   }
   // du = (dout @ W_fc2,r^T) * GeLU'(u), GeLU'(u) kept by the forward (in the
   // u buffer) or recomputed into the du buffer, then overwritten in place
@@ -563,8 +605,8 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, sd, db2_rows)))
     return e;
   g = wgrad_args(L, fl, h, at<void>(ws, L->z), dout, io->d_w_fc2, io->accumulate);
-  g.split = L->split_w2; g.ws = skw;
-  if ((e = run_gemm(L, g, sd))) return e;
+  g.split = L->split_w2; g.scale = unscale;
+  if ((e = run_gemm(L, g, sd, ws, true))) return e;
   g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
   g.A = dout; g.lda = h; g.a_kmajor = 1;
@@ -572,20 +614,21 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   g.epi = EPI_DGELU;
   g.aux = at<void>(ws, L->recompute_fc1 ? L->du : L->u); g.ldaux = fl;
   g.C = at<void>(ws, L->du); g.ldc = fl;
-  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = run_gemm(L, g, s, ws))) return e;
   // side stream: dW1 and db1 (need du) while dc is computed
   if ((e = fork_to(L, s, sd))) return e;
   g = wgrad_args(L, h, fl, c_act, at<void>(ws, L->du), io->d_w_fc1, io->accumulate);
-  g.split = L->split_w1; g.ws = skw;
-  if ((e = run_gemm(L, g, sd))) return e;
-  if ((e = bias_grad(L, at<void>(ws, L->du), L->adt, fl, io->d_b_fc1, io->accumulate, ws, sd)))
+  g.split = L->split_w1; g.scale = unscale;
+  if ((e = run_gemm(L, g, sd, ws, true))) return e;
+  if ((e = bias_grad(L, at<void>(ws, L->du), L->adt, fl, io->d_b_fc1, io->accumulate, ws, sd, -1,
+                     unscale)))
     return e;
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = fl;
   g.A = at<void>(ws, L->du); g.lda = fl; g.a_kmajor = 1;
   g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 1;
-  g.C = dc_out; g.ldc = h; g.c_dtype = DT_F32;
-  if ((e = run_gemm(L, g, s))) return e;
+  g.C = dc_out; g.ldc = h; g.c_dtype = DT_F32; g.scale = unscale;
+  if ((e = run_gemm(L, g, s, ws))) return e;
   return join_from(L, s, sd);
 }
 
@@ -599,12 +642,13 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
              const void* a_in = nullptr) {
   const int n = L->n, h = L->hidden, hl = L->hl;
   int e;
-  float* skw = at<float>(ws, L->splitk);
+  const float* unscale = chain_unscale(L, ws);
   if (!dh_in &&
       (e = ln_backward(L, dc, DT_F32, at<void>(ws, L->h_mid), at<float>(ws, L->mean2),
                        at<float>(ws, L->rstd2), p->ln2_gamma, L->sdt, io->dout,
                        at<float>(ws, L->dh_f), L->adt, at<void>(ws, L->dh_s), io->d_ln2_gamma,
-                       io->d_ln2_beta, io->d_b_o, io->accumulate, ws, s)))
+                       io->d_ln2_beta, io->d_b_o, io->accumulate, ws, s, -1,
+                       chain_scale(L, ws))))
     return e;
   const void* dh_s = dh_in ? dh_in : at<void>(ws, L->dh_s);
   const void* a_act = a_in ? a_in : at<void>(ws, L->a);
@@ -612,14 +656,14 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
   hipStream_t sd = side_stream(L, s);
   if ((e = fork_to(L, s, sd))) return e;
   GemmArgs g = wgrad_args(L, hl, h, at<void>(ws, L->o), dh_s, io->d_w_o, io->accumulate);
-  g.split = L->split_wo; g.ws = skw;
-  if ((e = run_gemm(L, g, sd))) return e;
+  g.split = L->split_wo; g.scale = unscale;
+  if ((e = run_gemm(L, g, sd, ws, true))) return e;
   g = gemm_base(L);
   g.M = n; g.N = hl; g.K = h;
   g.A = dh_s; g.lda = h; g.a_kmajor = 1;
   g.B = wmat(L, ws, L->w16_o, p->w_o); g.ldb = h; g.b_kmajor = 1;
   g.C = at<void>(ws, L->dO); g.ldc = hl;
-  if ((e = run_gemm(L, g, s))) return e;
+  if ((e = run_gemm(L, g, s, ws))) return e;
   {
     Scope ps(L, s, TP_K_ATTN_BWD, 8.0 * L->dh * L->Hl * L->attn_pairs,
              (double)n * 8 * hl * L->esz + 8.0 * n * L->Hl);
@@ -631,17 +675,17 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
   // side stream: dW_qkv and db_qkv (need dqkv) while da is computed
   if ((e = fork_to(L, s, sd))) return e;
   g = wgrad_args(L, h, 3 * hl, a_act, at<void>(ws, L->dqkv), io->d_w_qkv, io->accumulate);
-  g.split = L->split_wqkv; g.ws = skw;
-  if ((e = run_gemm(L, g, sd))) return e;
+  g.split = L->split_wqkv; g.scale = unscale;
+  if ((e = run_gemm(L, g, sd, ws, true))) return e;
   if ((e = bias_grad(L, at<void>(ws, L->dqkv), L->adt, 3 * hl, io->d_b_qkv, io->accumulate, ws,
-                     sd)))
+                     sd, -1, unscale)))
     return e;
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = 3 * hl;
   g.A = at<void>(ws, L->dqkv); g.lda = 3 * hl; g.a_kmajor = 1;
   g.B = wmat(L, ws, L->w16_qkv, p->w_qkv); g.ldb = 3 * hl; g.b_kmajor = 1;
-  g.C = da_out; g.ldc = h; g.c_dtype = DT_F32;
-  if ((e = run_gemm(L, g, s))) return e;
+  g.C = da_out; g.ldc = h; g.c_dtype = DT_F32; g.scale = unscale;
+  if ((e = run_gemm(L, g, s, ws))) return e;
   return join_from(L, s, sd);
 }
 
@@ -721,7 +765,8 @@ int bwd_sp(tp_layer* L, int phase, const tp_params* p, const tp_bwd_io* io, void
       return ln_backward(L, io->dc, DT_F32, at<void>(ws, L->h_mid), at<float>(ws, L->mean2),
                          at<float>(ws, L->rstd2), p->ln2_gamma, L->sdt, io->dout,
                          at<float>(ws, L->dh_f), L->adt, chunk_rows(io->gathered_grad, L),
-                         io->d_ln2_gamma, io->d_ln2_beta, io->d_b_o, io->accumulate, ws, s, nc);
+                         io->d_ln2_gamma, io->d_ln2_beta, io->d_b_o, io->accumulate, ws, s, nc,
+                         chain_scale(L, ws));
     case TP_BWD_SP_ATTN:
       if ((e = check_ptrs({io->gathered_grad, io->gathered_act, io->partial, io->d_w_qkv,
                            io->d_b_qkv, io->d_w_o})))
@@ -919,7 +964,7 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
     if (seq_par && n % t) return TP_ERR_SHAPE;
   }
   tp_layer* L = new (std::nothrow) tp_layer();
-  if (!L) return TP_ERR_ARG;
+  if (!L) return TP_ERR_NOMEM;
   L->hidden = hidden; L->heads = heads; L->ffn = ffn; L->seq = seq; L->batch = micro_batch;
   L->t = t; L->rank = rank; L->dtype = dtype; L->mask = mask;
   L->eps = eps; L->gelu_tanh = gelu == TP_GELU_TANH;
@@ -1014,14 +1059,13 @@ int tp_layer_decode_workspace(const tp_layer* L, size_t* bytes) {
   return TP_OK;
 }
 
-int tp_layer_decode(tp_layer* L, int phase, const tp_decode_io* io, void* hip_stream) {
+// Argument checks shared by both decode entry points (the workspace apart).
+static int decode_checks(tp_layer* L, int phase, const tp_decode_io* io) {
   if (!L || !io) return TP_ERR_ARG;
   if (L->mask != TP_MASK_CAUSAL || L->batch > 128) return TP_ERR_UNSUPPORTED;
   if (phase < TP_ALL || phase > TP_FWD_MLP) return TP_ERR_PHASE;
   int e = check_params(L, io->params);
   if (e) return e;
-  if (!io->workspace || io->workspace_bytes < L->dec.bytes) return TP_ERR_WORKSPACE;
-  if (!aligned(io->workspace)) return TP_ERR_ALIGN;
   if (phase != TP_FWD_MLP) {
     if ((e = check_ptrs({io->x, io->out, io->k_cache, io->v_cache, io->positions}))) return e;
     if (L->split_scores && (e = check_ptrs({io->k_cache_lo}))) return e;
@@ -1029,8 +1073,13 @@ int tp_layer_decode(tp_layer* L, int phase, const tp_decode_io* io, void* hip_st
   } else if ((e = check_ptrs({io->h_mid, io->out}))) {
     return e;
   }
-  hipStream_t s = (hipStream_t)hip_stream;
-  void* ws = io->workspace;
+  return TP_OK;
+}
+
+// Enqueues one decode phase with `ws` (L->dec.bytes, 16-byte aligned) as its
+// workspace.
+static int decode_run(tp_layer* L, int phase, const tp_decode_io* io, void* ws, hipStream_t s) {
+  int e;
   const tp_params* p = io->params;
   const bool designated = L->rank == 0;
   switch (phase) {
@@ -1047,6 +1096,14 @@ int tp_layer_decode(tp_layer* L, int phase, const tp_decode_io* io, void* hip_st
     default:
       return dec_mlp_phase(L, p, io->h_mid, io->out, DT_F32, designated, false, ws, s);
   }
+}
+
+int tp_layer_decode(tp_layer* L, int phase, const tp_decode_io* io, void* hip_stream) {
+  int e = decode_checks(L, phase, io);
+  if (e) return e;
+  if (!io->workspace || io->workspace_bytes < L->dec.bytes) return TP_ERR_WORKSPACE;
+  if (!aligned(io->workspace)) return TP_ERR_ALIGN;
+  return decode_run(L, phase, io, io->workspace, (hipStream_t)hip_stream);
 }
 
 int tp_layer_kv_fill(const tp_layer* L, const void* workspace, size_t workspace_bytes,
@@ -1097,8 +1154,9 @@ int tp_exchange_sum(void* dst, int dst_dtype, const float* const* parts, int npa
   return TP_OK;
 }
 
-int tp_layer_profile(tp_layer* L, int enable) {
-  if (!L) return TP_ERR_ARG;
+int tp_layer_profile(tp_layer* L, int enable, double attn_pairs) {
+  if (!L || !(attn_pairs >= 0.0)) return TP_ERR_ARG;
+  if (L->mask == TP_MASK_PADDING) L->attn_pairs = attn_pairs;
   Prof& p = L->prof;
   prof_fold(p);
   for (int k = 0; k < TP_K_COUNT; ++k) {
@@ -1138,6 +1196,15 @@ int tp_layer_tap(const tp_layer* L, int tap, size_t* offset, size_t* bytes) {
     case TP_TAP_FC1_OUT: r = &L->z; break;
     case TP_TAP_DQKV: r = &L->dqkv; break;
     case TP_TAP_DH: r = &L->dh_f; break;
+    case TP_TAP_QKV_LO:
+      if (!L->split_scores) return TP_ERR_UNSUPPORTED;
+      r = &L->qkv_lo;
+      break;
+    case TP_TAP_GRAD_SCALE:
+      if (L->sdt != DT_BF16) return TP_ERR_UNSUPPORTED;  // no scaling on the fp32 path
+      *offset = L->gscale.off + kAmaxFloats * sizeof(float);
+      *bytes = 2 * sizeof(float);
+      return TP_OK;
     default: return TP_ERR_ARG;
   }
   *offset = r->off;

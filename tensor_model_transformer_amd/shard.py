@@ -54,10 +54,9 @@ class Shard:
              "scores": scores, "recompute": recompute,
              "sequence_parallel": int(sequence_parallel)})
         self.dx_fp32 = dx_fp32
-        # the header's rule for the score precision (TP_SCORES_AUTO: split from hidden 8192)
-        self.split_scores = dims.dtype == "bf16" and (
-            scores == B.TP_SCORES_SPLIT or (scores == B.TP_SCORES_AUTO and dims.hidden >= 8192))
         _check("tp_layer_create", rc)
+        # whether the handle keeps the score residuals (what TP_SCORES_AUTO chose)
+        self.split_scores = B.tp_layer_tap(self.handle, "qkv_lo")[0] == B.TP_OK
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
         self.dws = None
         self.dws_bytes = 0

@@ -43,17 +43,27 @@ def to_np(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
+def local_inputs(w, rank=None):
+    """(params, x, dout, valid_len) of one rank from the seeded generator."""
+    r = w.rank if rank is None else rank
+    x, dout, vl = layer_inputs(w)
+    return rank_params(w, r), x, dout, vl
+
+
 def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True, scores=0,
-                  recompute=0):
-    """TP_ALL forward + backward of one rank on the GPU. Returns numpy dict."""
+                  recompute=0, gelu="erf", eps=1e-5, inputs=None):
+    """TP_ALL forward + backward of one rank on the GPU. Returns numpy dict.
+    `inputs` replaces the generated (params, x, dout, valid_len); its values
+    must already lie on the storage grid (bf16 or fp32)."""
     import torch
+    from tensor_model_transformer_amd import binding as B
     from tensor_model_transformer_amd.shard import Shard, _check
 
     d = w.dims
     r = w.rank if rank is None else rank
-    params = rank_params(w, r)
-    x, dout, vl = layer_inputs(w)
-    sh = Shard(d, r, dx_fp32=dx_fp32, scores=scores, recompute=recompute)
+    params, x, dout, vl = inputs if inputs is not None else local_inputs(w, r)
+    sh = Shard(d, r, dx_fp32=dx_fp32, scores=scores, recompute=recompute, eps=eps,
+               gelu=B.TP_GELU_TANH if gelu == "tanh" else B.TP_GELU_ERF)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()
@@ -79,7 +89,11 @@ def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True
     torch.cuda.synchronize()
     if taps:
         dt = torch.float16 if d.dtype == "bf16" else torch.float32
-        res["dqkv"] = to_np(sh.tap("dqkv").view(dt).reshape(d.tokens, 3 * d.hidden_local))
+        # the fp16 gradient chain holds S times its values (S = 1 for fp32)
+        unscale = to_np(sh.tap("grad_scale").view(torch.float32))[1] if d.dtype == "bf16" else 1.0
+        res["grad_scale"] = 1.0 / unscale
+        res["dqkv"] = unscale * to_np(sh.tap("dqkv").view(dt).reshape(d.tokens,
+                                                                     3 * d.hidden_local))
         res["dh"] = to_np(sh.tap("dh").view(torch.float32).reshape(d.tokens, d.hidden))
     res["out"] = to_np(out).reshape(d.batch, d.seq, d.hidden)
     res["dx"] = to_np(dx).reshape(d.batch, d.seq, d.hidden)
@@ -89,11 +103,12 @@ def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True
     return res
 
 
-def oracle_local(w, rank=None):
+def oracle_local(w, rank=None, gelu="erf", eps=1e-5, inputs=None):
     d = w.dims
-    r = w.rank if rank is None else rank
-    x, dout, vl = layer_inputs(w)
-    return OL.layer_local(rank_params(w, r), x, dout, d, vl)
+    params, x, dout, vl = inputs if inputs is not None else local_inputs(w, rank)
+    ref = OL.layer_local(params, x, dout, d, vl, eps=eps, gelu_form=gelu)
+    ref["gelu_form"] = gelu
+    return ref
 
 
 def compare_local(gpu, ref, tau, taps=False):
@@ -114,7 +129,8 @@ def compare_local(gpu, ref, tau, taps=False):
             if k in gpu:
                 ok &= check(k, gpu[k], ref[k], ti, report)
         if "dgelu" in gpu:  # the library keeps GeLU'(u) rather than u
-            ok &= check("dgelu", gpu["dgelu"], OL.gelu_grad(ref["u"]), ti, report)
+            ok &= check("dgelu", gpu["dgelu"], OL.gelu_grad(ref["u"], ref.get("gelu_form", "erf")),
+                        ti, report)
         ok &= check("lse", gpu["lse"], ref["lse"].reshape(-1), ti, report)
     return bool(ok), report
 

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 def test_enum_values_match_header():
     src = open(HEADER).read()
     for name in ("TP_OK", "TP_ERR_ARG", "TP_ERR_SHAPE", "TP_ERR_UNSUPPORTED", "TP_ERR_ALIGN",
-                 "TP_ERR_WORKSPACE", "TP_ERR_HIP", "TP_ERR_PHASE", "TP_DTYPE_F32",
+                 "TP_ERR_WORKSPACE", "TP_ERR_HIP", "TP_ERR_PHASE", "TP_ERR_NOMEM", "TP_DTYPE_F32",
                  "TP_DTYPE_BF16", "TP_MASK_CAUSAL", "TP_MASK_PADDING", "TP_FWD_ATTN",
                  "TP_FWD_MLP", "TP_BWD_MLP", "TP_BWD_ATTN", "TP_BWD_LN1"):
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", src)
@@ -91,6 +91,9 @@ def test_create_ok_and_workspace_plan(lib):
     seen = []
     for name in B.TAPS:
         rc, off, nb = B.tp_layer_tap(h, name)
+        if name == "qkv_lo":  # kept only with split scores (not chosen at hidden 128)
+            assert rc == B.TP_ERR_UNSUPPORTED
+            continue
         assert rc == B.TP_OK
         assert off % 256 == 0 and off + nb <= ws
         seen.append((off, off + nb))
@@ -100,6 +103,39 @@ def test_create_ok_and_workspace_plan(lib):
     assert B.tp_layer_tap(h, 99)[0] == B.TP_ERR_ARG
     assert B.tp_layer_destroy(h) == B.TP_OK
     assert B.tp_layer_destroy(None) == B.TP_OK
+
+
+def test_scale_and_residual_taps(lib):
+    # the gradient-chain scale exists on the 16-bit path only; the score
+    # residuals exactly when split scores are on (AUTO: from hidden 8192)
+    rc, h, _ = create(dtype=B.TP_DTYPE_F32)
+    assert rc == B.TP_OK
+    assert B.tp_layer_tap(h, "grad_scale")[0] == B.TP_ERR_UNSUPPORTED
+    assert B.tp_layer_tap(h, "qkv_lo")[0] == B.TP_ERR_UNSUPPORTED
+    B.tp_layer_destroy(h)
+    rc, h, _ = create()
+    rc2, off, nb = B.tp_layer_tap(h, "grad_scale")
+    assert rc2 == B.TP_OK and nb == 8
+    B.tp_layer_destroy(h)
+    for opts, hidden, split in (({"scores": B.TP_SCORES_SPLIT}, 128, True),
+                                ({"scores": B.TP_SCORES_FP16}, 8192, False),
+                                (None, 8192, True), (None, 4096, False)):
+        rc, h, _ = create(hidden=hidden, heads=hidden // 64, ffn=4 * hidden, opts=opts)
+        assert rc == B.TP_OK
+        rc2, _, nb = B.tp_layer_tap(h, "qkv_lo")
+        assert (rc2 == B.TP_OK) == split, (opts, hidden)
+        if split:  # fp16 [n, 3*h_l], n = 2*64 tokens, t = 2
+            assert nb == 2 * 64 * 3 * (hidden // 2) * 2
+        B.tp_layer_destroy(h)
+
+
+def test_profile_arguments(lib):
+    rc, h, _ = create()
+    assert B.tp_layer_profile(h, 1, -1.0) == B.TP_ERR_ARG
+    assert B.tp_layer_profile(h, 1, 0.0) == B.TP_OK
+    assert B.tp_layer_profile(h, 0) == B.TP_OK
+    assert B.tp_layer_profile(None, 0) == B.TP_ERR_ARG
+    B.tp_layer_destroy(h)
 
 
 def test_split_scores_workspace(lib):

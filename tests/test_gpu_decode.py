@@ -30,7 +30,7 @@ def _wl(name, batch, hidden, heads, ffn, t=1, dtype="bf16", seed=60, rank=0, seq
                                     mask="causal"), rank=rank, seed=seed, affine="perturbed")
 
 
-def run_decode(w, cache_len, positions="ragged", scores=0, rank=None):
+def run_decode(w, cache_len, positions="ragged", scores=0, rank=None, gelu="erf", eps=1e-5):
     """One TP_ALL decode step of one rank on the GPU. Returns numpy results
     and the inputs it used."""
     import torch
@@ -40,7 +40,9 @@ def run_decode(w, cache_len, positions="ragged", scores=0, rank=None):
     r = w.rank if rank is None else rank
     x, pos = decode_inputs(w, cache_len, positions)
     kc, vc = rank_caches(w, r, cache_len)
-    sh = Shard(d, r, scores=scores)
+    from tensor_model_transformer_amd import binding as B
+    sh = Shard(d, r, scores=scores, eps=eps,
+               gelu=B.TP_GELU_TANH if gelu == "tanh" else B.TP_GELU_ERF)
     p = sh.upload_params(rank_params(w, r))
     xd = torch.from_numpy(x).to(sh.device).to(sh.dtype)
     kd, vd = sh.upload_cache(kc), sh.upload_cache(vc)
@@ -58,10 +60,11 @@ def run_decode(w, cache_len, positions="ragged", scores=0, rank=None):
     return res, (x, pos, kc, vc)
 
 
-def compare_decode(w, gpu, inputs, tau):
+def compare_decode(w, gpu, inputs, tau, gelu="erf", eps=1e-5):
     d = w.dims
     x, pos, kc, vc = inputs
-    ref = OD.decode_step(rank_params(w, w.rank), x, kc, vc, pos, d.heads_local)
+    ref = OD.decode_step(rank_params(w, w.rank), x, kc, vc, pos, d.heads_local, eps=eps,
+                         gelu_form=gelu)
     rep = {"out": err_ratio(gpu["out"], ref["out"])}
     B_, Hl = d.batch, d.heads_local
     newk = np.stack([ref["k_cache"][b, :, pos[b]] for b in range(B_)])
@@ -106,6 +109,18 @@ def test_decode_matches_oracle(w, cache_len, positions, scores):
     rep = compare_decode(w, gpu, inputs, TAU[w.dims.dtype])
     print(f"[decode] {w.name}: {fmt(rep)}", flush=True)
     assert all(v <= TAU[w.dims.dtype] for v in rep.values()), fmt(rep)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_gelu_tanh_and_eps(dtype):
+    # opts.gelu = TP_GELU_TANH in the FC1 GEMV epilogue, opts.ln_eps in both
+    # LayerNorms (the decode-only fused residual + LN2 kernel included)
+    _need_gpu()
+    w = _wl(f"dec_tanh_eps_{dtype}", 3, 384, 4, 768, dtype=dtype, seed=61)
+    gpu, inputs = run_decode(w, 90, "ragged", gelu="tanh", eps=1e-3)
+    rep = compare_decode(w, gpu, inputs, TAU[dtype], gelu="tanh", eps=1e-3)
+    print(f"[decode] {w.name}: {fmt(rep)}", flush=True)
+    assert all(v <= TAU[dtype] for v in rep.values()), fmt(rep)
 
 
 def test_decode_is_deterministic():

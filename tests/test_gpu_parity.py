@@ -21,12 +21,12 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _run(w, rank=None, taps=False, scores=0):
+def _run(w, rank=None, taps=False, scores=0, gelu="erf", eps=1e-5):
     _need_gpu()
     print(f"\n[parity] {w.name} dims={w.dims} rank={w.rank if rank is None else rank} "
-          f"scores={scores}", flush=True)
-    gpu = run_gpu_local(w, rank, taps=taps, scores=scores)
-    ref = oracle_local(w, rank)
+          f"scores={scores} gelu={gelu} eps={eps}", flush=True)
+    gpu = run_gpu_local(w, rank, taps=taps, scores=scores, gelu=gelu, eps=eps)
+    ref = oracle_local(w, rank, gelu=gelu, eps=eps)
     ok, rep = compare_local(gpu, ref, TAU[w.dims.dtype], taps=taps)
     print(f"[parity] {w.name}: {fmt(rep)}", flush=True)
     assert ok, f"{w.name}: {fmt(rep)}"
@@ -290,3 +290,43 @@ def test_phased_sum_over_shards_equals_unsharded(w):
             rep[f"d_{k}_r{r}"] = err_ratio(g, part["grads"][r][k])
     print(f"[phased] {w.name}: {fmt(rep)}", flush=True)
     assert all(v <= tau for v in rep.values()), fmt(rep)
+
+
+# ---------------------------------------------------------------------------
+# the ABI's other GeLU form and LayerNorm epsilons (opts.gelu, opts.ln_eps)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("w", [SMALL_BF16[2], WORKLOADS["tiny_gpt_fp32"].with_(affine="perturbed")],
+                         ids=lambda w: w.name)
+def test_gelu_tanh_form(w):
+    # TP_GELU_TANH: the tanh approximation in the FC1 epilogue (GeLU and the
+    # kept derivative), against the oracle's tanh form
+    _run(w, taps=True, gelu="tanh")
+
+
+@pytest.mark.parametrize("eps", [1e-6, 1e-3])
+@pytest.mark.parametrize("w", [SMALL_BF16[0], WORKLOADS["tiny_gpt_fp32"].with_(affine="perturbed")],
+                         ids=lambda w: w.name)
+def test_layernorm_eps(w, eps):
+    _run(w, taps=True, eps=eps)
+
+
+# ---------------------------------------------------------------------------
+# GEMMs long in K (8192 = 128 K steps) and short in M: the launcher schedules
+# them stream-K (the K steps of a column of tiles spread over slots of
+# workgroups, split columns summed by the fix-up kernel), as it does for the
+# 1T shard's M = 2048 GEMMs. One row tile (M = 200: 256 slots, some of them
+# empty) and two (M = 320, the second partial: 128 slots). hidden 8192 also
+# turns split scores on.
+# ---------------------------------------------------------------------------
+STREAM_K = [
+    Workload("sk_h8192_causal", LayerDims(1, 200, 8192, 64, 16384, t=8, dtype="bf16",
+                                          mask="causal"), rank=3, seed=41, affine="perturbed"),
+    Workload("sk_h8192_padding", LayerDims(2, 160, 8192, 64, 16384, t=8, dtype="bf16",
+                                           mask="padding"), rank=5, seed=42, affine="perturbed",
+             len_range=(40, 160)),
+]
+
+
+@pytest.mark.parametrize("w", STREAM_K, ids=lambda w: w.name)
+def test_stream_k_shapes(w):
+    _run(w, taps=True)

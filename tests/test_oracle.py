@@ -61,6 +61,27 @@ def test_brute_force_padding_mask():
     assert rel_max(ref, bf) <= 1e-12
 
 
+@pytest.mark.parametrize("mask", ["causal", "padding"])
+def test_brute_force_log_sum_exp(mask):
+    # The log-sum-exp the backward recomputes P from (and the GPU's LSE tap is
+    # checked against): the vectorised oracle's lse [b, H, s] equals the
+    # normaliser the scalar loops accumulate row by row. Catches a dropped max
+    # shift, a wrong scale, or masked keys counted in the sum.
+    if mask == "causal":
+        w = WORKLOADS["tiny_gpt_fp32"].with_(affine="perturbed")
+    else:
+        w = tiny(mask="padding", t=1, batch=3, seq=6, len_range=(2, 6))
+    d = w.dims
+    x, dout, vl = layer_inputs(w)
+    p = rank_params(w, 0)
+    heads = d.heads_local
+    ref = L.layer(p, x, dout, heads, d.mask, vl)["lse"]
+    _, bl = brute.forward(p, x.astype(np.float64), heads, d.mask, vl, want_lse=True)
+    bl = np.array(bl)
+    assert ref.shape == bl.shape == (d.batch, heads, d.seq)
+    assert np.max(np.abs(ref - bl)) <= 1e-12 * max(1.0, float(np.max(np.abs(bl))))
+
+
 # --------------------------------------------------------------------------
 # check 1: the sum over shards equals the unsharded layer (f/g algebra)
 # --------------------------------------------------------------------------
@@ -306,6 +327,25 @@ def test_gelu_closed_forms():
     assert np.max(np.abs(num_t - L.gelu_grad(u, "tanh"))) <= 1e-8
     # the tanh form approximates the erf form to about 1e-3
     assert np.max(np.abs(L.gelu(u, "tanh") - g)) <= 1e-3
+
+
+@pytest.mark.parametrize("form", ["erf", "tanh"])
+def test_gelu_against_torch(form):
+    # An independent implementation: PyTorch's CPU GeLU in float64 (exact erf
+    # form for approximate="none", the Hendrycks-Gimpel tanh approximation for
+    # approximate="tanh"), and its autograd derivative. A wrong constant in
+    # either form (sqrt(2/pi), 0.044715, the 1/sqrt(2) of the erf argument) or
+    # a wrong derivative term fails here.
+    torch = pytest.importorskip("torch")
+    u = np.concatenate([np.linspace(-8.0, 8.0, 2001), [-0.0, 1e-8, -1e-8, 30.0, -30.0]])
+    ut = torch.tensor(u, dtype=torch.float64, requires_grad=True)
+    approx = "none" if form == "erf" else "tanh"
+    yt = torch.nn.functional.gelu(ut, approximate=approx)
+    (gt,) = torch.autograd.grad(yt.sum(), ut)
+    y = L.gelu(u, form)
+    g = L.gelu_grad(u, form)
+    assert np.max(np.abs(y - yt.detach().numpy())) <= 1e-14 * 30
+    assert np.max(np.abs(g - gt.numpy())) <= 1e-13
 
 
 # --------------------------------------------------------------------------
