@@ -366,6 +366,25 @@ int tp_layer_decode_workspace(const tp_layer *L, size_t *bytes);
 /* Enqueue one decode phase (TP_ALL, TP_FWD_ATTN or TP_FWD_MLP). */
 int tp_layer_decode(tp_layer *L, int phase, const tp_decode_io *io, void *hip_stream);
 
+/* tp_layer_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same phases, arguments, kernels and
+ * results as tp_layer_decode, except that io->workspace and
+ * io->workspace_bytes are not read: the decode scratch lives in a device
+ * array of TP_DECODE_STATIC_MAX_BYTES inside the library, one per device,
+ * held until the process ends (its address is looked up on the first call on
+ * each device, with that device current; hip_stream must belong to it).
+ * Handles whose tp_layer_decode_workspace exceeds that size get
+ * TP_ERR_WORKSPACE (32 MB holds every decode batch up to 128 of shards up to
+ * hidden 8192, and the 1T shard's up to 8). Nothing is allocated, no
+ * allocating library routine is called, and the call is not timed by
+ * tp_layer_profile. Every call on a device shares that device's array:
+ * calls that overlap on one device (two streams, two threads, two handles)
+ * race and must be ordered by the caller. The array keeps the last call's
+ * contents; the decode kernels need it in no particular state. */
+#define TP_DECODE_STATIC_MAX_BYTES (32u << 20)
+int tp_layer_decode_static(tp_layer *L, int phase, const tp_decode_io *io, void *hip_stream);
+
 /* Prefill into a cache: copy the K and V of every token of the last forward
  * on this handle (a TP_ALL, TP_FWD_ATTN or TP_FWD_SP_ATTN phase whose
  * workspace is passed here untouched) into rows 0..seq-1 of the caches of the

@@ -47,7 +47,9 @@ GRAD_FIELDS = tuple("d_" + f for f in PARAM_FIELDS)
 # Every symbol the header declares (checked by the CPU test of the library).
 EXPORTS = ("tp_layer_create", "tp_layer_fwd", "tp_layer_bwd", "tp_layer_destroy",
            "tp_exchange_sum", "tp_layer_tap", "tp_layer_profile", "tp_layer_profile_read",
-           "tp_layer_decode_workspace", "tp_layer_decode", "tp_layer_kv_fill")
+           "tp_layer_decode_workspace", "tp_layer_decode", "tp_layer_kv_fill",
+           "tp_layer_decode_static")
+TP_DECODE_STATIC_MAX_BYTES = 32 << 20
 KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce", "convert")
 
 
@@ -120,6 +122,8 @@ def lib():
         L.tp_layer_kv_fill.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                        c_int, c_void_p]
         L.tp_layer_kv_fill.restype = c_int
+        L.tp_layer_decode_static.argtypes = [c_void_p, c_int, POINTER(tp_decode_io), c_void_p]
+        L.tp_layer_decode_static.restype = c_int
         _lib = L
     return _lib
 
@@ -189,6 +193,11 @@ def tp_layer_decode_workspace(handle):
 
 def tp_layer_decode(handle, phase, io: tp_decode_io, stream=0):
     return lib().tp_layer_decode(handle, phase, ctypes.byref(io), stream)
+
+
+def tp_layer_decode_static(handle, phase, io: tp_decode_io, stream=0):
+    """tp_layer_decode with the library's own per-device scratch (io.workspace unused)."""
+    return lib().tp_layer_decode_static(handle, phase, ctypes.byref(io), stream)
 
 
 def tp_layer_kv_fill(handle, workspace, workspace_bytes, k_cache, v_cache, k_cache_lo,

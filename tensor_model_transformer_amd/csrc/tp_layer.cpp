@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cmath>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -1104,6 +1105,57 @@ int tp_layer_decode(tp_layer* L, int phase, const tp_decode_io* io, void* hip_st
   if (!io->workspace || io->workspace_bytes < L->dec.bytes) return TP_ERR_WORKSPACE;
   if (!aligned(io->workspace)) return TP_ERR_ALIGN;
   return decode_run(L, phase, io, io->workspace, (hipStream_t)hip_stream);
+}
+
+}  // extern "C"
+
+// ---- decode without a caller workspace -----------------------------------------
+// The scratch of tp_layer_decode_static: a file-scope device array. Every
+// device the library runs on holds its own copy until the process ends. In
+// host code `scratch` names a host-side stand-in, not the device memory: its
+// device address comes from hipGetSymbolAddress, looked up once per device
+// (with that device current) and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[TP_DECODE_STATIC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address, looked up on the first call on the device.
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TP_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return TP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return TP_ERR_HIP;
+    }
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return TP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int tp_layer_decode_static(tp_layer* L, int phase, const tp_decode_io* io, void* hip_stream) {
+  int e = decode_checks(L, phase, io);
+  if (e) return e;
+  if (L->dec.bytes > TP_DECODE_STATIC_MAX_BYTES) return TP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((e = device_scratch(&ws))) return e;
+  // Profiling creates HIP events on first use; this entry point creates
+  // nothing, so its launches are not timed.
+  const bool prof = L->prof.on;
+  L->prof.on = false;
+  e = decode_run(L, phase, io, ws, (hipStream_t)hip_stream);
+  L->prof.on = prof;
+  return e;
 }
 
 int tp_layer_kv_fill(const tp_layer* L, const void* workspace, size_t workspace_bytes,
