@@ -62,7 +62,7 @@ size_t reduce_scratch_floats(int nblk, int nout, int width);
 // With amax_part (kAmaxFloats floats of scratch) and scale_out (2 floats),
 // nseg must be 1 and dst = fp16(S * src) with the power of two S that puts
 // max|S src| in [1, 2); scale_out receives S and 1/S (device fp32).
-constexpr int kAmaxFloats = 256;
+constexpr int kAmaxFloats = 1024;
 hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
                   hipStream_t s, float* amax_part = nullptr, float* scale_out = nullptr);
 

@@ -577,7 +577,7 @@ hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts, int
 // 65504). Multiplying by S is exact; block 0 writes S and 1/S to scale_out.
 // ----------------------------------------------------------------------------
 constexpr int kAmaxBlocks = kAmaxFloats;  // one partial maximum per workgroup
-static_assert(kAmaxBlocks == 256, "pow2_scale reduces one partial per thread of a 256-thread block");
+static_assert(kAmaxBlocks % 256 == 0, "pow2_scale reduces the partials with a 256-thread block");
 
 struct CvtSegs {
   const bf16* src[4];
@@ -594,9 +594,19 @@ struct CvtSegs {
 __global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, size_t n,
                                                    float* __restrict__ part) {
   __shared__ float red[4];
-  const size_t nvec = n / 8;
+  const size_t nvec = n / 8, stride = (size_t)gridDim.x * 256;
   float m = 0.f;
-  for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += (size_t)gridDim.x * 256) {
+  size_t v = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; v + 3 * stride < nvec; v += 4 * stride) {  // four 16-byte loads in flight
+    float f[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Vec8<bf16>::load(x + 8 * (v + u * stride), f[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f[u][e]));
+  }
+  for (; v < nvec; v += stride) {
     float f[8];
     Vec8<bf16>::load(x + 8 * v, f);
 #pragma unroll
@@ -613,7 +623,9 @@ __global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, s
 
 // S from the partial maxima (every block of the conversion computes it).
 __device__ float pow2_scale(const float* part, float* red) {
-  float m = threadIdx.x < kAmaxBlocks ? part[threadIdx.x] : 0.f;
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < kAmaxBlocks / 256; ++i) m = fmaxf(m, part[i * 256 + threadIdx.x]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
