@@ -601,26 +601,43 @@ struct SkFix {
 
 // Sums the pieces of each split column in slot order and applies the
 // epilogue. Workgroup (q, r, chunk): rows [chunk*32, chunk*32+32) of row tile
-// r of split column q; a thread handles 4 consecutive columns of a row.
+// r of split column q; each thread owns NE float4 positions of those rows
+// (4 consecutive columns each) and loads them from every piece before the
+// epilogue, so NE loads per piece are in flight at once.
 template <int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_sk_fixup_kernel(GemmArgs g, SkPlan p, SkFix f) {
   constexpr int RCH = BM / 32;
+  constexpr int LPR = BN / 4;           // float4 per tile row
+  constexpr int NE = 32 * LPR / 256;    // float4 per thread
+  static_assert(32 * LPR % 256 == 0, "fix-up chunking");
   const int q = blockIdx.x / (p.U * RCH);
   const int r = (blockIdx.x / RCH) % p.U, chunk = blockIdx.x % RCH;
   const int c = f.col[q];
   const float sc = g.scale ? g.scale[0] : 1.f;
-  constexpr int LPR = BN / 4;  // threads per tile row
-  for (int e = threadIdx.x; e < 32 * LPR; e += 256) {
-    const int rr = chunk * 32 + e / LPR, cc = 4 * (e % LPR);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = f.j0[q]; j <= f.j1[q]; ++j) {
-      if (sk_begin(p, j) == sk_begin(p, j + 1)) continue;  // an empty slot wrote nothing
-      const int which = (int)(sk_begin(p, j) / p.kI) == c ? 0 : 1;
-      const float4 v = *reinterpret_cast<const float4*>(
-          g.ws + ((size_t)(j * 2 + which) * p.U + r) * (size_t)(BM * BN) + (size_t)rr * BN + cc);
-      acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+  float4 acc[NE];
+#pragma unroll
+  for (int it = 0; it < NE; ++it) acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = f.j0[q]; j <= f.j1[q]; ++j) {
+    if (sk_begin(p, j) == sk_begin(p, j + 1)) continue;  // an empty slot wrote nothing
+    const int which = (int)(sk_begin(p, j) / p.kI) == c ? 0 : 1;
+    const float* src = g.ws + ((size_t)(j * 2 + which) * p.U + r) * (size_t)(BM * BN) +
+                       (size_t)chunk * 32 * BN;
+    float4 v[NE];
+#pragma unroll
+    for (int it = 0; it < NE; ++it) {
+      const int e = threadIdx.x + it * 256;
+      v[it] = *reinterpret_cast<const float4*>(src + (size_t)(e / LPR) * BN + 4 * (e % LPR));
     }
-    epilogue4(g, r * BM + rr, c * BN + cc, acc, nullptr, sc);
+#pragma unroll
+    for (int it = 0; it < NE; ++it) {
+      acc[it].x += v[it].x; acc[it].y += v[it].y; acc[it].z += v[it].z; acc[it].w += v[it].w;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NE; ++it) {
+    const int e = threadIdx.x + it * 256;
+    float o[4] = {acc[it].x, acc[it].y, acc[it].z, acc[it].w};
+    epilogue4(g, r * BM + chunk * 32 + e / LPR, c * BN + 4 * (e % LPR), o, nullptr, sc);
   }
 }
 
