@@ -548,21 +548,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_dtl_kernel(GemmArgs g, 
 // ----------------------------------------------------------------------------
 // Stream-K schedule for GEMMs whose tile grid leaves the last round of
 // workgroups part empty (the 1T shard's M = 2048 GEMMs: 400 or 800 tiles on
-// 256 compute units). The work, a column of U = ceil(M / BM) output tiles
-// times kI K steps per tile column, is split evenly over S = 256 / U slots:
-// slot j takes the column K steps [j T / S, (j+1) T / S) of the
-// column-major order (T = columns * kI). The U workgroups of a slot compute
-// the U row tiles of the same column over the same K steps at the same time,
-// and sit on one XCD (workgroup w runs on XCD w mod 8), so each K step of
-// the column's B panel is fetched into that XCD's L2 once and read by all U.
-// A column a slot covers whole gets its epilogue at once; a column split
+// 256 compute units). A slot is Z = U x V workgroups on one XCD (workgroup w
+// runs on XCD w mod 8): the U = ceil(M / BM) row tiles of V adjacent tile
+// columns, a "unit" of V columns. The work, units x kI K steps, is split
+// evenly over the S = 256 / Z slots: slot j takes the unit K steps
+// [j T / S, (j+1) T / S) of the unit-major order (T = units * kI). The Z
+// workgroups of a slot compute their tiles over the same K steps at the same
+// time, so each K step of the unit's A row panels and B column panels is
+// fetched into that XCD's L2 once and read by all of them. V = 32 / U (a
+// slot is a whole XCD) shares the A panels across columns as a data-parallel
+// grid does; V = 1 leaves no column idle when the columns do not divide by
+// 32 / U. A unit a slot covers whole gets its epilogue at once; a unit split
 // between slots has each piece's raw accumulators stored in the partial
-// buffer ([S][2][U][BM][BN]: a slot's first and last columns) and
+// buffer ([S][2][Z][BM][BN]: a slot's first and last units) and
 // gemm_sk_fixup_kernel sums the pieces in slot order (deterministic) and
-// applies the epilogue. No workgroup waits for another.
+// applies the epilogue. Columns past the last one in the last unit idle. No
+// workgroup waits for another.
 // ----------------------------------------------------------------------------
 struct SkPlan {
-  int U, S, cols, kI;
+  int U, V, Z, S, cols, units, kI;
   long T;
 };
 
@@ -574,53 +578,60 @@ template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_sk_kernel(GemmArgs g, SkPlan p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int xcd = blockIdx.x % kXCDs, local = blockIdx.x / kXCDs;
-  const int per_xcd = p.S / kXCDs;  // slots per XCD (p.S = 256 / U, U divides 32)
-  const int slot = xcd * per_xcd + local / p.U, r = local % p.U;
+  const int per_xcd = p.S / kXCDs;  // slots per XCD (p.S = 256 / Z, Z divides 32)
+  const int slot = xcd * per_xcd + local / p.Z, ls = local % p.Z;
+  const int r = ls % p.U, v = ls / p.U;
   const long s0 = sk_begin(p, slot), s1 = sk_begin(p, slot + 1);
   if (s0 >= s1) return;
-  const int c_first = (int)(s0 / p.kI), c_last = (int)((s1 - 1) / p.kI);
-  for (int c = c_first; c <= c_last; ++c) {
-    const long cb = (long)c * p.kI;
-    const int k0 = (int)(max(s0, cb) - cb), k1 = (int)(min(s1, cb + p.kI) - cb);
+  const int u_first = (int)(s0 / p.kI), u_last = (int)((s1 - 1) / p.kI);
+  bool first_tile = true;
+  for (int u = u_first; u <= u_last; ++u) {
+    const int c = u * p.V + v;
+    if (c >= p.cols) continue;  // past the last column (uniform over the workgroup)
+    const long ub = (long)u * p.kI;
+    const int k0 = (int)(max(s0, ub) - ub), k1 = (int)(min(s1, ub + p.kI) - ub);
     float* pdst = nullptr;
     if (k1 - k0 < p.kI) {
-      const int which = c == c_first ? 0 : 1;
-      pdst = g.ws + ((size_t)(slot * 2 + which) * p.U + r) * (size_t)(BM * BN);
+      const int which = u == u_first ? 0 : 1;
+      pdst = g.ws + ((size_t)(slot * 2 + which) * p.Z + ls) * (size_t)(BM * BN);
     }
-    if (c != c_first) __syncthreads();  // the last epilogue's LDS reads are done
+    if (!first_tile) __syncthreads();  // the last epilogue's LDS reads are done
+    first_tile = false;
     dtl_tile<BM, BN, WM, WN, AK, BKM>(g, r * BM, c * BN, k0, k1, 0, pdst, smem);
   }
 }
 
-// Columns split between slots, and their slot range (host-computed).
+// Units split between slots, and their slot range (host-computed).
 constexpr int kSkMaxSplitCols = 64;
 struct SkFix {
   int n;
-  int col[kSkMaxSplitCols], j0[kSkMaxSplitCols], j1[kSkMaxSplitCols];
+  int col[kSkMaxSplitCols], j0[kSkMaxSplitCols], j1[kSkMaxSplitCols];  // col: the unit
 };
 
-// Sums the pieces of each split column in slot order and applies the
-// epilogue. Workgroup (q, r, chunk): rows [chunk*32, chunk*32+32) of row tile
-// r of split column q; each thread owns NE float4 positions of those rows
-// (4 consecutive columns each) and loads them from every piece before the
-// epilogue, so NE loads per piece are in flight at once.
+// Sums the pieces of each split unit in slot order and applies the
+// epilogue. Workgroup (q, ls, chunk): rows [chunk*32, chunk*32+32) of tile ls
+// (row ls % U, column unit * V + ls / U) of split unit q; each thread owns NE
+// float4 positions of those rows (4 consecutive columns each) and loads them
+// from every piece before the epilogue, so NE loads per piece are in flight.
 template <int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_sk_fixup_kernel(GemmArgs g, SkPlan p, SkFix f) {
   constexpr int RCH = BM / 32;
   constexpr int LPR = BN / 4;           // float4 per tile row
   constexpr int NE = 32 * LPR / 256;    // float4 per thread
   static_assert(32 * LPR % 256 == 0, "fix-up chunking");
-  const int q = blockIdx.x / (p.U * RCH);
-  const int r = (blockIdx.x / RCH) % p.U, chunk = blockIdx.x % RCH;
-  const int c = f.col[q];
+  const int q = blockIdx.x / (p.Z * RCH);
+  const int ls = (blockIdx.x / RCH) % p.Z, chunk = blockIdx.x % RCH;
+  const int r = ls % p.U, u = f.col[q];
+  const int c = u * p.V + ls / p.U;
+  if (c >= p.cols) return;  // an idle column: no pieces
   const float sc = g.scale ? g.scale[0] : 1.f;
   float4 acc[NE];
 #pragma unroll
   for (int it = 0; it < NE; ++it) acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = f.j0[q]; j <= f.j1[q]; ++j) {
     if (sk_begin(p, j) == sk_begin(p, j + 1)) continue;  // an empty slot wrote nothing
-    const int which = (int)(sk_begin(p, j) / p.kI) == c ? 0 : 1;
-    const float* src = g.ws + ((size_t)(j * 2 + which) * p.U + r) * (size_t)(BM * BN) +
+    const int which = (int)(sk_begin(p, j) / p.kI) == u ? 0 : 1;
+    const float* src = g.ws + ((size_t)(j * 2 + which) * p.Z + ls) * (size_t)(BM * BN) +
                        (size_t)chunk * 32 * BN;
     float4 v[NE];
 #pragma unroll
@@ -818,54 +829,62 @@ int gemm_choose_split(const GemmArgs& g) {
 }
 
 // ---- stream-K planning --------------------------------------------------------
-// Rows of tiles per slot and slots: U must divide the 32 CUs of an XCD.
-static bool sk_shape(const GemmArgs& g, const TileCfg& t, SkPlan* p) {
+// Slot shape for tile t: U = the row tiles (must divide the 32 CUs of an
+// XCD), V columns per unit (V = 1, or 32 / U with `wide`).
+static bool sk_shape(const GemmArgs& g, const TileCfg& t, int wide, SkPlan* p) {
   const long U = ceil_div(g.M, t.bm);
   if (t.per_cu != 1 || U > 32 || (32 % U) != 0) return false;
   p->U = (int)U;
-  p->S = kCUs / (int)U;
+  p->V = wide ? 32 / (int)U : 1;
+  p->Z = p->U * p->V;
+  p->S = kCUs / p->Z;
   p->cols = (int)ceil_div(g.N, t.bn);
+  p->units = (int)ceil_div(p->cols, p->V);
   p->kI = g.K / 64;
-  p->T = (long)p->cols * p->kI;
+  p->T = (long)p->units * p->kI;
   return true;
 }
 
-// The slot whose K-step range holds column K step i: the largest j with
+// The slot whose K-step range holds unit K step i: the largest j with
 // j T / S <= i (empty slots, possible only when T < S, are skipped this way).
 static int sk_slot_of(const SkPlan& p, long i) {
   return (int)(((i + 1) * p.S + p.T - 1) / p.T) - 1;
 }
 
-// The split columns and, for each, the first and last slot covering it.
+// The split units and, for each, the first and last slot covering it.
 static void sk_fix(const SkPlan& p, SkFix* f) {
   f->n = 0;
   for (int j = 1; j < p.S; ++j) {
     const long b = (long)j * p.T / p.S;  // slot j starts here
-    if (b % p.kI == 0 || b >= p.T) continue;  // on a column edge: nothing split there
-    const int c = (int)(b / p.kI);
-    if (f->n && f->col[f->n - 1] == c) continue;
+    if (b % p.kI == 0 || b >= p.T) continue;  // on a unit edge: nothing split there
+    const int u = (int)(b / p.kI);
+    if (f->n && f->col[f->n - 1] == u) continue;
     if (f->n == kSkMaxSplitCols) {  // too many to list: the caller rejects the plan
       f->n = kSkMaxSplitCols + 1;
       return;
     }
-    f->col[f->n] = c;
-    f->j0[f->n] = sk_slot_of(p, (long)c * p.kI);
-    f->j1[f->n] = sk_slot_of(p, (long)(c + 1) * p.kI - 1);
+    f->col[f->n] = u;
+    f->j0[f->n] = sk_slot_of(p, (long)u * p.kI);
+    f->j1[f->n] = sk_slot_of(p, (long)(u + 1) * p.kI - 1);
     ++f->n;
   }
 }
 
+// Modelled seconds: the slot's K steps, plus the pieces (at most two per
+// slot and tile, written then read). Single-column units (V = 1) pay about 5 %
+// per K step for fetching the A panels once per slot rather than once per XCD
+// (the 1T shard's M = 2048 GEMMs).
 static double sk_cost(const TileCfg& t, const SkPlan& p) {
   const long iters = ceil_div(p.T, p.S);
-  const double mac = (double)iters * t.bm * t.bn * 64 / t.eff;
-  // at most two pieces per slot and row tile, written then read
-  const double part = 2.0 * 2.0 * p.S * p.U * (double)t.bm * t.bn * 4;
+  const double shared = p.V == 1 && p.U < 32 ? 1.05 : 1.0;
+  const double mac = (double)iters * t.bm * t.bn * 64 / t.eff * shared;
+  const double part = 2.0 * 2.0 * p.S * p.Z * (double)t.bm * t.bn * 4;
   return mac / kMacPerCU + part / kPartialBW + kLaunch;
 }
 
-// Whether g runs stream-K (and on which tile): K a whole number of long
-// enough K steps, no split-K, a partial buffer, and a modelled time at
-// least 3 % below the best data-parallel grid's.
+// Whether g runs stream-K (and on which tile and slot shape): K a whole
+// number of long enough K steps, no split-K, a partial buffer, and a
+// modelled time at least 3 % below the best data-parallel grid's.
 static bool sk_choose(const GemmArgs& g, TileCfg* tile, SkPlan* plan, bool need_ws) {
   if (g.math != DT_F16 || g.split > 1 || g.K % 64 || g.K / 64 < 128) return false;
   if (need_ws && !g.ws) return false;
@@ -874,19 +893,21 @@ static bool sk_choose(const GemmArgs& g, TileCfg* tile, SkPlan* plan, bool need_
   bool found = false;
   double best = dp_cost * 0.97;
   for (const TileCfg& t : {kBig, kWide}) {
-    SkPlan p;
-    if (!sk_shape(g, t, &p)) continue;
-    const size_t need = (size_t)p.S * 2 * p.U * t.bm * t.bn;
-    if (need_ws && need > g.ws_floats) continue;
-    SkFix f;
-    sk_fix(p, &f);
-    if (f.n > kSkMaxSplitCols) continue;
-    const double c = sk_cost(t, p);
-    if (c < best) {
-      best = c;
-      *tile = t;
-      *plan = p;
-      found = true;
+    for (int wide = 0; wide < 2; ++wide) {
+      SkPlan p;
+      if (!sk_shape(g, t, wide, &p)) continue;
+      const size_t need = (size_t)p.S * 2 * p.Z * t.bm * t.bn;
+      if (need_ws && need > g.ws_floats) continue;
+      SkFix f;
+      sk_fix(p, &f);
+      if (f.n > kSkMaxSplitCols) continue;
+      const double c = sk_cost(t, p);
+      if (c < best) {
+        best = c;
+        *tile = t;
+        *plan = p;
+        found = true;
+      }
     }
   }
   return found;
@@ -901,7 +922,7 @@ size_t gemm_ws_floats(const GemmArgs& g) {
   }
   TileCfg t;
   SkPlan p;
-  if (sk_choose(g, &t, &p, false)) need = std::max(need, (size_t)p.S * 2 * p.U * t.bm * t.bn);
+  if (sk_choose(g, &t, &p, false)) need = std::max(need, (size_t)p.S * 2 * p.Z * t.bm * t.bn);
   return need;
 }
 
@@ -944,10 +965,10 @@ static hipError_t launch_f16(const GemmArgs& g, int split, hipStream_t s,
     sk_fix(*sk, &f);
     GemmArgs a = g;
     a.split = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(sk->S * sk->U)), dim3(NT), lds, s, a, *sk);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(sk->S * sk->Z)), dim3(NT), lds, s, a, *sk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || f.n == 0) return e;
-    hipLaunchKernelGGL((gemm_sk_fixup_kernel<BM, BN>), dim3((unsigned)(f.n * sk->U * (BM / 32))),
+    hipLaunchKernelGGL((gemm_sk_fixup_kernel<BM, BN>), dim3((unsigned)(f.n * sk->Z * (BM / 32))),
                        dim3(256), 0, s, a, *sk, f);
     return hipGetLastError();
   }
