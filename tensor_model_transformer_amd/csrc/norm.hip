@@ -20,8 +20,14 @@ template <> struct DtOf<f16> { static constexpr int v = DT_F16; };
 // ----------------------------------------------------------------------------
 // LayerNorm forward: one workgroup per row, the row held in registers.
 // ----------------------------------------------------------------------------
+// Rows of 1024 threads x 4 vectors (hidden above 16384, 16-bit output) fit
+// in 64 VGPRs without spilling, so two workgroups share a compute unit and
+// one's reductions overlap the other's loads and stores.
+template <typename To, int NT, int NV>
+constexpr int kLnFwdWaves = (NT == 1024 && NV == 4 && sizeof(To) == 2) ? 8 : 1;
+
 template <typename Tin, typename T, typename To, int NT, int NV>
-__global__ __launch_bounds__(NT) void ln_fwd_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kLnFwdWaves<To, NT, NV>))) void ln_fwd_kernel(
     const Tin* __restrict__ x, const T* __restrict__ gamma, const T* __restrict__ beta,
     To* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out,
     float* __restrict__ x_copy, int h, float eps) {
