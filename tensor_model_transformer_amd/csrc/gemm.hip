@@ -883,10 +883,15 @@ static double sk_cost(const TileCfg& t, const SkPlan& p) {
 }
 
 // Whether g runs stream-K (and on which tile and slot shape): K a whole
-// number of long enough K steps, no split-K, a partial buffer, and a
-// modelled time at least 3 % below the best data-parallel grid's.
+// number of long enough K steps (at least 128; 32 when M spans at most 8 row
+// tiles, where a data-parallel grid's rounds are coarsest: the 1T shard's
+// output projection, K = 3200, measured 444 -> 420 us, while shapes of 32
+// row tiles gained nothing), no split-K, a partial buffer, and a modelled
+// time at least 3 % below the best data-parallel grid's.
 static bool sk_choose(const GemmArgs& g, TileCfg* tile, SkPlan* plan, bool need_ws) {
-  if (g.math != DT_F16 || g.split > 1 || g.K % 64 || g.K / 64 < 128) return false;
+  if (g.math != DT_F16 || g.split > 1 || g.K % 64) return false;
+  const long ksteps = g.K / 64;
+  if (ksteps < 32 || (ksteps < 128 && ceil_div(g.M, 256) > 8)) return false;
   if (need_ws && !g.ws) return false;
   const TileCfg dp = choose_tile(g.M, g.N, 1);
   const double dp_cost = tile_cost(dp, g.M, g.N, 1) * (double)g.K / kMacPerCU;

@@ -324,6 +324,9 @@ STREAM_K = [
     Workload("sk_h8192_padding", LayerDims(2, 160, 8192, 64, 16384, t=8, dtype="bf16",
                                            mask="padding"), rank=5, seed=42, affine="perturbed",
              len_range=(40, 160)),
+    # M within 8 row tiles and K of 2048..6144: stream-K below 128 K steps
+    Workload("sk_h4096_t2_causal", LayerDims(1, 136, 4096, 32, 8192, t=2, dtype="bf16",
+                                             mask="causal"), rank=1, seed=43, affine="perturbed"),
 ]
 
 
