@@ -33,17 +33,15 @@ __device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
   f16x2 h = {(f16)lo, (f16)hi};
   return __builtin_bit_cast(uint32_t, h);
 }
-// 8 bf16 values to 8 fp16 values. Every normal bf16 value inside the fp16
-// range is exactly representable, so the rounding mode only matters for
-// values below fp16's normal range (absolute error < 2^-24).
+// 8 bf16 values to 8 fp16 values, rounded to nearest even as the weight
+// copies of the training path are. Every normal bf16 value inside the fp16
+// range is exactly representable; values beyond 65504 become infinite (a
+// weight outside fp16's range shows as a non-finite result, never as a
+// saturated finite one), values below the normal range round to subnormals.
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16),
-                                        __uint_as_float(w[i] & 0xffff0000u));
-    w[i] = __builtin_bit_cast(uint32_t, h);
-  }
+  for (int i = 0; i < 4; ++i) w[i] = pack2h(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xffff0000u));
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 

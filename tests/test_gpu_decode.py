@@ -30,9 +30,11 @@ def _wl(name, batch, hidden, heads, ffn, t=1, dtype="bf16", seed=60, rank=0, seq
                                     mask="causal"), rank=rank, seed=seed, affine="perturbed")
 
 
-def run_decode(w, cache_len, positions="ragged", scores=0, rank=None, gelu="erf", eps=1e-5):
+def run_decode(w, cache_len, positions="ragged", scores=0, rank=None, gelu="erf", eps=1e-5,
+               params=None):
     """One TP_ALL decode step of one rank on the GPU. Returns numpy results
-    and the inputs it used."""
+    and the inputs it used. `params` replaces the rank's generated
+    parameters (values on the storage grid)."""
     import torch
     from tensor_model_transformer_amd.shard import Shard, _check
 
@@ -43,7 +45,7 @@ def run_decode(w, cache_len, positions="ragged", scores=0, rank=None, gelu="erf"
     from tensor_model_transformer_amd import binding as B
     sh = Shard(d, r, scores=scores, eps=eps,
                gelu=B.TP_GELU_TANH if gelu == "tanh" else B.TP_GELU_ERF)
-    p = sh.upload_params(rank_params(w, r))
+    p = sh.upload_params(rank_params(w, r) if params is None else params)
     xd = torch.from_numpy(x).to(sh.device).to(sh.dtype)
     kd, vd = sh.upload_cache(kc), sh.upload_cache(vc)
     klo = torch.zeros_like(kd) if sh.split_scores else None
@@ -121,6 +123,20 @@ def test_decode_gelu_tanh_and_eps(dtype):
     rep = compare_decode(w, gpu, inputs, TAU[dtype], gelu="tanh", eps=1e-3)
     print(f"[decode] {w.name}: {fmt(rep)}", flush=True)
     assert all(v <= TAU[dtype] for v in rep.values()), fmt(rep)
+
+
+def test_decode_weights_beyond_fp16_are_not_silent():
+    # The GEMVs read the bf16 weights as fp16 operands. A weight beyond fp16's
+    # largest finite value (65504) must come out as a non-finite result, as in
+    # the training path, not as a finite value saturated at 65504.
+    _need_gpu()
+    w = _wl("dec_range_bf16", 3, 384, 4, 768, dtype="bf16", seed=62)
+    p = dict(rank_params(w, w.rank))
+    m = np.array(p["w_o"], copy=True)
+    m[:, 5] = np.float32(99840.0)  # 1e5 on the bf16 grid
+    p["w_o"] = m
+    gpu, _ = run_decode(w, 40, "ragged", params=p)
+    assert not np.all(np.isfinite(gpu["out"]))
 
 
 def test_decode_is_deterministic():
