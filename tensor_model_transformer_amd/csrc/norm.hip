@@ -100,6 +100,66 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kLnFwdWaves<
   }
 }
 
+// LayerNorm forward for rows of at most 4096 elements: one wave per row,
+// the row in registers (NV 8-wide vectors per lane), both reductions by
+// cross-lane shuffles, so no LDS round trip and no barrier; four rows per
+// 256-thread workgroup. Same arithmetic per element as ln_fwd_kernel (the
+// sums are taken in another order).
+template <typename Tin, typename T, typename To, int NV>
+__global__ __launch_bounds__(256) void ln_fwd_wave_kernel(
+    const Tin* __restrict__ x, const T* __restrict__ gamma, const T* __restrict__ beta,
+    To* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out,
+    float* __restrict__ x_copy, int rows, int h, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // uniform over the wave; no barrier follows
+  const int nvec = h >> 3;
+  const Tin* xr = x + (size_t)row * h;
+  float v[NV][8];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nvec) {
+      Vec8<Tin>::load(xr + 8 * j, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[i][e];
+    }
+  }
+  const float mu = wave_sum(s) / (float)h;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i < nvec) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[i][e] - mu;
+        sq += d * d;
+      }
+    }
+  }
+  const float rstd = 1.f / sqrtf(wave_sum(sq) / (float)h + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = lane + 64 * i;
+    if (j < nvec) {
+      // gamma and beta (the same for every row, so cached) load after the
+      // reductions: the registers go to more waves per SIMD instead
+      float g[8], b[8], o[8];
+      Vec8<T>::load(gamma + 8 * j, g);
+      Vec8<T>::load(beta + 8 * j, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = g[e] * ((v[i][e] - mu) * rstd) + b[e];
+      Vec8<To>::store(y + (size_t)row * h + 8 * j, o);
+      if (x_copy) Vec8<float>::store(x_copy + (size_t)row * h + 8 * j, v[i]);
+    }
+  }
+  if (lane == 0 && mean_out) {
+    mean_out[row] = mu;
+    rstd_out[row] = rstd;
+  }
+}
+
 // Threads per row and 8-wide vectors per thread for a row of h elements.
 static bool row_config(int h, int* nt, int* nv) {
   const int nvec = h / 8;
@@ -119,6 +179,21 @@ static hipError_t ln_fwd_t(const void* x, const void* gamma, const void* beta, v
   int nt, nv;
   if (!row_config(h, &nt, &nv)) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
+  // rows of at most 4096 elements: a wave per row (vectors per lane: the
+  // smallest instantiated count covering the row)
+  const int wv = (h / 8 + 63) / 64;
+  if (wv <= 8) {
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+#define TPL_LNW(NV_)                                                                       \
+  if (wv <= NV_) {                                                                         \
+    ln_fwd_wave_kernel<Tin, T, To, NV_><<<grid, 256, 0, s>>>(                              \
+        (const Tin*)x, (const T*)gamma, (const T*)beta, (To*)y, mean, rstd, x_copy, rows,  \
+        h, eps);                                                                           \
+    return hipGetLastError();                                                              \
+  }
+    TPL_LNW(1) TPL_LNW(2) TPL_LNW(3) TPL_LNW(4) TPL_LNW(6) TPL_LNW(8)
+#undef TPL_LNW
+  }
 #define TPL_LNF(NT_, NV_)                                                                   \
   if (nt == NT_ && nv == NV_) {                                                             \
     ln_fwd_kernel<Tin, T, To, NT_, NV_><<<rows, NT_, 0, s>>>(                               \
