@@ -748,6 +748,25 @@ __global__ __launch_bounds__(256) void to_f16_kernel(CvtSegs c) {
   }
 }
 
+// The unscaled copies (the weights): one 8-element vector per thread and a
+// grid covering every vector, so each thread has one load and one store in
+// flight and no workgroup loops (a grid-stride loop over a capped grid ran
+// these copies at 5.15 TB/s where a plain fp32 copy reaches 5.8).
+__global__ __launch_bounds__(256) void to_f16_flat_kernel(CvtSegs c) {
+  const size_t v = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= c.start[c.nseg]) return;
+  int sg = 0;
+  while (sg + 1 < c.nseg && v >= c.start[sg + 1]) ++sg;
+  const size_t i = 8 * (v - c.start[sg]);
+  if (i + 8 <= c.n[sg]) {
+    float f[8];
+    Vec8<bf16>::load(c.src[sg] + i, f);
+    Vec8<f16>::store(c.dst[sg] + i, f);
+  } else {
+    for (size_t e = i; e < c.n[sg]; ++e) c.dst[sg][e] = (f16)bf2f(c.src[sg][e]);
+  }
+}
+
 hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
                   hipStream_t s, float* amax_part, float* scale_out) {
   if (nseg < 1 || nseg > 4) return hipErrorInvalidValue;
@@ -773,6 +792,10 @@ hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count,
   }
   const size_t total = c.start[nseg];
   if (!total && !amax_part) return hipSuccess;  // (with a scale, one block still writes it)
+  if (!amax_part) {
+    to_f16_flat_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(c);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)std::max<size_t>(1, std::min<size_t>((total + 255) / 256, 8192));
   to_f16_kernel<<<grid, 256, 0, s>>>(c);
   return hipGetLastError();
