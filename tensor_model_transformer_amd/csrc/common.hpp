@@ -142,6 +142,13 @@ __device__ __forceinline__ void load4_dt(const void* base, int dt, size_t off, f
   else if (dt == 1) Vec4<bf16>::load((const bf16*)base + off, v);
   else Vec4<f16>::load((const f16*)base + off, v);
 }
+// Four fp32 values with a non-temporal (streaming) vector store.
+__device__ __forceinline__ void store4_f32_nt(float* p, const float v[4]) {
+  typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+  const f32x4_nt q = {v[0], v[1], v[2], v[3]};
+  __builtin_nontemporal_store(q, reinterpret_cast<f32x4_nt*>(p));
+}
+
 __device__ __forceinline__ void store4_dt(void* base, int dt, size_t off, const float v[4]) {
   if (dt == 0) Vec4<float>::store((float*)base + off, v);
   else if (dt == 1) Vec4<bf16>::store((bf16*)base + off, v);

@@ -99,7 +99,8 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, float
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] += o[e];
   }
-  store4_dt(g.C, g.c_dtype, off, v);
+  if (g.stream_out && g.c_dtype == DT_F32) store4_f32_nt((float*)g.C + off, v);
+  else store4_dt(g.C, g.c_dtype, off, v);
 }
 
 // Output tile of this workgroup. Workgroups are dealt to the 8 XCDs round
@@ -746,7 +747,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += v[e];
   }
-  Vec4<float>::store(c, acc);
+  if (g.stream_out) store4_f32_nt(c, acc);
+  else Vec4<float>::store(c, acc);
 }
 
 // ----------------------------------------------------------------------------

@@ -109,6 +109,10 @@ struct GemmArgs {
   // acc, before bias and residual): undoes the power-of-two scaling of the
   // backward's fp16 gradient chain in the GEMMs that leave it
   const float* scale;
+  // fp32 C written with non-temporal (streaming) stores: for outputs that no
+  // later kernel of the step reads (the weight gradients), so the writes do
+  // not displace operands from the caches
+  int stream_out;
 };
 hipError_t gemm(const GemmArgs& g, hipStream_t s);
 // Split-K factor the launcher would pick for a weight-gradient GEMM g.

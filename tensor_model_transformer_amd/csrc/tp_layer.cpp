@@ -137,6 +137,7 @@ GemmArgs wgrad_args(const tp_layer* L, int M, int N, const void* X, const void* 
   g.ldc = N;
   g.c_dtype = DT_F32;
   g.accumulate = accumulate;
+  g.stream_out = 1;  // the caller's gradient: no later kernel of the step reads it
   return g;
 }
 
