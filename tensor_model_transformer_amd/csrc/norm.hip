@@ -759,9 +759,16 @@ __global__ __launch_bounds__(256) void to_f16_flat_kernel(CvtSegs c) {
   while (sg + 1 < c.nseg && v >= c.start[sg + 1]) ++sg;
   const size_t i = 8 * (v - c.start[sg]);
   if (i + 8 <= c.n[sg]) {
-    float f[8];
-    Vec8<bf16>::load(c.src[sg] + i, f);
-    Vec8<f16>::store(c.dst[sg] + i, f);
+    // the bf16 source is read once and the copy is far larger than the
+    // caches: both sides stream (non-temporal), which leaves the LayerNorm
+    // input that follows in the last-level cache (1T shard: LN forward
+    // 125 -> 109 us, the copies themselves within 1 %)
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c.src[sg] + i));
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack2h(__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xffff0000u));
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(c.dst[sg] + i));
   } else {
     for (size_t e = i; e < c.n[sg]; ++e) c.dst[sg][e] = (f16)bf2f(c.src[sg][e]);
   }
