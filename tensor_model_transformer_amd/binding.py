@@ -31,6 +31,7 @@ ERROR_NAMES = {0: "TP_OK", -1: "TP_ERR_ARG", -2: "TP_ERR_SHAPE", -3: "TP_ERR_UNS
 TP_DTYPE_F32, TP_DTYPE_BF16 = 0, 1
 TP_SCORES_AUTO, TP_SCORES_FP16, TP_SCORES_SPLIT = 0, 1, 2
 TP_RECOMPUTE_NONE, TP_RECOMPUTE_FC1 = 0, 1
+TP_OVERLAP_AUTO, TP_OVERLAP_OFF, TP_OVERLAP_ON = 0, 1, 2
 TP_FWD_SP_LN1, TP_FWD_SP_ATTN, TP_FWD_SP_LN2, TP_FWD_SP_MLP, TP_FWD_SP_OUT = 3, 4, 5, 6, 7
 TP_BWD_SP_MLP, TP_BWD_SP_LN2, TP_BWD_SP_ATTN, TP_BWD_SP_LN1 = 4, 5, 6, 7
 TP_MASK_CAUSAL, TP_MASK_PADDING = 0, 1
@@ -55,7 +56,7 @@ KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce", "conve
 
 class tp_layer_opts(Structure):
     _fields_ = [("ln_eps", c_float), ("gelu", c_int), ("dx_dtype", c_int), ("scores", c_int),
-                ("recompute", c_int), ("sequence_parallel", c_int)]
+                ("recompute", c_int), ("sequence_parallel", c_int), ("overlap_wgrad", c_int)]
 
 
 class tp_params(Structure):
@@ -138,7 +139,8 @@ def tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, 
                                        int(opts.get("dx_dtype", TP_DTYPE_F32)),
                                        int(opts.get("scores", TP_SCORES_AUTO)),
                                        int(opts.get("recompute", TP_RECOMPUTE_NONE)),
-                                       int(opts.get("sequence_parallel", 0))))
+                                       int(opts.get("sequence_parallel", 0)),
+                                       int(opts.get("overlap_wgrad", TP_OVERLAP_AUTO))))
     rc = lib().tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, o,
                                ctypes.byref(h), ctypes.byref(ws))
     return rc, h.value, ws.value

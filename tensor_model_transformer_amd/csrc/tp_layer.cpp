@@ -32,6 +32,10 @@ constexpr size_t kAlign = 256;
 // moves softmax outputs by several tenths of a percent, visible in the
 // gradient of W_qkv; at hidden <= 3072 the spread is about 1.
 constexpr int kSplitScoresHidden = 8192;
+// opts.overlap_wgrad = TP_OVERLAP_AUTO overlaps from this width (measured:
+// the 1T shard's backward 0.2-0.5 % faster with the overlap, the narrower
+// shards' 0.3-3 % slower).
+constexpr int kOverlapHidden = 8192;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -99,6 +103,7 @@ struct tp_layer {
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   bool side_tried = false;
+  bool overlap_wgrad = false;  // weight gradients on the side stream (opts)
   // decode (one row per sequence): its own workspace plan
   struct Dec {
     Region a, apart, o, h_mid, c, z, gpart;
@@ -369,10 +374,12 @@ int run_gemm(tp_layer* L, GemmArgs g, hipStream_t s, void* ws, bool wgrad = fals
   return TP_OK;
 }
 
-// The side stream (created on first use), or the caller's stream if none or
-// while profiling (each event pair then brackets its launch group alone).
+// The side stream (created on first use) when the handle overlaps the weight
+// gradients (opts.overlap_wgrad), else the caller's stream; also the caller's
+// stream while profiling (each event pair then brackets its launch group
+// alone) or if the side stream could not be created.
 hipStream_t side_stream(tp_layer* L, hipStream_t s) {
-  if (L->prof.on) return s;
+  if (L->prof.on || !L->overlap_wgrad) return s;
   if (!L->side_tried) {
     L->side_tried = true;
     hipStream_t st = nullptr;
@@ -948,6 +955,7 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   int scores = TP_SCORES_AUTO;
   int recompute = TP_RECOMPUTE_NONE;
   int seq_par = 0;
+  int overlap = TP_OVERLAP_AUTO;
   if (opts) {
     eps = opts->ln_eps;
     gelu = opts->gelu;
@@ -955,6 +963,7 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
     scores = opts->scores;
     recompute = opts->recompute;
     seq_par = opts->sequence_parallel;
+    overlap = opts->overlap_wgrad;
     if (!(eps > 0.f)) return TP_ERR_ARG;
     if (gelu != TP_GELU_ERF && gelu != TP_GELU_TANH) return TP_ERR_UNSUPPORTED;
     if (dx_dtype != TP_DTYPE_F32 && dx_dtype != dtype) return TP_ERR_UNSUPPORTED;
@@ -964,6 +973,8 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
     if (recompute != TP_RECOMPUTE_NONE && recompute != TP_RECOMPUTE_FC1) return TP_ERR_UNSUPPORTED;
     if (seq_par != 0 && seq_par != 1) return TP_ERR_UNSUPPORTED;
     if (seq_par && n % t) return TP_ERR_SHAPE;
+    if (overlap != TP_OVERLAP_AUTO && overlap != TP_OVERLAP_OFF && overlap != TP_OVERLAP_ON)
+      return TP_ERR_UNSUPPORTED;
   }
   tp_layer* L = new (std::nothrow) tp_layer();
   if (!L) return TP_ERR_NOMEM;
@@ -973,6 +984,8 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   L->dx_f32 = dx_dtype == TP_DTYPE_F32;
   L->recompute_fc1 = recompute == TP_RECOMPUTE_FC1;
   L->sp = seq_par == 1;
+  L->overlap_wgrad = overlap == TP_OVERLAP_ON ||
+                     (overlap == TP_OVERLAP_AUTO && hidden >= kOverlapHidden);
   L->nc = (int)(n / t);
   L->split_scores = dtype == TP_DTYPE_BF16 &&
                     (scores == TP_SCORES_SPLIT ||

@@ -124,6 +124,21 @@ def test_recompute_fc1_is_bitwise_equal(w):
         assert np.array_equal(a["grads"][k], b["grads"][k]), k
 
 
+@pytest.mark.parametrize("w", [SMALL_BF16[0], SMALL_BF16[4]], ids=lambda w: w.name)
+def test_overlap_wgrad_is_bitwise_equal(w):
+    # opts.overlap_wgrad = TP_OVERLAP_ON runs the weight and bias gradients
+    # on the handle's second stream: the same kernels on the same inputs, so
+    # every result is bitwise unchanged, also when the gradients accumulate
+    _need_gpu()
+    from tensor_model_transformer_amd import binding as B
+    for twice in (False, True):
+        a = run_gpu_local(w, accumulate_twice=twice, overlap_wgrad=B.TP_OVERLAP_OFF)
+        b = run_gpu_local(w, accumulate_twice=twice, overlap_wgrad=B.TP_OVERLAP_ON)
+        assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["dx"], b["dx"])
+        for k in a["grads"]:
+            assert np.array_equal(a["grads"][k], b["grads"][k]), (k, twice)
+
+
 def test_recompute_fc1_fp32_parity():
     _need_gpu()
     from tensor_model_transformer_amd import binding as B
@@ -164,19 +179,20 @@ def test_accumulate_adds_gradients():
         assert err_ratio(g, 2.0 * ref["grads"][k]) <= TAU["bf16"], k
 
 
-def test_graph_replay_matches_eager():
-    """Forward + backward (TP_ALL) captured in a HIP graph on a side stream:
-    the backward's second stream joins the capture through its fork/join
-    events. Every replay, with eager work in between, reproduces the eager
-    outputs and gradients bit for bit."""
+@pytest.mark.parametrize("overlap", [1, 2], ids=["serial", "overlap"])
+def test_graph_replay_matches_eager(overlap):
+    """Forward + backward (TP_ALL) captured in a HIP graph on a side stream;
+    with TP_OVERLAP_ON the backward's second stream joins the capture
+    through its fork/join events. Every replay, with eager work in between,
+    reproduces the eager outputs and gradients bit for bit."""
     _need_gpu()
     import torch
     from tensor_model_transformer_amd.shard import Shard, _check
     w = SMALL_BF16[0]
     d = w.dims
-    print(f"\n[graph] {w.name} dims={d}", flush=True)
+    print(f"\n[graph] {w.name} dims={d} overlap={overlap}", flush=True)
     x, dout, vl = layer_inputs(w)
-    sh = Shard(d, 0)
+    sh = Shard(d, 0, overlap_wgrad=overlap)
     p = sh.upload_params(rank_params(w, 0), vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()
