@@ -190,16 +190,18 @@ typedef struct {
   int sequence_parallel;  /* 0 (default) or 1: the TP_*_SP_* phases below */
   int overlap_wgrad;      /* TP_OVERLAP_AUTO (default, also a zeroed struct),
                              TP_OVERLAP_OFF or TP_OVERLAP_ON: whether the
-                             backward runs the weight and bias gradients on a
-                             second stream of the handle, overlapping the
-                             data-gradient chain (each phase joins it before
-                             returning), or every kernel on the caller's
-                             stream. Results are bitwise identical. AUTO
-                             overlaps from hidden >= 8192: on one MI355X the
-                             overlap measured 0.2-0.5 % faster on the 1T shard
-                             and 0.3-3 % slower on the 1.2B, 8.3B and BERT
-                             shards, where the overlapped GEMMs compete for
-                             the same compute units. */
+                             backward computes the gradient of W_o on a second
+                             stream of the handle while dO and the attention
+                             backward run on the caller's stream (the phase
+                             joins it before returning), or every kernel on
+                             the caller's stream. Results are bitwise
+                             identical. AUTO overlaps from hidden >= 8192: on
+                             one MI355X the overlap measured about 1 % faster
+                             on the 1T shard and 0.2-0.4 % slower on the 1.2B
+                             and 8.3B shards. (Overlapping the other weight
+                             gradients with the data-gradient GEMMs measured
+                             slower everywhere: the GEMMs compete for the same
+                             compute units.) */
 } tp_layer_opts;
 
 /* Parameters of rank r (shapes above) and, for TP_MASK_PADDING, the number

@@ -33,8 +33,8 @@ constexpr size_t kAlign = 256;
 // gradient of W_qkv; at hidden <= 3072 the spread is about 1.
 constexpr int kSplitScoresHidden = 8192;
 // opts.overlap_wgrad = TP_OVERLAP_AUTO overlaps from this width (measured:
-// the 1T shard's backward 0.2-0.5 % faster with the overlap, the narrower
-// shards' 0.3-3 % slower).
+// the 1T shard's step about 1 % faster with the overlap, the 1.2B and 8.3B
+// shards' 0.2-0.4 % slower).
 constexpr int kOverlapHidden = 8192;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -78,7 +78,8 @@ struct tp_layer {
   // stream-K pieces of the GEMMs on the caller's stream (forward, data
   // gradients); splitk holds the weight gradients' split-K partials
   Region skp;
-  // column-sum partials of the bias gradients that run on the side stream
+  // column-sum partials of the bias gradients (apart from the LayerNorm
+  // backward's, which a bias gradient may follow in the same phase)
   Region part2;
   // fp16 copies of the bf16 weights (made by the forward, read again by the
   // backward) and of the upstream gradient: the MFMA GEMMs read fp16 only
@@ -542,7 +543,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
 
 // ---- backward pieces -------------------------------------------------------
 // Bias gradient: out (+)= column sums of y [n, cols] (two-stage, deterministic).
-// Bias gradient (column sums of y) on the side stream, with its own partials.
+// Bias gradient (column sums of y), with its own partials.
 int bias_grad(tp_layer* L, const void* y, int y_dtype, int cols, float* out, int accumulate,
               void* ws, hipStream_t s, int rows = -1, const float* scale = nullptr) {
   if (rows < 0) rows = L->n;
@@ -608,14 +609,12 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   // du = (dout @ W_fc2,r^T) * GeLU'(u), GeLU'(u) kept by the forward (in the
   // u buffer) or recomputed into the du buffer, then overwritten in place
   // (each element is read, then written, by the same thread of the epilogue)
-  // side stream: db2 and dW2 (need only dout and z) while du is computed
-  hipStream_t sd = side_stream(L, s);
-  if ((e = fork_to(L, s, sd))) return e;
-  if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, sd, db2_rows)))
+  // db2 and dW2 (need only dout and z)
+  if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s, db2_rows)))
     return e;
   g = wgrad_args(L, fl, h, at<void>(ws, L->z), dout, io->d_w_fc2, io->accumulate);
   g.split = L->split_w2; g.scale = unscale;
-  if ((e = run_gemm(L, g, sd, ws, true))) return e;
+  if ((e = run_gemm(L, g, s, ws, true))) return e;
   g = gemm_base(L);
   g.M = n; g.N = fl; g.K = h;
   g.A = dout; g.lda = h; g.a_kmajor = 1;
@@ -624,12 +623,11 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   g.aux = at<void>(ws, L->recompute_fc1 ? L->du : L->u); g.ldaux = fl;
   g.C = at<void>(ws, L->du); g.ldc = fl;
   if ((e = run_gemm(L, g, s, ws))) return e;
-  // side stream: dW1 and db1 (need du) while dc is computed
-  if ((e = fork_to(L, s, sd))) return e;
+  // dW1 and db1 (need du)
   g = wgrad_args(L, h, fl, c_act, at<void>(ws, L->du), io->d_w_fc1, io->accumulate);
   g.split = L->split_w1; g.scale = unscale;
-  if ((e = run_gemm(L, g, sd, ws, true))) return e;
-  if ((e = bias_grad(L, at<void>(ws, L->du), L->adt, fl, io->d_b_fc1, io->accumulate, ws, sd, -1,
+  if ((e = run_gemm(L, g, s, ws, true))) return e;
+  if ((e = bias_grad(L, at<void>(ws, L->du), L->adt, fl, io->d_b_fc1, io->accumulate, ws, s, -1,
                      unscale)))
     return e;
   g = gemm_base(L);
@@ -637,8 +635,7 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   g.A = at<void>(ws, L->du); g.lda = fl; g.a_kmajor = 1;
   g.B = wmat(L, ws, L->w16_fc1, p->w_fc1); g.ldb = fl; g.b_kmajor = 1;
   g.C = dc_out; g.ldc = h; g.c_dtype = DT_F32; g.scale = unscale;
-  if ((e = run_gemm(L, g, s, ws))) return e;
-  return join_from(L, s, sd);
+  return run_gemm(L, g, s, ws);
 }
 
 // dc (summed) -> dh, LN2 grads, db_o -> dW_o, do -> attention -> dqkv ->
@@ -661,7 +658,9 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
     return e;
   const void* dh_s = dh_in ? dh_in : at<void>(ws, L->dh_s);
   const void* a_act = a_in ? a_in : at<void>(ws, L->a);
-  // side stream: dW_o (needs dh) during the attention backward
+  // dW_o (needs dh) on the side stream, when the handle overlaps, during dO
+  // and the attention backward: the one pairing where the overlap measured
+  // faster (the attention kernels leave compute units idle that the GEMM fills)
   hipStream_t sd = side_stream(L, s);
   if ((e = fork_to(L, s, sd))) return e;
   GemmArgs g = wgrad_args(L, hl, h, at<void>(ws, L->o), dh_s, io->d_w_o, io->accumulate);
@@ -681,21 +680,21 @@ int bwd_attn(tp_layer* L, const tp_params* p, const tp_bwd_io* io, const float* 
                      at<float>(ws, L->lse2), at<float>(ws, L->delta), at<void>(ws, L->dqkv),
                      p->valid_len, L->batch, L->seq, L->Hl, L->dh, L->mask, s));
   }
-  // side stream: dW_qkv and db_qkv (need dqkv) while da is computed
-  if ((e = fork_to(L, s, sd))) return e;
+  // dW_o is done before dW_qkv, which uses the same weight-gradient scratch
+  if ((e = join_from(L, s, sd))) return e;
+  // dW_qkv and db_qkv (need dqkv)
   g = wgrad_args(L, h, 3 * hl, a_act, at<void>(ws, L->dqkv), io->d_w_qkv, io->accumulate);
   g.split = L->split_wqkv; g.scale = unscale;
-  if ((e = run_gemm(L, g, sd, ws, true))) return e;
+  if ((e = run_gemm(L, g, s, ws, true))) return e;
   if ((e = bias_grad(L, at<void>(ws, L->dqkv), L->adt, 3 * hl, io->d_b_qkv, io->accumulate, ws,
-                     sd, -1, unscale)))
+                     s, -1, unscale)))
     return e;
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = 3 * hl;
   g.A = at<void>(ws, L->dqkv); g.lda = 3 * hl; g.a_kmajor = 1;
   g.B = wmat(L, ws, L->w16_qkv, p->w_qkv); g.ldb = 3 * hl; g.b_kmajor = 1;
   g.C = da_out; g.ldc = h; g.c_dtype = DT_F32; g.scale = unscale;
-  if ((e = run_gemm(L, g, s, ws))) return e;
-  return join_from(L, s, sd);
+  return run_gemm(L, g, s, ws);
 }
 
 // da (summed) -> dx (+ dh), LN1 grads.
