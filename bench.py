@@ -434,7 +434,7 @@ def _median(v):
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
-def make_train_step(w, sp=False, recompute=False, params=None, overlap_wgrad=0):
+def make_train_step(w, sp=False, recompute=False, params=None, overlap=0):
     """Uploads the workload and returns (step, shard, valid_len, cleanup)."""
     import torch
     from tensor_model_transformer_amd import binding as B
@@ -446,7 +446,7 @@ def make_train_step(w, sp=False, recompute=False, params=None, overlap_wgrad=0):
         params = rank_params(w)
     x, dout, vl = layer_inputs(w)
     sh = Shard(d, w.rank, recompute=B.TP_RECOMPUTE_FC1 if recompute else B.TP_RECOMPUTE_NONE,
-               sequence_parallel=sp, overlap_wgrad=overlap_wgrad)
+               sequence_parallel=sp, overlap=overlap)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()
@@ -512,7 +512,7 @@ def bench_train(args):
     sp = args.layout == "sp"
     params = rank_params(w)
     overlap = {"auto": B.TP_OVERLAP_AUTO, "off": B.TP_OVERLAP_OFF,
-               "on": B.TP_OVERLAP_ON}[args.overlap_wgrad]
+               "on": B.TP_OVERLAP_ON}[args.overlap]
     step, sh, vl, cleanup = make_train_step(w, sp, args.recompute, params, overlap)
     flops = algorithmic_flops(d, vl)
     sclk = None if args.no_sclk else SclkSampler()
@@ -572,7 +572,7 @@ def bench_train(args):
         for name in OTHER_WORKLOADS:
             ow = WORKLOADS[name]
             ostep, osh, ovl, oclean = make_train_step(ow, False, args.recompute,
-                                                      overlap_wgrad=overlap)
+                                                      overlap=overlap)
             oper, _, _, _ = timed_steps(ostep, max(args.steps, 50), args.warmup)
             ost = step_stats(oper, algorithmic_flops(ow.dims, ovl))
             others[name] = {k: ost[k] for k in ("value", "pct_of_peak", "ms_per_step", "ms_min",
@@ -607,7 +607,7 @@ def bench_train(args):
                    "hidden": d.hidden, "heads": d.heads, "ffn": d.ffn, "t": d.t,
                    "rank": w.rank, "mask": d.mask, "gflop_per_step": flops / 1e9,
                    "recompute": "fc1" if args.recompute else "none", "layout": args.layout,
-                   "overlap_wgrad": args.overlap_wgrad,
+                   "overlap": args.overlap,
                    "workspace_bytes": ws_bytes},
         "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown,
         "other_workloads": others or None,
@@ -636,8 +636,8 @@ def main():
                          "sequence-parallel phases (its kernels only, exchanges excluded)")
     ap.add_argument("--recompute", action="store_true",
                     help="recompute the FC1 pre-activation in backward (TP_RECOMPUTE_FC1)")
-    ap.add_argument("--overlap-wgrad", choices=("auto", "off", "on"), default="auto",
-                    help="weight gradients on the handle's second stream (opts.overlap_wgrad; "
+    ap.add_argument("--overlap", choices=("auto", "off", "on"), default="auto",
+                    help="weight gradients on the handle's second stream (opts.overlap; "
                          "auto: from hidden 8192)")
     ap.add_argument("--mode", choices=("train", "decode"), default="train",
                     help="train: forward + backward (the headline); decode: one decode step")

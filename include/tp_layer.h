@@ -188,20 +188,22 @@ typedef struct {
   int scores;       /* TP_SCORES_AUTO (default), TP_SCORES_FP16 or TP_SCORES_SPLIT */
   int recompute;    /* TP_RECOMPUTE_NONE (default) or TP_RECOMPUTE_FC1 */
   int sequence_parallel;  /* 0 (default) or 1: the TP_*_SP_* phases below */
-  int overlap_wgrad;      /* TP_OVERLAP_AUTO (default, also a zeroed struct),
-                             TP_OVERLAP_OFF or TP_OVERLAP_ON: whether the
-                             backward computes the gradient of W_o on a second
-                             stream of the handle while dO and the attention
-                             backward run on the caller's stream (the phase
-                             joins it before returning), or every kernel on
-                             the caller's stream. Results are bitwise
-                             identical. AUTO overlaps from hidden >= 8192: on
-                             one MI355X the overlap measured about 1 % faster
-                             on the 1T shard and 0.2-0.4 % slower on the 1.2B
-                             and 8.3B shards. (Overlapping the other weight
-                             gradients with the data-gradient GEMMs measured
-                             slower everywhere: the GEMMs compete for the same
-                             compute units.) */
+  int overlap;      /* TP_OVERLAP_AUTO (default, also a zeroed struct),
+                       TP_OVERLAP_OFF or TP_OVERLAP_ON: whether TP_ALL runs
+                       two independent pieces on a second stream of the
+                       handle, joined before its results are used: in the
+                       forward (bf16 layers) the fp16 copies of the MLP
+                       weights while attention and the output projection run;
+                       in the backward the gradient of W_o while dO and the
+                       attention backward run. Otherwise every kernel runs on
+                       the caller's stream. Results are bitwise identical.
+                       AUTO overlaps from hidden >= 8192: on one MI355X the
+                       two overlaps took the 1T shard's step 13.79 -> 13.67
+                       -> 13.30 ms (measured in one box each), while the
+                       backward one made the 1.2B and 8.3B shards 0.5 %
+                       slower. (Overlapping the other weight gradients with
+                       the data-gradient GEMMs measured slower everywhere:
+                       the GEMMs compete for the same compute units.) */
 } tp_layer_opts;
 
 /* Parameters of rank r (shapes above) and, for TP_MASK_PADDING, the number

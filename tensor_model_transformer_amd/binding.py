@@ -56,7 +56,7 @@ KCLASSES = ("gemm", "attn_fwd", "attn_bwd", "ln_fwd", "ln_bwd", "reduce", "conve
 
 class tp_layer_opts(Structure):
     _fields_ = [("ln_eps", c_float), ("gelu", c_int), ("dx_dtype", c_int), ("scores", c_int),
-                ("recompute", c_int), ("sequence_parallel", c_int), ("overlap_wgrad", c_int)]
+                ("recompute", c_int), ("sequence_parallel", c_int), ("overlap", c_int)]
 
 
 class tp_params(Structure):
@@ -140,7 +140,7 @@ def tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, 
                                        int(opts.get("scores", TP_SCORES_AUTO)),
                                        int(opts.get("recompute", TP_RECOMPUTE_NONE)),
                                        int(opts.get("sequence_parallel", 0)),
-                                       int(opts.get("overlap_wgrad", TP_OVERLAP_AUTO))))
+                                       int(opts.get("overlap", TP_OVERLAP_AUTO))))
     rc = lib().tp_layer_create(hidden, heads, ffn, seq, micro_batch, t, rank, dtype, mask, o,
                                ctypes.byref(h), ctypes.byref(ws))
     return rc, h.value, ws.value

@@ -32,9 +32,9 @@ constexpr size_t kAlign = 256;
 // moves softmax outputs by several tenths of a percent, visible in the
 // gradient of W_qkv; at hidden <= 3072 the spread is about 1.
 constexpr int kSplitScoresHidden = 8192;
-// opts.overlap_wgrad = TP_OVERLAP_AUTO overlaps from this width (measured:
-// the 1T shard's step about 1 % faster with the overlap, the 1.2B and 8.3B
-// shards' 0.2-0.4 % slower).
+// opts.overlap = TP_OVERLAP_AUTO overlaps from this width (measured: the 1T
+// shard's step about 2 % faster with the two overlaps, the 1.2B and 8.3B
+// shards' 0.5 % slower with the backward one).
 constexpr int kOverlapHidden = 8192;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -104,7 +104,7 @@ struct tp_layer {
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   bool side_tried = false;
-  bool overlap_wgrad = false;  // weight gradients on the side stream (opts)
+  bool overlap = false;  // independent pieces of TP_ALL on the side stream (opts)
   // decode (one row per sequence): its own workspace plan
   struct Dec {
     Region a, apart, o, h_mid, c, z, gpart;
@@ -375,12 +375,12 @@ int run_gemm(tp_layer* L, GemmArgs g, hipStream_t s, void* ws, bool wgrad = fals
   return TP_OK;
 }
 
-// The side stream (created on first use) when the handle overlaps the weight
-// gradients (opts.overlap_wgrad), else the caller's stream; also the caller's
+// The side stream (created on first use) when the handle overlaps
+// (opts.overlap), else the caller's stream; also the caller's
 // stream while profiling (each event pair then brackets its launch group
 // alone) or if the side stream could not be created.
 hipStream_t side_stream(tp_layer* L, hipStream_t s) {
-  if (L->prof.on || !L->overlap_wgrad) return s;
+  if (L->prof.on || !L->overlap) return s;
   if (!L->side_tried) {
     L->side_tried = true;
     hipStream_t st = nullptr;
@@ -457,8 +457,10 @@ int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
 // x -> a -> qkv -> o -> (o @ W_o) [+ b_o + x] into `dst` (fp32 [n, h]).
 // With a_in (the sequence-parallel layout) LN1 has run per chunk already and
 // a_in is the gathered [n, h] LayerNorm output.
+int convert_mlp_weights(tp_layer* L, const tp_params* p, void* ws, hipStream_t s);
+
 int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool designated,
-             void* ws, hipStream_t s, const void* a_in = nullptr) {
+             void* ws, hipStream_t s, const void* a_in = nullptr, hipStream_t mlp_cvt = nullptr) {
   const int n = L->n, h = L->hidden, hl = L->hl;
   int e;
   const double nh = (double)n * h;
@@ -481,6 +483,11 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
     g.C2 = qkv_lo(L, ws); g.ldc2 = 3 * hl; g.c2_dtype = DT_F16;
   }
   if ((e = run_gemm(L, g, s, ws))) return e;
+  // the MLP weights' fp16 copies on the side stream while attention runs
+  if (mlp_cvt) {
+    if ((e = fork_to(L, s, mlp_cvt))) return e;
+    if ((e = convert_mlp_weights(L, p, ws, mlp_cvt))) return e;
+  }
   {
   Scope ps(L, s, TP_K_ATTN_FWD, 4.0 * L->dh * L->Hl * L->attn_pairs,
            (double)n * 4 * hl * L->esz + 4.0 * n * L->Hl);
@@ -504,14 +511,18 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
 // h_mid (fp32) -> c -> u, z -> (z @ W_fc2) [+ b_fc2 + h_mid] into `out`.
 // With c_in (sequence-parallel layout) LN2 has run per chunk already and c_in
 // is the gathered [n, h] LayerNorm output.
+int convert_mlp_weights(tp_layer* L, const tp_params* p, void* ws, hipStream_t s) {
+  const size_t hf = (size_t)L->hidden * L->fl;
+  return to_f16_copies(L, {p->w_fc1, p->w_fc2}, {&L->w16_fc1, &L->w16_fc2}, {hf, hf}, ws, s);
+}
+
 int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, int out_f32,
-            bool designated, void* ws, hipStream_t s, const void* c_in = nullptr) {
+            bool designated, void* ws, hipStream_t s, const void* c_in = nullptr,
+            bool converted = false) {
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
   float* h_mid = at<float>(ws, L->h_mid);
-  if ((e = to_f16_copies(L, {p->w_fc1, p->w_fc2}, {&L->w16_fc1, &L->w16_fc2},
-                         {(size_t)h * fl, (size_t)fl * h}, ws, s)))
-    return e;
+  if (!converted && (e = convert_mlp_weights(L, p, ws, s))) return e;
   if (!c_in) {
   Scope ps(L, s, TP_K_LN_FWD, 0,
            (double)n * h * (4 + L->esz + (h_mid_in == h_mid ? 0 : 4)) + 8.0 * n);
@@ -962,7 +973,7 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
     scores = opts->scores;
     recompute = opts->recompute;
     seq_par = opts->sequence_parallel;
-    overlap = opts->overlap_wgrad;
+    overlap = opts->overlap;
     if (!(eps > 0.f)) return TP_ERR_ARG;
     if (gelu != TP_GELU_ERF && gelu != TP_GELU_TANH) return TP_ERR_UNSUPPORTED;
     if (dx_dtype != TP_DTYPE_F32 && dx_dtype != dtype) return TP_ERR_UNSUPPORTED;
@@ -983,7 +994,7 @@ int tp_layer_create(int hidden, int heads, int ffn, int seq, int micro_batch, in
   L->dx_f32 = dx_dtype == TP_DTYPE_F32;
   L->recompute_fc1 = recompute == TP_RECOMPUTE_FC1;
   L->sp = seq_par == 1;
-  L->overlap_wgrad = overlap == TP_OVERLAP_ON ||
+  L->overlap = overlap == TP_OVERLAP_ON ||
                      (overlap == TP_OVERLAP_AUTO && hidden >= kOverlapHidden);
   L->nc = (int)(n / t);
   L->split_scores = dtype == TP_DTYPE_BF16 &&
@@ -1014,10 +1025,15 @@ int tp_layer_fwd(tp_layer* L, int phase, const tp_fwd_io* io, void* hip_stream) 
   const tp_params* p = io->params;
   const bool designated = L->rank == 0;
   switch (phase) {
-    case TP_ALL:
+    case TP_ALL: {
       if ((e = check_ptrs({io->x, io->out}))) return e;
-      if ((e = fwd_attn(L, p, io->x, at<float>(ws, L->h_mid), true, ws, s))) return e;
-      return fwd_mlp(L, p, at<float>(ws, L->h_mid), io->out, 0, true, ws, s);
+      hipStream_t sd = L->sdt == DT_BF16 ? side_stream(L, s) : s;
+      if ((e = fwd_attn(L, p, io->x, at<float>(ws, L->h_mid), true, ws, s, nullptr,
+                        sd != s ? sd : nullptr)))
+        return e;
+      if (sd != s && (e = join_from(L, s, sd))) return e;
+      return fwd_mlp(L, p, at<float>(ws, L->h_mid), io->out, 0, true, ws, s, nullptr, sd != s);
+    }
     case TP_FWD_ATTN:
       if ((e = check_ptrs({io->x, io->out}))) return e;
       return fwd_attn(L, p, io->x, (float*)io->out, designated, ws, s);

@@ -41,7 +41,7 @@ class Shard:
     def __init__(self, dims: LayerDims, rank: int, device="cuda:0", gelu: int = B.TP_GELU_ERF,
                  eps: float = 1e-5, dx_fp32: bool = True, scores: int = B.TP_SCORES_AUTO,
                  recompute: int = B.TP_RECOMPUTE_NONE, sequence_parallel: bool = False,
-                 overlap_wgrad: int = B.TP_OVERLAP_AUTO):
+                 overlap: int = B.TP_OVERLAP_AUTO):
         self.dims = dims
         self.rank = rank
         self.device = torch.device(device)
@@ -54,7 +54,7 @@ class Shard:
              "dx_dtype": B.TP_DTYPE_F32 if dx_fp32 or dims.dtype == "f32" else B.TP_DTYPE_BF16,
              "scores": scores, "recompute": recompute,
              "sequence_parallel": int(sequence_parallel),
-             "overlap_wgrad": overlap_wgrad})
+             "overlap": overlap})
         self.dx_fp32 = dx_fp32
         _check("tp_layer_create", rc)
         # whether the handle keeps the score residuals (what TP_SCORES_AUTO chose)

@@ -51,7 +51,7 @@ def local_inputs(w, rank=None):
 
 
 def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True, scores=0,
-                  recompute=0, gelu="erf", eps=1e-5, inputs=None, overlap_wgrad=0):
+                  recompute=0, gelu="erf", eps=1e-5, inputs=None, overlap=0):
     """TP_ALL forward + backward of one rank on the GPU. Returns numpy dict.
     `inputs` replaces the generated (params, x, dout, valid_len); its values
     must already lie on the storage grid (bf16 or fp32)."""
@@ -64,7 +64,7 @@ def run_gpu_local(w, rank=None, taps=False, accumulate_twice=False, dx_fp32=True
     params, x, dout, vl = inputs if inputs is not None else local_inputs(w, r)
     sh = Shard(d, r, dx_fp32=dx_fp32, scores=scores, recompute=recompute, eps=eps,
                gelu=B.TP_GELU_TANH if gelu == "tanh" else B.TP_GELU_ERF,
-               overlap_wgrad=overlap_wgrad)
+               overlap=overlap)
     p = sh.upload_params(params, vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()

@@ -75,7 +75,7 @@ def create(**kw):
     (dict(opts={"scores": 3}), B.TP_ERR_UNSUPPORTED),
     (dict(opts={"recompute": 2}), B.TP_ERR_UNSUPPORTED),
     (dict(opts={"sequence_parallel": 2}), B.TP_ERR_UNSUPPORTED),
-    (dict(opts={"overlap_wgrad": 3}), B.TP_ERR_UNSUPPORTED),
+    (dict(opts={"overlap": 3}), B.TP_ERR_UNSUPPORTED),
     (dict(seq=63, micro_batch=1, opts={"sequence_parallel": 1}), B.TP_ERR_SHAPE),  # n % t
     (dict(dtype=B.TP_DTYPE_F32, opts={"scores": B.TP_SCORES_SPLIT}), B.TP_ERR_UNSUPPORTED),
 ])

@@ -125,15 +125,15 @@ def test_recompute_fc1_is_bitwise_equal(w):
 
 
 @pytest.mark.parametrize("w", [SMALL_BF16[0], SMALL_BF16[4]], ids=lambda w: w.name)
-def test_overlap_wgrad_is_bitwise_equal(w):
-    # opts.overlap_wgrad = TP_OVERLAP_ON runs the weight and bias gradients
+def test_overlap_is_bitwise_equal(w):
+    # opts.overlap = TP_OVERLAP_ON runs the weight and bias gradients
     # on the handle's second stream: the same kernels on the same inputs, so
     # every result is bitwise unchanged, also when the gradients accumulate
     _need_gpu()
     from tensor_model_transformer_amd import binding as B
     for twice in (False, True):
-        a = run_gpu_local(w, accumulate_twice=twice, overlap_wgrad=B.TP_OVERLAP_OFF)
-        b = run_gpu_local(w, accumulate_twice=twice, overlap_wgrad=B.TP_OVERLAP_ON)
+        a = run_gpu_local(w, accumulate_twice=twice, overlap=B.TP_OVERLAP_OFF)
+        b = run_gpu_local(w, accumulate_twice=twice, overlap=B.TP_OVERLAP_ON)
         assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["dx"], b["dx"])
         for k in a["grads"]:
             assert np.array_equal(a["grads"][k], b["grads"][k]), (k, twice)
@@ -192,7 +192,7 @@ def test_graph_replay_matches_eager(overlap):
     d = w.dims
     print(f"\n[graph] {w.name} dims={d} overlap={overlap}", flush=True)
     x, dout, vl = layer_inputs(w)
-    sh = Shard(d, 0, overlap_wgrad=overlap)
+    sh = Shard(d, 0, overlap=overlap)
     p = sh.upload_params(rank_params(w, 0), vl if d.mask == "padding" else None)
     xd, doutd = sh.act(x), sh.act(dout)
     out, dx = sh.empty_act(), sh.empty_dx()
