@@ -23,15 +23,19 @@
 // Scores are kept in the log2 domain (scale * log2(e) folded into S) and the
 // per-row normaliser is saved as lse2 = max + log2(sum).
 //
-// Backward (deterministic, no atomics): one kernel owns a block of queries
-// and sweeps the keys (dQ); it runs first and also writes delta =
-// rowsum(dO * O) of its queries. Another owns a block of keys and sweeps the
-// queries (dK, dV), reading delta. P is recomputed from lse2.
+// Backward (deterministic, no atomics): a small kernel writes delta =
+// rowsum(dO * O) per query first. Then one grid holds two kinds of
+// workgroups: one owns a block of queries and sweeps the keys (dQ), the other
+// owns a block of keys and sweeps the queries (dK, dV). P is recomputed from
+// lse2.
 //
 // fp32 path: one thread per query (forward, dQ) or key (dK, dV) with exact
 // fp32 arithmetic.
 #include <math.h>
 
+#include <algorithm>
+
+#include "attn_sched.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -157,32 +161,15 @@ __device__ __forceinline__ void pair32(float x, float* a, float* b) {
   *b = __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Workgroup coordinates on a 1-D grid of nblk * Hl * batch workgroups of
-// 128 rows each: (block along the sequence, head, sequence). Workgroup i runs
-// on XCD i % 8 (round-robin dispatch). When the (sequence, head) pairs divide
-// evenly over the 8 XCDs, each XCD takes whole pairs, so the workgroups that
-// stream one pair's K and V (or Q and dO) share that XCD's L2 instead of each
-// XCD reading every pair; an XCD starts the blocks of rank 0 of all its pairs
-// first, then rank 1, and so on. Otherwise, when the workgroups divide by 8,
-// XCD x takes the x-th eighth of the pair-major order (a pair straddles at
-// most two XCDs). Block = rank, or nblk-1-rank with `reverse` (the causal
-// forward and dQ put their longest query blocks first).
+// Workgroup coordinates (block along the sequence, head, sequence, role) of
+// this workgroup in the rank-ordered job lists of attn_sched.hpp.
 struct AttnWG {
-  int blk, head, b;
+  int blk, head, b, role;
 };
-__device__ __forceinline__ AttnWG attn_wg(int nblk, int Hl, int batch, bool reverse) {
-  const int i = blockIdx.x, npairs = Hl * batch, nwg = nblk * npairs;
-  int rank, pair;
-  if (npairs % 8 == 0) {
-    const int per = npairs / 8, s = i / 8;
-    rank = s / per;
-    pair = (i % 8) + 8 * (s % per);
-  } else {
-    const int l = nwg % 8 == 0 ? (i % 8) * (nwg / 8) + i / 8 : i;
-    rank = l % nblk;
-    pair = l / nblk;
-  }
-  return AttnWG{reverse ? nblk - 1 - rank : rank, pair % Hl, pair / Hl};
+__device__ __forceinline__ AttnWG attn_wg(int nblk, int Hl, int batch, int nroles, bool rev0,
+                                          bool rev1) {
+  const AttnJob jb = attn_job((int)blockIdx.x, nblk, Hl * batch, nroles, rev0, rev1);
+  return AttnWG{jb.blk, jb.pair % Hl, jb.pair / Hl, jb.role};
 }
 
 // LDS stages: three when three stages of the workgroups that share a compute
@@ -232,7 +219,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFwdWaves<D
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const AttnWG wg = attn_wg((seq + 127) / 128, Hl, batch, causal);
+  const AttnWG wg = attn_wg((seq + 127) / 128, Hl, batch, 1, causal, false);
+  if (wg.blk < 0) return;
   const int qb = wg.blk, head = wg.head, b = wg.b;
   const int qw0 = qb * 128 + w * 32;
   const int q = qw0 + l32;
@@ -480,20 +468,18 @@ __global__ __launch_bounds__(64) void attn_delta_kernel(const T* __restrict__ o,
 // from HBM into LDS stages. Q^T and dO^T operands are read from the row-major
 // tiles with transposing LDS reads.
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D, SPLIT>))) void attn_bwd_dkdv_f16_kernel(
+__device__ __forceinline__ void attn_bwd_dkdv_f16(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
-    const int* __restrict__ valid_len, int batch, int seq, int Hl, int causal, float sl2,
-    float scale) {
+    const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale,
+    const AttnWG wg, unsigned char* smem) {
   constexpr int QB = 64, TILE = QB * D, NT = SPLIT ? 3 : 2;
   constexpr int SE = kQgStageBytes<D, SPLIT> / 2;  // stage size in f16 elements
-  extern __shared__ __align__(16) unsigned char smem[];
   // [stages][Q tile, dO tile (, Q residual tile), lse2[QB], delta[QB] (fp32)]
   f16* lds = reinterpret_cast<f16*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const AttnWG wg = attn_wg((seq + 127) / 128, Hl, batch, false);
   const int kblk = wg.blk, head = wg.head, b = wg.b;
   const int kw0 = kblk * 128 + w * 32;
   const int key = kw0 + l32;
@@ -647,19 +633,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<
 // fp16 backward: dQ (a workgroup owns 128 queries, 32 per wave)
 // ============================================================================
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D, SPLIT>))) void attn_bwd_dq_f16_kernel(
+__device__ __forceinline__ void attn_bwd_dq_f16(
     const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
-    const f16* __restrict__ o, const float* __restrict__ lse2, float* __restrict__ delta,
-    f16* __restrict__ dqkv,
-    const int* __restrict__ valid_len, int batch, int seq, int Hl, int causal, float sl2,
-    float scale) {
+    const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
+    const int* __restrict__ valid_len, int seq, int Hl, int causal, float sl2, float scale,
+    const AttnWG wg, unsigned char* smem) {
   constexpr int KB = 64, TILE = KB * D, NT = SPLIT ? 3 : 2;
-  extern __shared__ __align__(16) unsigned char smem[];
   f16* lds = reinterpret_cast<f16*>(smem);  // [stages][K tile, V tile (, K residual tile)]
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const AttnWG wg = attn_wg((seq + 127) / 128, Hl, batch, causal);
   const int qb = wg.blk, head = wg.head, b = wg.b;
   const int qw0 = qb * 128 + w * 32;
   const int q = qw0 + l32;
@@ -669,7 +652,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D,
   const f16* Kp = Qp + D;
   const f16* Vp = Qp + 2 * D;
   const f16* dOp = dO + tok0 * ldo + (size_t)head * D;
-  const f16* Op = o + tok0 * ldo + (size_t)head * D;
   const int L = causal ? seq : min(max(valid_len[b], 0), seq);
   const int kv_end = causal ? min(seq, qb * 128 + 128) : L;
   const int lim = causal ? min(q + 1, seq) : L;
@@ -681,30 +663,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D,
   f16x8 qf[D / 16], gf[D / 16], ql[SPLIT ? D / 16 : 1];
   auto load_regs = [&]() {
   lq = qok ? lse2[((size_t)b * Hl + head) * seq + q] : 0.f;
-  // delta = rowsum(dO * O) of this query: each lane half sums its columns
-  float dsum = 0.f;
+  dq_ = qok ? delta[((size_t)b * Hl + head) * seq + q] : 0.f;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0), ov = make_uint4(0, 0, 0, 0);
+    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
     if (qok) {
       a = *reinterpret_cast<const uint4*>(Qp + (size_t)q * ldq + 16 * ks + 8 * hh);
       c = *reinterpret_cast<const uint4*>(dOp + (size_t)q * ldo + 16 * ks + 8 * hh);
-      ov = *reinterpret_cast<const uint4*>(Op + (size_t)q * ldo + 16 * ks + 8 * hh);
     }
     qf[ks] = __builtin_bit_cast(f16x8, a);
     gf[ks] = __builtin_bit_cast(f16x8, c);
-    const f16x8 of = __builtin_bit_cast(f16x8, ov);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)gf[ks][e], (float)of[e], dsum);
     if constexpr (SPLIT) {
       uint4 r = make_uint4(0, 0, 0, 0);
       if (qok) r = *reinterpret_cast<const uint4*>(Qlp + (size_t)q * ldq + 16 * ks + 8 * hh);
       ql[ks] = __builtin_bit_cast(f16x8, r);
     }
   }
-  dsum += __shfl_xor(dsum, 32, 64);
-  dq_ = dsum;
-  if (qok && hh == 0) delta[((size_t)b * Hl + head) * seq + q] = dsum;
   };
   f32x16 dQ[D / 32];
 #pragma unroll
@@ -788,6 +762,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDqWaves<D,
         Vec4<f16>::store(dq + 32 * t + 8 * jj + 4 * hh, a);
       }
   }
+}
+
+// ============================================================================
+// fp16 backward: one launch of both roles
+// ============================================================================
+// Workgroups of the dQ role and of the dK/dV role share one grid, in rank
+// order per XCD (attn_sched.hpp): under the causal mask a 128-row block's work grows
+// from 1 to nblk units along the sequence, and with one workgroup per compute
+// unit (head dim 160) two separate launches each end on their longest blocks
+// while most compute units idle; in one list the short blocks of either role
+// fill in behind the long ones (1T shard: 20 heads x 16 blocks per role).
+// delta = rowsum(dO * O) comes from attn_delta_kernel, launched before.
+template <int D, bool SPLIT>
+constexpr int kBwdWaves = kDqWaves<D, SPLIT> < kDkdvWaves<D, SPLIT> ? kDqWaves<D, SPLIT>
+                                                                     : kDkdvWaves<D, SPLIT>;
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdWaves<D, SPLIT>))) void attn_bwd_f16_kernel(
+    const f16* __restrict__ qkv, const f16* __restrict__ qkv_lo, const f16* __restrict__ dO,
+    const float* __restrict__ lse2, const float* __restrict__ delta, f16* __restrict__ dqkv,
+    const int* __restrict__ valid_len, int batch, int seq, int Hl, int causal, float sl2,
+    float scale) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const AttnWG wg = attn_wg((seq + 127) / 128, Hl, batch, 2, causal, false);
+  if (wg.blk < 0) return;
+  if (wg.role == 0)
+    attn_bwd_dq_f16<D, SPLIT>(qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, seq, Hl, causal, sl2,
+                              scale, wg, smem);
+  else
+    attn_bwd_dkdv_f16<D, SPLIT>(qkv, qkv_lo, dO, lse2, delta, dqkv, valid_len, seq, Hl, causal,
+                                sl2, scale, wg, smem);
 }
 
 // ============================================================================
@@ -959,26 +963,19 @@ static hipError_t fwd_f16(const void* qkv, const void* qkv_lo, void* o, float* l
   return hipGetLastError();
 }
 
+// delta first (its own kernel), then both roles in one grid.
 template <int D, bool SPLIT>
-// dQ runs first: it also computes delta = rowsum(dO * O), which dK/dV reads.
-static hipError_t bwd_f16(const void* qkv, const void* qkv_lo, const void* o, const void* dO,
-                          const float* lse2, float* delta, void* dqkv, const int* vl, int batch,
-                          int seq, int Hl, int causal, float sl2, float scale, hipStream_t s) {
-  auto k1 = attn_bwd_dkdv_f16_kernel<D, SPLIT>;
-  auto k2 = attn_bwd_dq_f16_kernel<D, SPLIT>;
-  const size_t lds1 = dkdv_lds<D, SPLIT>(), lds2 = dq_lds<D, SPLIT>();
-  hipError_t e = set_lds(k1, lds1);
-  if (e == hipSuccess) e = set_lds(k2, lds2);
+static hipError_t bwd_f16(const void* qkv, const void* qkv_lo, const void* dO, const float* lse2,
+                          const float* delta, void* dqkv, const int* vl, int batch, int seq,
+                          int Hl, int causal, float sl2, float scale, hipStream_t s) {
+  auto k = attn_bwd_f16_kernel<D, SPLIT>;
+  const size_t lds = std::max(dkdv_lds<D, SPLIT>(), dq_lds<D, SPLIT>());
+  hipError_t e = set_lds(k, lds);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((seq + 127) / 128 * Hl * batch));
-  hipLaunchKernelGGL(k2, grid, dim3(256), lds2, s, (const f16*)qkv,
-                     (const f16*)qkv_lo, (const f16*)dO, (const f16*)o, lse2, delta, (f16*)dqkv,
-                     vl, batch, seq, Hl, causal, sl2, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k1, grid, dim3(256), lds1, s, (const f16*)qkv,
-                     (const f16*)qkv_lo, (const f16*)dO, lse2, delta, (f16*)dqkv, vl, batch, seq,
-                     Hl, causal, sl2, scale);
+  dim3 grid((unsigned)(2 * ((seq + 127) / 128) * Hl * batch));
+  hipLaunchKernelGGL(k, grid, dim3(256), lds, s, (const f16*)qkv, (const f16*)qkv_lo,
+                     (const f16*)dO, lse2, delta, (f16*)dqkv, vl, batch, seq, Hl, causal, sl2,
+                     scale);
   return hipGetLastError();
 }
 
@@ -1004,10 +1001,10 @@ static hipError_t bwd_d(int dtype, const void* qkv, const void* qkv_lo, const vo
                         float scale, hipStream_t s) {
   if (dtype == DT_F16) {
     if (qkv_lo)
-      return bwd_f16<D, true>(qkv, qkv_lo, o, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal,
-                              sl2, scale, s);
-    return bwd_f16<D, false>(qkv, nullptr, o, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal,
-                             sl2, scale, s);
+      return bwd_f16<D, true>(qkv, qkv_lo, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal, sl2,
+                              scale, s);
+    return bwd_f16<D, false>(qkv, nullptr, dO, lse2, delta, dqkv, vl, batch, seq, Hl, causal, sl2,
+                             scale, s);
   } else {
     const long n = (long)batch * Hl * seq;
     const unsigned g = (unsigned)((n + 63) / 64);
@@ -1048,13 +1045,15 @@ hipError_t attn_bwd(int dtype, const void* qkv, const void* qkv_lo, const void* 
   if (batch == 0 || seq == 0 || Hl == 0) return hipSuccess;
   if (qkv_lo && dtype != DT_F16) return hipErrorInvalidValue;
   if (3L * Hl * D * 128 >= (1L << 31)) return hipErrorInvalidValue;
-  // fp32: delta by its own kernel; fp16: the dQ kernel computes it
-  if (dtype != DT_F16) {
+  // delta = rowsum(dO * O) per (token, head), read by the dQ and dK/dV kernels
+  if (dtype == DT_F16)
+    attn_delta_kernel<f16><<<(unsigned)(batch * seq), 64, (size_t)Hl * D / 8 * 4, s>>>(
+        (const f16*)o, (const f16*)dO, delta, seq, Hl, D);
+  else
     attn_delta_kernel<float><<<(unsigned)(batch * seq), 64, (size_t)Hl * D / 4 * 4, s>>>(
         (const float*)o, (const float*)dO, delta, seq, Hl, D);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int causal = mask == 0;
   const double sc = 1.0 / sqrt((double)D);
   const float sl2 = (float)(1.4426950408889634 * sc), scale = (float)sc;
