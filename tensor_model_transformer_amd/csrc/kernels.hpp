@@ -50,9 +50,9 @@ hipError_t residual_add(const float* a, int bias_dtype, const void* bias, int r_
                         hipStream_t s);
 
 // out_k[j] (+)= scale * sum_b part[b][k][j] for k < nout (part is
-// [nblk][nout][width]; scale: optional device fp32, 1 when null). The buffer
-// must hold reduce_scratch_floats(nblk, nout, width) floats: the block
-// partials followed by room for the group partials of stage 1.
+// [nblk][nout][width]; scale: optional device fp32, 1 when null), summed in
+// a fixed order (deterministic). reduce_scratch_floats(nblk, nout, width) is
+// the size of part in floats.
 hipError_t reduce_partials(const float* part, int nblk, int nout, int width,
                            float* out0, float* out1, float* out2, int accumulate,
                            hipStream_t s, const float* scale = nullptr);

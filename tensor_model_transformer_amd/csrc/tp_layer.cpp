@@ -553,8 +553,8 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
 }
 
 // ---- backward pieces -------------------------------------------------------
-// Bias gradient: out (+)= column sums of y [n, cols] (two-stage, deterministic).
-// Bias gradient (column sums of y), with its own partials.
+// Bias gradient: out (+)= column sums of y [n, cols] (block partials in its
+// own scratch, then one deterministic reduction).
 int bias_grad(tp_layer* L, const void* y, int y_dtype, int cols, float* out, int accumulate,
               void* ws, hipStream_t s, int rows = -1, const float* scale = nullptr) {
   if (rows < 0) rows = L->n;
