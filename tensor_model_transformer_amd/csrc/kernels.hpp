@@ -42,6 +42,11 @@ int ln_bwd_blocks(int rows, int h, int* rows_per_blk);
 hipError_t colsum_partial(int y_dtype, const void* y, int rows, int cols, int ld,
                           float* part, int rows_per_blk, hipStream_t s);
 int colsum_blocks(int rows, int cols, int* rows_per_blk);
+// colsum_partial of a bf16 matrix that also writes the kAmaxFloats partial
+// maxima of |y| to_f16 takes with amax_ready (cols % 8 == 0; at most
+// kAmaxFloats workgroups, else hipErrorInvalidValue; rows, cols > 0).
+hipError_t colsum_amax_partial(const void* y, int rows, int cols, int ld, float* part,
+                               int rows_per_blk, float* amax_part, hipStream_t s);
 // out[rows, h] = a (fp32) + bias[h] + r; dtypes DT_F32 / DT_BF16 as listed in
 // norm.hip (fp32 bias/r/out, or bf16 bias with bf16 r -> fp32 out, or bf16
 // bias with fp32 r -> bf16 out).
@@ -61,10 +66,12 @@ size_t reduce_scratch_floats(int nblk, int nout, int width);
 // dst[k][i] = fp16(src[k][i]) for bf16 src, i < count[k], k < nseg (1..4).
 // With amax_part (kAmaxFloats floats of scratch) and scale_out (2 floats),
 // nseg must be 1 and dst = fp16(S * src) with the power of two S that puts
-// max|S src| in [1, 2); scale_out receives S and 1/S (device fp32).
+// max|S src| in [1, 2); scale_out receives S and 1/S (device fp32). With
+// amax_ready the partial maxima are in amax_part already (colsum_amax_partial).
 constexpr int kAmaxFloats = 1024;
 hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
-                  hipStream_t s, float* amax_part = nullptr, float* scale_out = nullptr);
+                  hipStream_t s, float* amax_part = nullptr, float* scale_out = nullptr,
+                  bool amax_ready = false);
 
 // dst[i] = sum_p parts[p][i]  (fp32 sum in order), written as dst_dtype.
 hipError_t exchange_sum(void* dst, int dst_dtype, const float* const* parts,

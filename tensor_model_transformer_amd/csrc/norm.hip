@@ -472,33 +472,60 @@ hipError_t ln_bwd(int p_dtype, const float* dy, int x_dtype, const void* x,
 // ----------------------------------------------------------------------------
 // Column partial sums (bias gradients): part[blk][c] = sum over the block's rows.
 // ----------------------------------------------------------------------------
-template <typename T>
+// With AMAX the workgroup also writes max|y| over its elements to
+// amax[blockIdx.y * gridDim.x + blockIdx.x], and workgroup 0 zeroes the rest
+// of the kAmaxFloats entries: the partial maxima of the upstream gradient,
+// read in the same pass as its bias gradient's column sums.
+template <typename T, bool AMAX = false>
 __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ y, int rows,
                                                      int cols, int ld, float* __restrict__ part,
-                                                     int rows_per_blk) {
+                                                     int rows_per_blk, float* __restrict__ amax) {
   const int j = blockIdx.x * 256 + threadIdx.x;  // vector index (8 columns)
-  if (8 * j >= cols) return;
-  const int r0 = blockIdx.y * rows_per_blk;
-  const int r1 = min(rows, r0 + rows_per_blk);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int r = r0;
-  // 8 rows in flight at a time, summed in row order
-  for (; r + 8 <= r1; r += 8) {
-    float v[8][8];
+  const bool active = 8 * j < cols;
+  if (!AMAX && !active) return;
+  float m = 0.f;
+  if (active) {
+    const int r0 = blockIdx.y * rows_per_blk;
+    const int r1 = min(rows, r0 + rows_per_blk);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int r = r0;
+    // 8 rows in flight at a time, summed in row order
+    for (; r + 8 <= r1; r += 8) {
+      float v[8][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) Vec8<T>::load(y + (size_t)(r + u) * ld + 8 * j, v[u]);
+      for (int u = 0; u < 8; ++u) Vec8<T>::load(y + (size_t)(r + u) * ld + 8 * j, v[u]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
+        for (int e = 0; e < 8; ++e) {
+          acc[e] += v[u][e];
+          if constexpr (AMAX) m = fmaxf(m, fabsf(v[u][e]));
+        }
+    }
+    for (; r < r1; ++r) {
+      float v[8];
+      Vec8<T>::load(y + (size_t)r * ld + 8 * j, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[e] += v[e];
+        if constexpr (AMAX) m = fmaxf(m, fabsf(v[e]));
+      }
+    }
+    Vec8<float>::store(part + (size_t)blockIdx.y * cols + 8 * j, acc);
   }
-  for (; r < r1; ++r) {
-    float v[8];
-    Vec8<T>::load(y + (size_t)r * ld + 8 * j, v);
+  if constexpr (AMAX) {
+    // the entries past the grid's workgroups hold zero (no effect on the maximum)
+    const int nwg = gridDim.x * gridDim.y;
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      for (int i = nwg + threadIdx.x; i < kAmaxFloats; i += 256) amax[i] = 0.f;
+    __shared__ float red[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      amax[blockIdx.y * gridDim.x + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   }
-  Vec8<float>::store(part + (size_t)blockIdx.y * cols + 8 * j, acc);
 }
 
 int colsum_blocks(int rows, int cols, int* rows_per_blk) {
@@ -516,11 +543,25 @@ hipError_t colsum_partial(int y_dtype, const void* y, int rows, int cols, int ld
   if (nblk == 0 || cols == 0) return hipSuccess;
   dim3 grid((cols / 8 + 255) / 256, nblk);
   if (y_dtype == DT_BF16)
-    colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)y, rows, cols, ld, part, rows_per_blk);
+    colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)y, rows, cols, ld, part, rows_per_blk,
+                                             nullptr);
   else if (y_dtype == DT_F16)
-    colsum_kernel<f16><<<grid, 256, 0, s>>>((const f16*)y, rows, cols, ld, part, rows_per_blk);
+    colsum_kernel<f16><<<grid, 256, 0, s>>>((const f16*)y, rows, cols, ld, part, rows_per_blk,
+                                            nullptr);
   else
-    colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)y, rows, cols, ld, part, rows_per_blk);
+    colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)y, rows, cols, ld, part,
+                                              rows_per_blk, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t colsum_amax_partial(const void* y, int rows, int cols, int ld, float* part,
+                               int rows_per_blk, float* amax_part, hipStream_t s) {
+  const int nblk = (rows + rows_per_blk - 1) / rows_per_blk;
+  const int gx = (cols / 8 + 255) / 256;
+  if (cols % 8 || (long)gx * nblk > kAmaxFloats) return hipErrorInvalidValue;
+  if (nblk == 0 || cols == 0) return hipErrorInvalidValue;
+  colsum_kernel<bf16, true><<<dim3(gx, nblk), 256, 0, s>>>((const bf16*)y, rows, cols, ld, part,
+                                                          rows_per_blk, amax_part);
   return hipGetLastError();
 }
 
@@ -767,7 +808,7 @@ __global__ __launch_bounds__(256) void to_f16_flat_kernel(CvtSegs c) {
 }
 
 hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count, int nseg,
-                  hipStream_t s, float* amax_part, float* scale_out) {
+                  hipStream_t s, float* amax_part, float* scale_out, bool amax_ready) {
   if (nseg < 1 || nseg > 4) return hipErrorInvalidValue;
   if ((amax_part == nullptr) != (scale_out == nullptr)) return hipErrorInvalidValue;
   CvtSegs c = {};
@@ -783,11 +824,14 @@ hipError_t to_f16(const void* const* src, void* const* dst, const size_t* count,
   c.scale_out = scale_out;
   if (amax_part) {
     // the maximum over every segment, one launch per segment (the upstream
-    // gradient is a single segment)
+    // gradient is a single segment); amax_ready: colsum_amax_partial has
+    // written the partial maxima already
     if (nseg != 1) return hipErrorInvalidValue;
-    amax_kernel<<<kAmaxBlocks, 256, 0, s>>>((const bf16*)src[0], count[0], amax_part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!amax_ready) {
+      amax_kernel<<<kAmaxBlocks, 256, 0, s>>>((const bf16*)src[0], count[0], amax_part);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   const size_t total = c.start[nseg];
   if (!total && !amax_part) return hipSuccess;  // (with a scale, one block still writes it)

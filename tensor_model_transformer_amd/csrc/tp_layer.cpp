@@ -430,7 +430,7 @@ const float* chain_unscale(tp_layer* L, void* ws) {
 // this call derives from it and stores in the workspace).
 int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
                   std::initializer_list<const Region*> dst, std::initializer_list<size_t> count,
-                  void* ws, hipStream_t s, bool scaled = false) {
+                  void* ws, hipStream_t s, bool scaled = false, bool amax_ready = false) {
   if (L->sdt != DT_BF16) return TP_OK;
   const void* sp[4];
   void* dp[4];
@@ -446,10 +446,10 @@ int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
     bytes += 4.0 * np[k];
     ++k;
   }
-  if (scaled) bytes += 2.0 * np[0];  // the maximum's pass over the gradient
+  if (scaled && !amax_ready) bytes += 2.0 * np[0];  // the maximum's pass over the gradient
   Scope ps(L, s, TP_K_CONVERT, 0, bytes);
   float* gs = scaled ? at<float>(ws, L->gscale) : nullptr;
-  HIP_TRY(to_f16(sp, dp, np, k, s, gs, scaled ? gs + kAmaxFloats : nullptr));
+  HIP_TRY(to_f16(sp, dp, np, k, s, gs, scaled ? gs + kAmaxFloats : nullptr, amax_ready));
   return TP_OK;
 }
 
@@ -601,7 +601,19 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   int e;
   // the upstream gradient as the GEMMs read it (fp16 copy for a bf16 layer)
   const void* dout = dout_full ? dout_full : io->dout;
-  if ((e = to_f16_copies(L, {dout}, {&L->dout16}, {(size_t)n * h}, ws, s, true))) return e;
+  // bf16 layer, one [n, h] upstream gradient: a single pass over it gives
+  // db2's column partials and the partial maxima of its scaled fp16 copy
+  int rpb2 = 0;
+  const int nb2 = colsum_blocks(n, h, &rpb2);
+  const bool db2_fused = L->sdt == DT_BF16 && !dout_full && n > 0 && h % 8 == 0 &&
+                         (long)((h / 8 + 255) / 256) * nb2 <= kAmaxFloats;
+  if (db2_fused) {
+    Scope ps(L, s, TP_K_REDUCE, 0, (double)n * h * L->esz + 4.0 * h);
+    HIP_TRY(colsum_amax_partial(io->dout, n, h, h, at<float>(ws, L->part2), rpb2,
+                                at<float>(ws, L->gscale), s));
+  }
+  if ((e = to_f16_copies(L, {dout}, {&L->dout16}, {(size_t)n * h}, ws, s, true, db2_fused)))
+    return e;
   if (L->sdt == DT_BF16) dout = at<void>(ws, L->dout16);
   const float* unscale = chain_unscale(L, ws);
   const void* c_act = c_in ? c_in : at<void>(ws, L->c);
@@ -621,8 +633,14 @@ int bwd_mlp(tp_layer* L, const tp_params* p, const tp_bwd_io* io, float* dc_out,
   // u buffer) or recomputed into the du buffer, then overwritten in place
   // (each element is read, then written, by the same thread of the epilogue)
   // db2 and dW2 (need only dout and z)
-  if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s, db2_rows)))
+  if (db2_fused) {
+    Scope ps(L, s, TP_K_REDUCE, 0, (double)nb2 * h * 4);
+    HIP_TRY(reduce_partials(at<float>(ws, L->part2), nb2, 1, h, io->d_b_fc2, nullptr, nullptr,
+                            io->accumulate, s));
+  } else if ((e = bias_grad(L, io->dout, L->sdt, h, io->d_b_fc2, io->accumulate, ws, s,
+                            db2_rows))) {
     return e;
+  }
   g = wgrad_args(L, fl, h, at<void>(ws, L->z), dout, io->d_w_fc2, io->accumulate);
   g.split = L->split_w2; g.scale = unscale;
   if ((e = run_gemm(L, g, s, ws, true))) return e;
