@@ -432,21 +432,37 @@ __device__ __forceinline__ void dtl_tile(const GemmArgs& g, int m0, int n0, int 
     OA::load(ra, lda, m0, (kt0 + j) * BK, As + st * BM * BK, wid, lane);
     OB::load(rb, ldb, n0, (kt0 + j) * BK, Bs + st * BN * BK, wid, lane);
   };
+  // The operand fragments of K sub-step ks + 1 are read from LDS before the
+  // MFMAs of sub-step ks issue (two fragment sets in registers); the
+  // scheduling barriers keep the compiler from moving each read back next to
+  // its MFMA, which left a full LDS latency before every other MFMA of a wave
+  // (1T shard GEMMs 0.8 % faster in sum).
   auto compute = [&](int j, int st) {
     const uint16_t* as = As + st * BM * BK;
     const uint16_t* bs = Bs + st * BN * BK;
+    f16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = OA::frag(as, wm * WTM + 32 * i, 0, lane);
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) bfr[0][jj] = OB::frag(bs, wn * WTN + 32 * jj, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      f16x8 af[TM], bfr[TN];
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = OA::frag(as, wm * WTM + 32 * i, ks, lane);
+        for (int i = 0; i < TM; ++i) af[nxt][i] = OA::frag(as, wm * WTM + 32 * i, ks + 1, lane);
 #pragma unroll
-      for (int jj = 0; jj < TN; ++jj) bfr[jj] = OB::frag(bs, wn * WTN + 32 * jj, ks, lane);
+        for (int jj = 0; jj < TN; ++jj)
+          bfr[nxt][jj] = OB::frag(bs, wn * WTN + 32 * jj, ks + 1, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[jj], af[i], acc[i][jj], 0, 0, 0);
+          acc[i][jj] =
+              __builtin_amdgcn_mfma_f32_32x32x16_f16(bfr[cur][jj], af[cur][i], acc[i][jj], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   dtl_prologue<S>(nk, issue);
