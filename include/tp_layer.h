@@ -193,7 +193,8 @@ typedef struct {
                        two independent pieces on a second stream of the
                        handle, joined before its results are used: in the
                        forward (bf16 layers) the fp16 copies of the MLP
-                       weights while attention and the output projection run;
+                       weights while attention and the output projection run
+                       (FC1 waits for W_fc1's copy only, FC2 for W_fc2's);
                        in the backward the gradient of W_o while dO and the
                        attention backward run. Otherwise every kernel runs on
                        the caller's stream. Results are bitwise identical.

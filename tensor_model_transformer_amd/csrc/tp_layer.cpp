@@ -102,7 +102,7 @@ struct tp_layer {
   // current device by the first backward call; null if that failed (then
   // everything runs on the caller's stream).
   hipStream_t side = nullptr;
-  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr, fc1_ev = nullptr;
   bool side_tried = false;
   bool overlap = false;  // independent pieces of TP_ALL on the side stream (opts)
   // decode (one row per sequence): its own workspace plan
@@ -384,14 +384,17 @@ hipStream_t side_stream(tp_layer* L, hipStream_t s) {
   if (!L->side_tried) {
     L->side_tried = true;
     hipStream_t st = nullptr;
-    hipEvent_t a = nullptr, b = nullptr;
+    hipEvent_t a = nullptr, b = nullptr, c = nullptr;
     if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess &&
         hipEventCreateWithFlags(&a, hipEventDisableTiming) == hipSuccess &&
-        hipEventCreateWithFlags(&b, hipEventDisableTiming) == hipSuccess) {
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) == hipSuccess &&
+        hipEventCreateWithFlags(&c, hipEventDisableTiming) == hipSuccess) {
       L->side = st;
       L->fork_ev = a;
       L->join_ev = b;
+      L->fc1_ev = c;
     } else {
+      if (c) (void)hipEventDestroy(c);
       if (b) (void)hipEventDestroy(b);
       if (a) (void)hipEventDestroy(a);
       if (st) (void)hipStreamDestroy(st);
@@ -486,7 +489,10 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   // the MLP weights' fp16 copies on the side stream while attention runs
   if (mlp_cvt) {
     if ((e = fork_to(L, s, mlp_cvt))) return e;
-    if ((e = convert_mlp_weights(L, p, ws, mlp_cvt))) return e;
+    const size_t hf = (size_t)L->hidden * L->fl;
+    if ((e = to_f16_copies(L, {p->w_fc1}, {&L->w16_fc1}, {hf}, ws, mlp_cvt))) return e;
+    HIP_TRY(hipEventRecord(L->fc1_ev, mlp_cvt));
+    if ((e = to_f16_copies(L, {p->w_fc2}, {&L->w16_fc2}, {hf}, ws, mlp_cvt))) return e;
   }
   {
   Scope ps(L, s, TP_K_ATTN_FWD, 4.0 * L->dh * L->Hl * L->attn_pairs,
@@ -518,7 +524,8 @@ int convert_mlp_weights(tp_layer* L, const tp_params* p, void* ws, hipStream_t s
 
 int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, int out_f32,
             bool designated, void* ws, hipStream_t s, const void* c_in = nullptr,
-            bool converted = false) {
+            hipStream_t side_cvt = nullptr) {
+  const bool converted = side_cvt != nullptr;
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
   float* h_mid = at<float>(ws, L->h_mid);
@@ -539,6 +546,8 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   g.C = L->recompute_fc1 ? nullptr : at<void>(ws, L->u); g.ldc = fl;
   g.C2 = at<void>(ws, L->z); g.ldc2 = fl;
   if ((e = run_gemm(L, g, s, ws))) return e;
+  // W_fc2's copy (side stream) may still run beside LN2 and FC1
+  if (converted && (e = join_from(L, s, side_cvt))) return e;
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = fl;
   g.A = at<void>(ws, L->z); g.lda = fl; g.a_kmajor = 1;
@@ -1049,8 +1058,10 @@ int tp_layer_fwd(tp_layer* L, int phase, const tp_fwd_io* io, void* hip_stream) 
       if ((e = fwd_attn(L, p, io->x, at<float>(ws, L->h_mid), true, ws, s, nullptr,
                         sd != s ? sd : nullptr)))
         return e;
-      if (sd != s && (e = join_from(L, s, sd))) return e;
-      return fwd_mlp(L, p, at<float>(ws, L->h_mid), io->out, 0, true, ws, s, nullptr, sd != s);
+      // FC1 waits for W_fc1's copy only; fwd_mlp joins the rest before FC2
+      if (sd != s) HIP_TRY(hipStreamWaitEvent(s, L->fc1_ev, 0));
+      return fwd_mlp(L, p, at<float>(ws, L->h_mid), io->out, 0, true, ws, s, nullptr,
+                     sd != s ? sd : nullptr);
     }
     case TP_FWD_ATTN:
       if ((e = check_ptrs({io->x, io->out}))) return e;
@@ -1232,6 +1243,7 @@ int tp_layer_destroy(tp_layer* L) {
       (void)hipStreamSynchronize(L->side);
       (void)hipEventDestroy(L->fork_ev);
       (void)hipEventDestroy(L->join_ev);
+      (void)hipEventDestroy(L->fc1_ev);
       (void)hipStreamDestroy(L->side);
     }
   }
