@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
   // Column sums over the block's rows: dgamma, dbeta and (DSUM) dx. Rows of
   // 1024 threads keep the dx sums in LDS, each thread its own entries (no
   // barrier needed), so the other two fit the registers.
-  constexpr bool kLdsSum = DSUM && NT > 512;
+  constexpr bool kLdsSum = DSUM && NT > 768;
   __shared__ float4 dsl[kLdsSum ? 2 * NV * NT : 1];
   float dg[NV][8], db[NV][8], ds[(DSUM && !kLdsSum) ? NV : 1][8];
 #pragma unroll
@@ -256,11 +256,11 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(
     for (int i = 0; i < 2 * NV; ++i) dsl[i * NT + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  // Rows of up to 512 threads: row r + 1's inputs (with its mean and rstd)
+  // Rows of up to 768 threads: row r + 1's inputs (with its mean and rstd)
   // are fetched while row r is reduced and written, and gamma is loaded once.
   // Wider rows (1024 threads) have no registers for the second copy and load
   // each row in turn.
-  if constexpr (NT <= 512) {
+  if constexpr (NT <= 768) {
   float nd[NV][8], nx[NV][8], nr[NV][8], gm[NV][8];
   float nmu = 0.f, nrs = 0.f;
 #define TPL_LNB_FETCH(ROW)                                                     \
@@ -443,7 +443,23 @@ static hipError_t ln_bwd_t(const float* dy, const void* x, const float* mean,
           (Ts*)dx_st, st_scale, part, rows_per_blk, rows, h);                              \
     return hipGetLastError();                                                              \
   }
-  TPL_LNB(256, 1) TPL_LNB(256, 2) TPL_LNB(512, 2) TPL_LNB(1024, 2) TPL_LNB(1024, 4)
+  // rows of at most 768 vectors: one vector per thread, the workgroup as
+  // wide as the row (rounded up to whole waves), so no thread idles on a
+  // second, partly used vector (h = 3072: 384 threads, where 256 threads of
+  // two vectors each left half the second vectors empty)
+  if (h / 8 <= 768) {
+    const int nt1 = (h / 8 + 63) / 64 * 64;
+    if (want_dsum)
+      ln_bwd_kernel<T, Tx, Tr, Ts, 768, 1, true><<<nblk, nt1, 0, s>>>(
+          dy, (const Tx*)x, mean, rstd, (const T*)gamma, (const Tr*)dres, dx_f32, (Ts*)dx_st,
+          st_scale, part, rows_per_blk, rows, h);
+    else
+      ln_bwd_kernel<T, Tx, Tr, Ts, 768, 1, false><<<nblk, nt1, 0, s>>>(
+          dy, (const Tx*)x, mean, rstd, (const T*)gamma, (const Tr*)dres, dx_f32, (Ts*)dx_st,
+          st_scale, part, rows_per_blk, rows, h);
+    return hipGetLastError();
+  }
+  TPL_LNB(512, 2) TPL_LNB(1024, 2) TPL_LNB(1024, 4)
 #undef TPL_LNB
   return hipErrorInvalidValue;
 }
