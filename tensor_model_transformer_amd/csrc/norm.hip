@@ -1,6 +1,8 @@
 // LayerNorm forward/backward, column reductions and the single-GPU exchange
-// sum. All HBM-bound: one pass over each tensor, 16-byte vector accesses,
-// fp32 statistics, deterministic (no atomics) two-stage column sums.
+// sum. All HBM-bound: one pass over each tensor (the LayerNorm backward of
+// rows wider than 6144 elements reads its inputs twice), 16-byte vector
+// accesses, fp32 statistics; column sums as block partials plus one
+// reduction, in a fixed order (deterministic, no atomics).
 //
 // LayerNorm placement follows "Megatron-LM: GPU-Cluster Training Parallelism",
 // section "Paper 1: BERT LayerNorm Rearrangement" (pre-LN: each sublayer reads
