@@ -68,10 +68,10 @@ def test_small_bf16_local(w):
     _run(w, taps=True)
 
 
-# Attention workgroup placement over the 8 XCDs: 6 (sequence, head) pairs x 4
-# query blocks (the pairs do not divide by 8, the 24 workgroups do: each XCD
-# takes a contiguous eighth of the pair-major order) and 16 pairs x 3 blocks
-# (whole pairs per XCD, three ranks of blocks).
+# Attention job lists over the 8 XCDs: 6 (sequence, head) pairs x 4 query
+# blocks (the pairs do not divide by 8: each pair is cut into 4 parts by block
+# rank modulo 4 and every XCD takes 3 parts) and 16 pairs x 3 blocks (whole
+# pairs per XCD, three ranks of blocks); the backward's grid holds both roles.
 PLACEMENT = [
     Workload("pairs6_blocks4", LayerDims(2, 400, 384, 6, 768, t=2, dtype="bf16", mask="causal"),
              rank=1, seed=27, affine="perturbed"),
