@@ -96,11 +96,12 @@ struct tp_layer {
   // causal from the shape; padding as given to tp_layer_profile (0 = unknown)
   double attn_pairs;
   Prof prof;
-  // Side stream of the backward: the weight gradients (and bias column sums)
-  // run on it concurrently with the data-gradient chain on the caller's
-  // stream; every phase joins it back before returning. Created on the
-  // current device by the first backward call; null if that failed (then
-  // everything runs on the caller's stream).
+  // Side stream of TP_ALL with opts.overlap: in the forward the fp16 copies of
+  // the MLP weights (fc1_ev marks the end of W_fc1's), in the backward the
+  // output projection's weight gradient, each beside the caller's stream;
+  // every call joins it back before returning. Created on the current device
+  // by the first call that uses it; null if that failed (then everything
+  // runs on the caller's stream).
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr, fc1_ev = nullptr;
   bool side_tried = false;
