@@ -463,14 +463,24 @@ int to_f16_copies(tp_layer* L, std::initializer_list<const void*> src,
 // a_in is the gathered [n, h] LayerNorm output.
 int convert_mlp_weights(tp_layer* L, const tp_params* p, void* ws, hipStream_t s);
 
+// With mlp_cvt the MLP weights' copies go to that stream after the QKV GEMM;
+// with all_cvt they are made here, in the same launch as W_qkv's and W_o's.
 int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool designated,
-             void* ws, hipStream_t s, const void* a_in = nullptr, hipStream_t mlp_cvt = nullptr) {
+             void* ws, hipStream_t s, const void* a_in = nullptr, hipStream_t mlp_cvt = nullptr,
+             bool all_cvt = false) {
   const int n = L->n, h = L->hidden, hl = L->hl;
   int e;
   const double nh = (double)n * h;
-  if ((e = to_f16_copies(L, {p->w_qkv, p->w_o}, {&L->w16_qkv, &L->w16_o},
-                         {(size_t)h * 3 * hl, (size_t)hl * h}, ws, s)))
+  const size_t hf = (size_t)h * L->fl;
+  if (all_cvt) {
+    if ((e = to_f16_copies(L, {p->w_qkv, p->w_o, p->w_fc1, p->w_fc2},
+                           {&L->w16_qkv, &L->w16_o, &L->w16_fc1, &L->w16_fc2},
+                           {(size_t)h * 3 * hl, (size_t)hl * h, hf, hf}, ws, s)))
+      return e;
+  } else if ((e = to_f16_copies(L, {p->w_qkv, p->w_o}, {&L->w16_qkv, &L->w16_o},
+                                {(size_t)h * 3 * hl, (size_t)hl * h}, ws, s))) {
     return e;
+  }
   if (!a_in) {
   Scope ps(L, s, TP_K_LN_FWD, 0, nh * 2 * L->esz + 8.0 * n);
   HIP_TRY(ln_fwd(L->sdt, L->sdt, L->adt, x, p->ln1_gamma, p->ln1_beta, at<void>(ws, L->a),
@@ -490,7 +500,6 @@ int fwd_attn(tp_layer* L, const tp_params* p, const void* x, float* dst, bool de
   // the MLP weights' fp16 copies on the side stream while attention runs
   if (mlp_cvt) {
     if ((e = fork_to(L, s, mlp_cvt))) return e;
-    const size_t hf = (size_t)L->hidden * L->fl;
     if ((e = to_f16_copies(L, {p->w_fc1}, {&L->w16_fc1}, {hf}, ws, mlp_cvt))) return e;
     HIP_TRY(hipEventRecord(L->fc1_ev, mlp_cvt));
     if ((e = to_f16_copies(L, {p->w_fc2}, {&L->w16_fc2}, {hf}, ws, mlp_cvt))) return e;
@@ -525,8 +534,8 @@ int convert_mlp_weights(tp_layer* L, const tp_params* p, void* ws, hipStream_t s
 
 int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, int out_f32,
             bool designated, void* ws, hipStream_t s, const void* c_in = nullptr,
-            hipStream_t side_cvt = nullptr) {
-  const bool converted = side_cvt != nullptr;
+            hipStream_t side_cvt = nullptr, bool converted_here = false) {
+  const bool converted = side_cvt != nullptr || converted_here;
   const int n = L->n, h = L->hidden, fl = L->fl;
   int e;
   float* h_mid = at<float>(ws, L->h_mid);
@@ -548,7 +557,7 @@ int fwd_mlp(tp_layer* L, const tp_params* p, const float* h_mid_in, void* out, i
   g.C2 = at<void>(ws, L->z); g.ldc2 = fl;
   if ((e = run_gemm(L, g, s, ws))) return e;
   // W_fc2's copy (side stream) may still run beside LN2 and FC1
-  if (converted && (e = join_from(L, s, side_cvt))) return e;
+  if (side_cvt && (e = join_from(L, s, side_cvt))) return e;
   g = gemm_base(L);
   g.M = n; g.N = h; g.K = fl;
   g.A = at<void>(ws, L->z); g.lda = fl; g.a_kmajor = 1;
@@ -1055,14 +1064,17 @@ int tp_layer_fwd(tp_layer* L, int phase, const tp_fwd_io* io, void* hip_stream) 
   switch (phase) {
     case TP_ALL: {
       if ((e = check_ptrs({io->x, io->out}))) return e;
-      hipStream_t sd = L->sdt == DT_BF16 ? side_stream(L, s) : s;
+      // bf16: the weights' fp16 copies in one launch, or the MLP's on the side
+      // stream (overlap); FC1 then waits for W_fc1's copy only and fwd_mlp
+      // joins the rest before FC2
+      const bool cvt = L->sdt == DT_BF16;
+      hipStream_t sd = cvt ? side_stream(L, s) : s;
       if ((e = fwd_attn(L, p, io->x, at<float>(ws, L->h_mid), true, ws, s, nullptr,
-                        sd != s ? sd : nullptr)))
+                        sd != s ? sd : nullptr, cvt && sd == s)))
         return e;
-      // FC1 waits for W_fc1's copy only; fwd_mlp joins the rest before FC2
       if (sd != s) HIP_TRY(hipStreamWaitEvent(s, L->fc1_ev, 0));
       return fwd_mlp(L, p, at<float>(ws, L->h_mid), io->out, 0, true, ws, s, nullptr,
-                     sd != s ? sd : nullptr);
+                     sd != s ? sd : nullptr, cvt && sd == s);
     }
     case TP_FWD_ATTN:
       if ((e = check_ptrs({io->x, io->out}))) return e;
